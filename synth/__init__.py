@@ -1,0 +1,136 @@
+"""Seeded synthetic inputs shared by the oracle tests, the GPU tests and the
+benchmark. Holds no arithmetic of the quantization method: only random draws
+with the shapes and distributions of the five workloads, bf16 rounding of the
+draws, and routing draws.
+
+Workloads (data seed 1000 + workload number, one PCG64 sub-stream per tensor):
+  1 single tensor: X, W float32 [256, 256] ~ N(0,1), 8 distinct seeded
+    positions of each scaled by 100.
+  2 MoE expert forward: x bf16 [16384, 4096] ~ N(0,1); W bf16 [64, 1536, 4096]
+    ~ N(0, 0.02); top-8 of 64 experts, uniform, distinct per token.
+  3 weight requantization: workload 2's W quantized to NVFP4.
+  4 backward GEMMs: g bf16 [131072, 1536] ~ N(0, 1e-3), 0.1% of entries
+    scaled by 50; workload 2's routing and x.
+  5 large skewed forward: x bf16 [65536, 7168] ~ Student-t(3);
+    W bf16 [128, 2048, 7168] ~ N(0, 0.02); top-8 of 128 experts with Zipf(1.1)
+    popularity.
+"""
+import numpy as np
+
+WORKLOADS = {
+    1: dict(rows=256, cols=256, outliers=8, outlier_scale=100.0, sr_seed=0),
+    2: dict(tokens=16384, hidden=4096, experts=64, topk=8, ffn=1536, w_std=0.02),
+    3: dict(experts=64, ffn=1536, hidden=4096, sr_seed=42),
+    4: dict(tokens=16384, hidden=4096, experts=64, topk=8, ffn=1536, g_std=1e-3,
+            spike_frac=1e-3, spike_scale=50.0, sr_seed=42),
+    5: dict(tokens=65536, hidden=7168, experts=128, topk=8, ffn=2048, w_std=0.02, zipf_s=1.1),
+}
+
+_CHUNK = 1 << 24
+
+
+def rng_for(workload, stream):
+    """Independent PCG64 stream for tensor ``stream`` of a workload."""
+    return np.random.Generator(np.random.PCG64(np.random.SeedSequence([1000 + int(workload), int(stream)])))
+
+
+def bf16_bits(f32):
+    """float32 -> bfloat16 bit patterns (uint16), round to nearest even."""
+    b = np.ascontiguousarray(f32, dtype=np.float32).view(np.uint32)
+    return ((b + np.uint32(0x7FFF) + ((b >> np.uint32(16)) & np.uint32(1))) >> np.uint32(16)).astype(np.uint16)
+
+
+def bf16_to_f32(bits):
+    """bfloat16 bit patterns -> float32 (exact)."""
+    return (np.asarray(bits, dtype=np.uint16).astype(np.uint32) << np.uint32(16)).view(np.float32)
+
+
+def normal_bf16(shape, std, rng):
+    """bf16 bits of N(0, std^2) draws, generated in chunks."""
+    n = int(np.prod(shape))
+    out = np.empty(n, dtype=np.uint16)
+    for s in range(0, n, _CHUNK):
+        m = min(_CHUNK, n - s)
+        out[s:s + m] = bf16_bits(rng.standard_normal(m, dtype=np.float32) * np.float32(std))
+    return out.reshape(shape)
+
+
+def student_t_bf16(shape, dof, rng):
+    n = int(np.prod(shape))
+    out = np.empty(n, dtype=np.uint16)
+    for s in range(0, n, _CHUNK):
+        m = min(_CHUNK, n - s)
+        out[s:s + m] = bf16_bits(rng.standard_t(dof, m).astype(np.float32))
+    return out.reshape(shape)
+
+
+def topk_uniform(tokens, experts, k, rng):
+    """k distinct experts per token, uniformly at random."""
+    out = np.empty((tokens, k), dtype=np.int32)
+    for s in range(0, tokens, 8192):
+        m = min(8192, tokens - s)
+        out[s:s + m] = np.argsort(rng.random((m, experts)), axis=1)[:, :k]
+    return out
+
+
+def topk_zipf(tokens, experts, k, s_exp, rng):
+    """k distinct experts per token; expert r-1 has popularity ~ r^-s
+    (Gumbel top-k of the log popularities)."""
+    logp = -s_exp * np.log(np.arange(1, experts + 1, dtype=np.float64))
+    out = np.empty((tokens, k), dtype=np.int32)
+    for s in range(0, tokens, 8192):
+        m = min(8192, tokens - s)
+        g = logp[None, :] - np.log(-np.log(rng.random((m, experts))))
+        out[s:s + m] = np.argsort(-g, axis=1)[:, :k]
+    return out
+
+
+def workload1():
+    """(X, W) float32 [256, 256] with 8 outliers each."""
+    p = WORKLOADS[1]
+    out = []
+    for stream in (0, 1):
+        rng = rng_for(1, stream)
+        x = rng.standard_normal((p["rows"], p["cols"]), dtype=np.float32)
+        pos = rng.choice(x.size, size=p["outliers"], replace=False)
+        x.reshape(-1)[pos] *= np.float32(p["outlier_scale"])
+        out.append(x)
+    return out[0], out[1]
+
+
+def moe_activations(workload, tokens=None, hidden=None):
+    p = WORKLOADS[workload]
+    shape = (tokens or p["tokens"], hidden or p["hidden"])
+    if workload == 5:
+        return student_t_bf16(shape, 3, rng_for(5, 0))
+    return normal_bf16(shape, 1.0, rng_for(workload, 0))
+
+
+def moe_weights(workload, experts=None, ffn=None, hidden=None):
+    p = WORKLOADS[workload]
+    shape = (experts or p["experts"], ffn or p["ffn"], hidden or p["hidden"])
+    return normal_bf16(shape, p["w_std"], rng_for(workload, 1))
+
+
+def moe_routing(workload, tokens=None, experts=None):
+    p = WORKLOADS[workload]
+    t = tokens or p["tokens"]
+    e = experts or p["experts"]
+    if workload == 5:
+        return topk_zipf(t, e, p["topk"], p["zipf_s"], rng_for(5, 2))
+    return topk_uniform(t, e, p["topk"], rng_for(workload, 2))
+
+
+def output_grad(rows, cols, workload=4):
+    """g bf16 [rows, cols] ~ N(0, 1e-3) with 0.1% of entries scaled by 50."""
+    p = WORKLOADS[4]
+    rng = rng_for(workload, 3)
+    n = rows * cols
+    out = np.empty(n, dtype=np.uint16)
+    for s in range(0, n, _CHUNK):
+        m = min(_CHUNK, n - s)
+        v = rng.standard_normal(m, dtype=np.float32) * np.float32(p["g_std"])
+        spike = rng.random(m) < p["spike_frac"]
+        v[spike] *= np.float32(p["spike_scale"])
+        out[s:s + m] = bf16_bits(v)
+    return out.reshape(rows, cols)

@@ -1,0 +1,327 @@
+"""Pins of the oracle's quantizers: the pages' worked examples, brute force
+over every 16x16 tile of small inputs, and the SR unbiasedness test."""
+import json
+import os
+from fractions import Fraction
+
+import numpy as np
+import pytest
+
+from oracle import formats as F
+from oracle import quant as Q
+from oracle.rng import sr_bits16
+
+GOLD = json.load(open(os.path.join(os.path.dirname(__file__), "golden", "worked_examples.json")))
+f32 = np.float32
+
+
+def q1(row, outer=1.0):
+    """Quantize one row with a given outer scale; return (codes, scale values)."""
+    x = np.asarray(row, dtype=f32)[None, None, :]
+    p, s, _ = Q.quantize_nvfp4(x, Q.OUTER_GIVEN, np.array([outer], f32))
+    return F.unpack_fp4(p)[0, 0], F.e4m3_decode(s[0, 0])
+
+
+def test_minus_54_block():
+    g = GOLD["block_max_minus_54"]
+    row = np.zeros(16, f32)
+    row[3] = g["block_max"]
+    row[5] = 10.0
+    codes, sc = q1(row, g["outer"])
+    assert sc[0] == g["scale"]
+    assert F.e2m1_decode(codes[3]) == g["value"]
+
+
+def test_figure1_593_7():
+    g = GOLD["figure1_593_7"]
+    row = np.zeros(16, f32)
+    row[0] = g["input"]
+    codes, sc = q1(row, g["outer"])
+    assert sc[0] == g["scale"]
+    assert F.e2m1_decode(codes[0]) == g["value"]
+    rec = F.e2m1_decode(codes[0]) * sc[0]
+    assert rec == g["reconstructed"]
+    assert abs((rec - g["input"]) - g["error"]) < 1e-3
+
+
+def test_5_4_forward_value():
+    g = GOLD["sr_5_4"]
+    row = np.zeros(16, f32)
+    row[0] = g["forward_block_max"]
+    row[1] = g["input"]
+    codes, sc = q1(row)
+    assert sc[0] == g["forward_scale"]
+    assert F.e2m1_decode(codes[1]) * sc[0] == g["forward_value"]
+
+
+@pytest.mark.parametrize("key,outer", [("outer_1", 1.0), ("outer_2", 2.0), ("outer_0_5", 0.5)])
+def test_range_shifts_with_outer_scale(key, outer):
+    lo, hi = GOLD["range"][key]
+    # the largest magnitude is representable exactly
+    codes, sc = q1(np.r_[hi, np.zeros(15)], outer)
+    assert F.e2m1_decode(codes[0]) * sc[0] * outer == hi
+    # the smallest: a block whose max is 6 * 2^-9 * outer has the smallest scale 2^-9
+    blk = np.zeros(16, f32)
+    blk[0] = 6 * 2.0 ** -9 * outer
+    blk[1] = lo
+    codes, sc = q1(blk, outer)
+    assert sc[0] == 2.0 ** -9
+    assert F.e2m1_decode(codes[1]) * sc[0] * outer == lo
+    # half of it is a tie between 0 and the smallest value and rounds to even (0)
+    blk[1] = lo / 2
+    codes, sc = q1(blk, outer)
+    assert F.e2m1_decode(codes[1]) == 0
+
+
+def test_outer_scale_per_tensor_row_expert():
+    rng = np.random.default_rng(5)
+    x = rng.standard_normal((3, 8, 64)).astype(f32) * np.array([1, 100, 1e-3], f32)[:, None, None]
+    for mode in (Q.OUTER_TENSOR, Q.OUTER_ROW):
+        p, s, st = Q.quantize_nvfp4(x, mode)
+        amax = np.abs(x).max(axis=(1, 2)) if mode == Q.OUTER_TENSOR else np.abs(x).max(axis=2)
+        assert np.array_equal(st, (amax / f32(2688)).astype(f32))
+        xh = Q.dequantize_nvfp4_f64(p, s, st, mode)
+        # the group maximum is reproduced to within one FP4/E4M3 step of the top of the range
+        top = np.abs(xh).max(axis=(1, 2)) if mode == Q.OUTER_TENSOR else np.abs(xh).max(axis=2)
+        assert np.all(np.abs(top - amax) <= amax * 2e-3)
+    # all-zero group -> outer scale 1 and zero codes
+    z = np.zeros((1, 2, 32), f32)
+    p, s, st = Q.quantize_nvfp4(z, Q.OUTER_TENSOR)
+    assert st[0] == 1.0 and not p.any() and not s.any()
+
+
+def _near_tie(v, grid, rel=1e-6):
+    mids = (grid[1:] + grid[:-1]) / 2
+    return np.min(np.abs(v[:, None] - mids[None, :]), axis=1) <= rel * np.maximum(np.abs(v), 1e-30)
+
+
+@pytest.mark.parametrize("shape,dist,seed", [((32, 32), "normal", 0), ((64, 64), "normal", 1),
+                                             ((64, 64), "t3", 2), ((32, 32), "outlier", 3),
+                                             ((32, 32), "zeros", 4), ((64, 64), "wide", 5)])
+def test_brute_force_every_16x16_tile(shape, dist, seed):
+    rng = np.random.default_rng(seed)
+    if dist == "normal":
+        x = rng.standard_normal(shape)
+    elif dist == "t3":
+        x = rng.standard_t(3, shape)
+    elif dist == "outlier":
+        x = rng.uniform(1, 2, shape)
+        x[rng.integers(0, shape[0]), rng.integers(0, shape[1])] = 1000.0
+    elif dist == "zeros":
+        x = rng.standard_normal(shape)
+        x[:16, :16] = 0.0
+        x[16:, 16:] = -0.0
+    else:
+        x = rng.standard_normal(shape) * np.exp(rng.uniform(-20, 20, shape))
+    x = x.astype(f32)
+    for mode, outer in ((Q.OUTER_TENSOR, None), (Q.OUTER_GIVEN, np.array([0.37], f32))):
+        p, s, st = Q.quantize_nvfp4(x[None], mode, outer)
+        codes = F.unpack_fp4(p)[0]
+        st = float(np.asarray(st).reshape(-1)[0])
+        R, C = shape
+        for ti in range(R // 16):
+            for tj in range(C // 16):
+                blk = x[ti * 16:(ti + 1) * 16, tj * 16:(tj + 1) * 16].astype(np.float64)   # 16 row blocks
+                ab = np.abs(blk).max(axis=1)
+                ratio = ab / (6 * st)
+                got_s = s[0, ti * 16:(ti + 1) * 16, tj]
+                want_s = np.argmin(np.abs(F.E4M3_VAL[None, :] - ratio[:, None]), axis=1)
+                bad = (got_s != want_s) & ~_near_tie(ratio, F.E4M3_VAL)
+                assert not bad.any(), (ti, tj)
+                D = F.e4m3_decode(got_s) * st
+                live = D >= 2.0 ** -126
+                yv = np.where(live[:, None], blk / np.where(live, D, 1)[:, None], 0.0)
+                want_c = np.argmin(np.abs(F.E2M1_MAG[None, :] - np.abs(yv).reshape(-1)[:, None]), axis=1).reshape(16, 16)
+                got_c = codes[ti * 16:(ti + 1) * 16, tj * 16:(tj + 1) * 16]
+                nt = _near_tie(np.abs(yv).reshape(-1), F.E2M1_MAG).reshape(16, 16)
+                assert not (((got_c & 7) != want_c) & ~nt).any(), (ti, tj)
+                assert np.array_equal(got_c >> 3, np.signbit(blk.astype(f32)).astype(np.uint8))
+
+
+def test_figure3_outlier_tile():
+    g = GOLD["figure3_outlier_tile"]
+    rng = np.random.default_rng(11)
+    x = rng.uniform(1.0, 2.0, (16, 16)).astype(f32)
+    x[15, 7] = 100.0                                         # one outlier in the last row
+    p, s, _ = Q.quantize_nvfp4(x[None], Q.OUTER_GIVEN, np.array([1.0], f32))
+    assert int(np.count_nonzero(F.unpack_fp4(p)[0] & 7)) == g["survive_1x16"]
+    codes, _ = Q.quantize_nvfp4_tile16(x, 1.0)
+    assert int(np.count_nonzero(codes & 7)) == g["survive_16x16"]
+
+
+def test_figure2_row_vs_column_scaling():
+    g = GOLD["figure2_row_tile"]
+    rng = np.random.default_rng(12)
+    x = rng.uniform(0.5, 2.0, (16, 16)).astype(f32)
+    x[0] = rng.uniform(40.0, 64.0, 16).astype(f32)           # first row large
+    p, s, _ = Q.quantize_nvfp4(x[None], Q.OUTER_GIVEN, np.array([1.0], f32))
+    assert int(np.count_nonzero(F.unpack_fp4(p)[0] & 7)) == g["survive_rows"]
+    # 16x1 column blocks = 1x16 blocks of the transpose
+    p, s, _ = Q.quantize_nvfp4(x.T.copy()[None], Q.OUTER_GIVEN, np.array([1.0], f32))
+    c = F.unpack_fp4(p)[0].T
+    assert np.all(c[0] & 7)                                   # the large row survives
+    assert int(np.count_nonzero(c[1:] & 7)) < 240 // 2        # most small values flush
+
+
+# ------------------------------------------------------------------ SR
+def sr_example_tile():
+    """16x32 tile whose transposed block 0 holds the dequantized 4.5 next to a
+    12 (new scale 12/6 = 2) and a 2688 elsewhere so the new outer scale is 1."""
+    g = GOLD["sr_5_4"]
+    x = np.full((16, 32), 0.125, f32)
+    x[0, 0] = g["input"]
+    x[0, 1] = g["forward_block_max"]
+    x[1, 0] = 12.0
+    x[2, 20] = 2688.0
+    return x
+
+
+def test_sr_worked_example_rn_and_counts():
+    g = GOLD["sr_5_4"]
+    x = sr_example_tile()
+    p, s, st = Q.quantize_nvfp4(x[None], Q.OUTER_GIVEN, np.array([1.0], f32))
+    xh = Q.dequantize_nvfp4(p, s, st, Q.OUTER_GIVEN)[0]
+    assert xh[0, 0] == g["forward_value"] and xh[1, 0] == 12.0 and xh[2, 20] == 2688.0
+    # deterministic rounding of the transposed value
+    pr, sr, str_ = Q.requant_transpose_sr(p, s, st, Q.OUTER_GIVEN, Q.NVFP4, 0, 0, rnd=Q.RN)
+    assert str_[0] == 1.0 and F.e4m3_decode(sr[0, 0, 0]) == g["new_scale"]
+    assert F.e2m1_decode(F.unpack_fp4(pr)[0, 0, 0]) == g["rn_code_value"]
+    # stochastic rounding over 10^4 seeds: 2 w.p. 3/4, 3 w.p. 1/4
+    n = 10_000
+    highs = 0
+    for seed in range(n):
+        pr, sr, _ = Q.requant_transpose_sr(p, s, st, Q.OUTER_GIVEN, Q.NVFP4, seed, 0)
+        v = F.e2m1_decode(F.unpack_fp4(pr)[0, 0, 0])
+        assert v in (g["sr_low"], g["sr_high"])
+        highs += v == g["sr_high"]
+    mean = n * g["p_high"]
+    sd = np.sqrt(n * g["p_high"] * (1 - g["p_high"]))
+    assert abs(highs - mean) <= 4 * sd
+    # and the 16-bit draw gives exactly p = 1/4: 16384 of the 65536 values satisfy (r + 1/2)/2^16 < 1/4
+    assert np.count_nonzero((np.arange(65536) + 0.5) / 65536 < 0.25) == 16384
+
+
+def _sr_stats(vals, z, step, n):
+    """Fraction of elements whose mean over n draws lies outside
+    4 sigma/sqrt(n) (+ one draw and the 2^-17 resolution) of z, and the pooled z-score."""
+    mean = vals.mean(axis=0)
+    frac = np.clip((np.abs(z) - np.floor(np.abs(z) / step) * step) / step, 0, 1)
+    sigma = step * np.sqrt(frac * (1 - frac))
+    dev = np.abs(mean - z)
+    bad = dev > 4 * sigma / np.sqrt(n) + step / n + step * 2.0 ** -17
+    pooled = np.sum(mean - z) / np.sqrt(np.sum(sigma ** 2) / n + 1e-300)
+    return int(bad.sum()), float(pooled)
+
+
+@pytest.mark.parametrize("fmt", [Q.NVFP4, Q.MXFP8])
+def test_sr_unbiased_over_10k_seeds(fmt):
+    """Mean of the SR requantization over 10^4 seeds vs the dequantized input
+    (E[w_q] = E[(w_q^T)^T])."""
+    rng = np.random.default_rng(7)
+    x = rng.standard_normal((64, 64)).astype(f32)
+    x[3, 5] = 40.0
+    p, s, st = Q.quantize_nvfp4(x[None], Q.OUTER_TENSOR)
+    z = Q.dequantize_nvfp4(p, s, st, Q.OUTER_TENSOR)[0].T.astype(np.float64)   # [C, R]
+    n = 10_000
+    vals = np.empty((n, 64, 64))
+    for seed in range(n):
+        out = Q.requant_transpose_sr(p, s, st, Q.OUTER_TENSOR, fmt, seed, 5)
+        if fmt == Q.NVFP4:
+            pc, sc, st2 = out
+            vals[seed] = F.e2m1_decode(F.unpack_fp4(pc)[0]) * np.repeat(F.e4m3_decode(sc[0]), 16, axis=1) * float(st2[0])
+            if seed == 0:
+                step = np.repeat(F.e4m3_decode(sc[0]), 16, axis=1) * float(st2[0])
+                y = z / step
+                step = step * np.where(np.abs(y) < 2, 0.5, np.where(np.abs(y) < 4, 1.0, 2.0))
+        else:
+            pc, sc = out
+            vals[seed] = Q.dequantize_mxfp8_f64(pc[0], sc[0])
+            if seed == 0:
+                scale = np.repeat(F.e8m0_decode(sc[0]), 32, axis=1)
+                y = np.abs(z) / scale
+                e = np.floor(np.log2(np.maximum(y, 2.0 ** -6)))
+                step = 2.0 ** (e - 3) * scale
+    # scales do not depend on the seed
+    bad, pooled = _sr_stats(vals, z, step, n)
+    assert bad <= 3, bad
+    assert abs(pooled) <= 4, pooled
+
+
+def test_requant_scales_seed_independent_and_brute_force():
+    rng = np.random.default_rng(9)
+    x = (rng.standard_normal((64, 96)) * np.exp(rng.uniform(-4, 4, (64, 96)))).astype(f32)
+    p, s, st = Q.quantize_nvfp4(x[None], Q.OUTER_ROW)
+    z = Q.dequantize_nvfp4(p, s, st, Q.OUTER_ROW)[0].T.astype(np.float64)      # [96, 64]
+    c1, s1 = Q.requant_transpose_sr(p, s, st, Q.OUTER_ROW, Q.MXFP8, 1, 3)
+    c2, s2 = Q.requant_transpose_sr(p, s, st, Q.OUTER_ROW, Q.MXFP8, 2, 3)
+    assert np.array_equal(s1, s2) and not np.array_equal(c1, c2)
+    ab = np.abs(z).reshape(96, 2, 32).max(axis=2)
+    # smallest E8M0 code c with a_b <= 448 * 2^(c-127), by trying every code
+    cand = ab[..., None] <= 448.0 * np.ldexp(1.0, np.arange(255) - 127)
+    assert np.array_equal(s1[0], np.argmax(cand, axis=-1))
+    # every SR code is one of the two grid neighbours of y = z / scale
+    y = z / np.repeat(F.e8m0_decode(s1[0]), 32, axis=1)
+    v = np.abs(F.e4m3_decode(c1[0]))
+    lo_idx = np.searchsorted(F.E4M3_VAL, np.abs(y), side="right") - 1
+    assert np.all((v == F.E4M3_VAL[lo_idx]) | (v == F.E4M3_VAL[np.minimum(lo_idx + 1, 126)]))
+    # NVFP4 target: round-up scale is the smallest code >= exact a_b / (6 s_t')
+    c3, s3, st3 = Q.requant_transpose_sr(p, s, st, Q.OUTER_ROW, Q.NVFP4, 1, 3)
+    assert st3[0] == np.float32(np.float32(np.abs(z).max()) / np.float32(2688))
+    ab16 = np.abs(z).reshape(96, 4, 16).max(axis=2)
+    ratio = ab16 / (6 * float(st3[0]))
+    ge = F.E4M3_VAL[None, None, :] >= ratio[..., None]
+    want = np.where(ge.any(-1), np.argmax(ge, axis=-1), 0x7E)
+    # exempt ratios within float32 rounding of a grid value (the spec divides in float32)
+    near = np.min(np.abs(F.E4M3_VAL[None, None, :] - ratio[..., None]), axis=-1) <= 1e-6 * ratio
+    assert not ((s3[0] != want) & ~near).any()
+    assert np.count_nonzero(near) < ratio.size // 50
+
+
+def test_sr_decision_matches_definition_on_random_elements():
+    """Independent exact check of a sample of SR decisions with rationals."""
+    rng = np.random.default_rng(13)
+    x = rng.standard_normal((32, 64)).astype(f32)
+    p, s, st = Q.quantize_nvfp4(x[None], Q.OUTER_TENSOR)
+    codes, sc = Q.requant_transpose_sr(p, s, st, Q.OUTER_TENSOR, Q.MXFP8, 1234, 9)
+    z = Q.dequantize_nvfp4(p, s, st, Q.OUTER_TENSOR)[0].T
+    idx = np.arange(64 * 32, dtype=np.uint64).reshape(64, 32)
+    r = sr_bits16(1234, 9, idx)
+    for (i, j) in [(a, b) for a in range(0, 64, 7) for b in range(0, 32, 3)]:
+        e = int(sc[0, i, j // 32]) - 127
+        y = Fraction(float(z[i, j])) / Fraction(2) ** e
+        m = abs(y)
+        grid = [Fraction(float(g)) for g in F.E4M3_VAL]
+        lo = max(g for g in grid if g <= m)
+        hi = min([g for g in grid if g > m], default=lo)
+        delta = (m - lo) / (hi - lo) if hi != lo else Fraction(0)
+        up = Fraction(2 * int(r[i, j]) + 1, 1 << 17) < delta
+        want = hi if up else lo
+        assert Fraction(float(abs(F.e4m3_decode(codes[0, i, j])))) == want
+
+
+def test_mxfp8_rn_and_zero_block():
+    x = np.zeros((2, 64), f32)
+    x[0, :32] = np.linspace(-3, 500, 32)
+    c, s = Q.quantize_mxfp8(x, Q.RN)
+    # block max 500 -> smallest 2^e with 500 <= 448 * 2^e is 2^1
+    assert s[0, 0] == 128 and s[0, 1] == 0 and s[1, 0] == 0
+    assert not c[1].any() and not c[0, 32:].any()
+    assert np.all(np.abs(F.e4m3_decode(c[0, :32]) * 2 - x[0, :32]) <= np.abs(x[0, :32]) / 16 + 1e-9)
+
+
+def test_segmented_transposed_layout_and_padding():
+    rng = np.random.default_rng(3)
+    seg = np.array([0, 5, 5, 40, 72], dtype=np.int64)          # includes an empty and a ragged segment
+    x = rng.standard_normal((72, 64)).astype(f32)
+    codes, scales = Q.quantize_mxfp8_transposed(x, seg, Q.SR, 4, 2)
+    mp, base = Q.segmented_layout(seg, 64)
+    assert mp == [32, 0, 64, 32] and codes.size == 64 * 128 and scales.size == 64 * 4
+    # segment 2 = rows 5..39 (35 rows) padded to 64 tokens; the padding is code 0
+    blk = codes[base[2]:base[2] + 64 * 64].reshape(64, 64)
+    assert not blk[:, 35:].any()
+    # same values as the plain transposed quantizer applied to the padded segment
+    Z = np.zeros((64, 64), f32)
+    Z[:, :35] = x[5:40].T
+    idx = (np.uint64(base[2]) + np.arange(64 * 64, dtype=np.uint64)).reshape(64, 64)
+    c2, s2 = Q.mxfp8_quantize(Z, idx, Q.SR, 4, 2)
+    assert np.array_equal(blk, c2)
