@@ -1,0 +1,149 @@
+// Device helpers shared by the bsq kernels (gfx950 only).
+//
+// Rounding rules follow "End-to-End 4-Bit Training": FP4 values
+// +-{0,0.5,1,1.5,2,3,4,6}, E4M3 block scales (max 448), E8M0 MX scales
+// (section "Low-precision formats on Blackwell"); stochastic rounding rounds
+// up or down with probability given by the distance to each neighbour
+// (section "Re-quantization with stochastic rounding").
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace bsqd {
+
+constexpr float kFltMinNormal = 1.17549435082228750797e-38f;  // 2^-126
+constexpr float kTwoPowM17 = 7.62939453125e-06f;              // 2^-17
+
+// ---------------------------------------------------------------- bf16
+__device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
+__device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xFFFF0000u); }
+
+// ---------------------------------------------------------------- E4M3
+// Exact decode (hardware convert, OCP E4M3FN on gfx950).
+__device__ __forceinline__ float e4m3_val(uint32_t code) {
+  return __builtin_amdgcn_cvt_f32_fp8((int)code, 0);
+}
+// Non-negative r -> E4M3 code, round to nearest even, saturating at 448. The
+// hardware convert rounds to nearest even for |v| <= 464 and gives NaN above,
+// so clamping to 448 first yields exactly the saturating rounding.
+__device__ __forceinline__ uint32_t e4m3_rne_sat(float r) {
+  return (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(fminf(r, 448.0f), 0.0f, 0, false) & 0xFFu;
+}
+// Non-negative r -> smallest E4M3 code whose value is >= r, capped at 448.
+__device__ __forceinline__ uint32_t e4m3_ru_cap(float r) {
+  uint32_t c = e4m3_rne_sat(r);
+  if (c < 0x7Eu && e4m3_val(c) < r) c += 1u;
+  return c;
+}
+// Value already on the E4M3 grid (|v| <= 448) -> code (exact).
+__device__ __forceinline__ uint32_t e4m3_exact(float v) {
+  return (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(v, 0.0f, 0, false) & 0xFFu;
+}
+// Two values on the E4M3 grid -> two codes packed in the low 16 bits.
+__device__ __forceinline__ uint32_t e4m3_exact2(float a, float b) {
+  return (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(a, b, 0, false) & 0xFFFFu;
+}
+
+// ---------------------------------------------------------------- E2M1
+// Two floats -> two E2M1 codes written into byte `sel` of `old` (a in the
+// low nibble). With scale 1.0 the hardware convert is round to nearest even,
+// saturating at 6, sign kept (checked over every float32 pattern below 12).
+#define BSQ_CVT_FP4X2(old, a, b, sel) \
+  __builtin_amdgcn_cvt_scalef32_pk_fp4_f32((old), (a), (b), 1.0f, (sel))
+
+// ---------------------------------------------------------------- E8M0
+// Smallest e with a <= 448 * 2^e, clamped to [-127, 127]; 0 gives -127.
+// 448 = 1.75 * 2^8: a = 2^E * 1.f needs e = E - 8, or E - 7 when 1.f > 1.75.
+__device__ __forceinline__ int e8m0_exponent(float a) {
+  uint32_t b = __float_as_uint(a);
+  int E = (int)(b >> 23) - 127;
+  int e = E - 8 + ((b & 0x7FFFFFu) > 0x600000u ? 1 : 0);
+  if (a == 0.0f) e = -127;
+  return e < -127 ? -127 : (e > 127 ? 127 : e);
+}
+// 2^-e as float32 for e in [-127, 126].
+__device__ __forceinline__ float pow2_neg(int e) { return __uint_as_float((uint32_t)(127 - e) << 23); }
+
+// ---------------------------------------------------------------- Philox4x32-10
+// Salmon, Moraes, Dror, Shaw, "Parallel random numbers: as easy as 1, 2, 3"
+// (SC'11): ten rounds of two 32x32->64 multiplies by 0xD2511F53 / 0xCD9E8D57
+// with the key bumped by (0x9E3779B9, 0xBB67AE85) between rounds.
+struct U32x4 { uint32_t v[4]; };
+__device__ __forceinline__ U32x4 philox4x32_10(uint32_t c0, uint32_t c1, uint32_t c2, uint32_t c3,
+                                               uint32_t k0, uint32_t k1) {
+#pragma unroll
+  for (int i = 0; i < 10; ++i) {
+    if (i) { k0 += 0x9E3779B9u; k1 += 0xBB67AE85u; }
+    const uint64_t p0 = (uint64_t)0xD2511F53u * c0;
+    const uint64_t p1 = (uint64_t)0xCD9E8D57u * c2;
+    const uint32_t n0 = (uint32_t)(p1 >> 32) ^ c1 ^ k0;
+    const uint32_t n2 = (uint32_t)(p0 >> 32) ^ c3 ^ k1;
+    c1 = (uint32_t)p1;
+    c3 = (uint32_t)p0;
+    c0 = n0;
+    c2 = n2;
+  }
+  U32x4 r;
+  r.v[0] = c0; r.v[1] = c1; r.v[2] = c2; r.v[3] = c3;
+  return r;
+}
+// The four words serving output indices 8*grp .. 8*grp+7 (index i takes half
+// i&1 of word (i>>1)&3).
+__device__ __forceinline__ U32x4 sr_words(uint64_t seed, uint64_t stream, uint64_t grp) {
+  return philox4x32_10((uint32_t)grp, (uint32_t)(grp >> 32), (uint32_t)stream,
+                       (uint32_t)(stream >> 32), (uint32_t)seed, (uint32_t)(seed >> 32));
+}
+__device__ __forceinline__ uint32_t r16_of(const U32x4& w, int i) {
+  return (w.v[(i >> 1) & 3] >> (16 * (i & 1))) & 0xFFFFu;
+}
+
+// ---------------------------------------------------------------- stochastic rounding
+// u = (2 r + 1) / 2^17; round away from zero iff u < delta, delta the position
+// of |y| between its two grid neighbours (exact in float32 here).
+//
+// E4M3 target, |y| <= 448. For |y| >= 2^-6 the grid keeps 3 mantissa bits, so
+// delta = t / 2^20 with t the 20 dropped mantissa bits, and
+// u < delta  <=>  8 (2 r + 1) < t. Below 2^-6 the step is 2^-9.
+__device__ __forceinline__ float sr_e4m3(float y, uint32_t r16) {
+  const uint32_t b = __float_as_uint(y);
+  const uint32_t s = b & 0x80000000u;
+  uint32_t a = b & 0x7FFFFFFFu;
+  if (a >= 0x3C800000u) {
+    const uint32_t t = a & 0xFFFFFu;
+    a = (a & 0xFFF00000u) + (((r16 << 4) + 8u < t) ? 0x100000u : 0u);
+  } else {
+    const float q = __uint_as_float(a) * 512.0f;
+    float fl = floorf(q);
+    const float u = (float)(2u * r16 + 1u) * kTwoPowM17;
+    fl += (u < q - fl) ? 1.0f : 0.0f;
+    a = __float_as_uint(fl * 0.001953125f);
+  }
+  return __uint_as_float(a | s);
+}
+// E2M1 target: steps 0.5 below 2, 1 in [2, 4), 2 in [4, 6); 6 and above -> 6.
+__device__ __forceinline__ float sr_e2m1(float y, uint32_t r16) {
+  const float m = fabsf(y);
+  const float inv = m < 2.0f ? 2.0f : (m < 4.0f ? 1.0f : 0.5f);
+  const float step = m < 2.0f ? 0.5f : (m < 4.0f ? 1.0f : 2.0f);
+  const float q = m * inv;
+  float fl = floorf(q);
+  const float u = (float)(2u * r16 + 1u) * kTwoPowM17;
+  fl += (u < q - fl) ? 1.0f : 0.0f;
+  const float mag = m >= 6.0f ? 6.0f : fl * step;
+  return copysignf(mag, y);
+}
+
+// ---------------------------------------------------------------- reductions
+__device__ __forceinline__ float wave_max(float v) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) v = fmaxf(v, __shfl_xor(v, o, 64));
+  return v;
+}
+template <int G>
+__device__ __forceinline__ float group_max(float v) {  // over aligned groups of G lanes, G <= 64
+#pragma unroll
+  for (int o = G / 2; o > 0; o >>= 1) v = fmaxf(v, __shfl_xor(v, o, 64));
+  return v;
+}
+
+}  // namespace bsqd

@@ -1,0 +1,26 @@
+// Host-side helpers of the C ABI: argument validation and launch checks.
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "../../include/bsq.h"
+
+namespace bsqh {
+
+inline bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+inline hipStream_t as_stream(bsq_stream_t s) { return reinterpret_cast<hipStream_t>(s); }
+inline int launch_status() { return hipGetLastError() == hipSuccess ? BSQ_OK : BSQ_E_LAUNCH; }
+
+// Upper bound on the number of row tiles of height `tile` over `num_segments`
+// segments holding `total_rows` rows in all (each segment wastes at most one
+// partial tile).
+inline int64_t tile_bound(int64_t total_rows, int64_t num_segments, int64_t tile) {
+  return (total_rows + tile - 1) / tile + num_segments;
+}
+
+}  // namespace bsqh
+
+#define BSQ_REQUIRE(cond, err) \
+  do {                         \
+    if (!(cond)) return (err); \
+  } while (0)

@@ -1,0 +1,356 @@
+// Row-wise block quantizers: round-to-nearest NVFP4 and row-wise MXFP8.
+//
+// "End-to-End 4-Bit Training", section "Low-precision formats on Blackwell":
+// each block of 16 consecutive values is scaled from its largest magnitude
+// (an E4M3 scale), values round to the nearest FP4 value, and an FP32 outer
+// scale over a large group shifts the representable range [2^-10, 2688];
+// MXFP8 uses blocks of 32 with E8M0 scales. Section "Recipe details": outer
+// scales per token for activations, per expert for weights. The quantized
+// linear layer figure (section "Re-quantization with stochastic rounding")
+// quantizes the BF16 output gradient to MXFP8 with stochastic rounding.
+//
+// HBM-bound kernels: each thread owns whole blocks, loads them with 16-byte
+// vector loads, reduces the block maximum in registers and writes packed codes
+// with one 8- or 16-byte store. Per-row outer scales reduce across the threads
+// of a row; per-tensor outer scales take a separate max pass that runs over
+// chunks small enough for the second read to come from the on-die cache.
+#include "bsq_device.h"
+#include "bsq_internal.h"
+
+using namespace bsqd;
+
+namespace {
+
+constexpr int kThreads = 256;
+constexpr int64_t kTensorChunkBytes = 64ll << 20;
+
+// 16 consecutive elements of type T (bf16 bit patterns or float).
+template <typename T> struct Blk16;
+template <> struct Blk16<uint16_t> {
+  uint32_t w[8];
+  __device__ __forceinline__ void load(const uint16_t* p) {
+    const uint4* q = reinterpret_cast<const uint4*>(p);
+    const uint4 a = q[0], b = q[1];
+    w[0] = a.x; w[1] = a.y; w[2] = a.z; w[3] = a.w;
+    w[4] = b.x; w[5] = b.y; w[6] = b.z; w[7] = b.w;
+  }
+  __device__ __forceinline__ float get(int i) const { return (i & 1) ? bf16_hi(w[i >> 1]) : bf16_lo(w[i >> 1]); }
+  __device__ __forceinline__ float absmax() const {
+    uint32_t m = 0;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      const uint32_t a = w[i] & 0x7FFF7FFFu;
+      const uint32_t lo = a & 0xFFFFu, hi = a >> 16;
+      m = max(m, max(lo, hi));
+    }
+    return __uint_as_float(m << 16);  // magnitudes compare like their bit patterns
+  }
+};
+template <> struct Blk16<float> {
+  float w[16];
+  __device__ __forceinline__ void load(const float* p) {
+    const float4* q = reinterpret_cast<const float4*>(p);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const float4 v = q[i];
+      w[4 * i] = v.x; w[4 * i + 1] = v.y; w[4 * i + 2] = v.z; w[4 * i + 3] = v.w;
+    }
+  }
+  __device__ __forceinline__ float get(int i) const { return w[i]; }
+  __device__ __forceinline__ float absmax() const {
+    float m = 0.0f;
+#pragma unroll
+    for (int i = 0; i < 16; ++i) m = fmaxf(m, fabsf(w[i]));
+    return m;
+  }
+};
+
+template <typename T>
+__device__ __forceinline__ float absmax16B(const uint4 v);
+template <>
+__device__ __forceinline__ float absmax16B<uint16_t>(const uint4 v) {
+  const uint32_t w[4] = {v.x & 0x7FFF7FFFu, v.y & 0x7FFF7FFFu, v.z & 0x7FFF7FFFu, v.w & 0x7FFF7FFFu};
+  uint32_t m = 0;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) m = max(m, max(w[i] & 0xFFFFu, w[i] >> 16));
+  return __uint_as_float(m << 16);
+}
+template <>
+__device__ __forceinline__ float absmax16B<float>(const uint4 v) {
+  return fmaxf(fmaxf(fabsf(__uint_as_float(v.x)), fabsf(__uint_as_float(v.y))),
+               fmaxf(fabsf(__uint_as_float(v.z)), fabsf(__uint_as_float(v.w))));
+}
+
+__global__ void k_fill_u32(uint32_t* __restrict__ p, uint32_t v, int64_t n) {
+  const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (i < n) p[i] = v;
+}
+__global__ void k_copy_f32(const float* __restrict__ s, float* __restrict__ d, int64_t n) {
+  const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (i < n) d[i] = s[i];
+}
+
+// Largest magnitude of each batch item [item0, item0 + gridDim.y), merged
+// into amax_bits[item] with an atomic max on the bit pattern (non-negative
+// floats order like their bits).
+template <typename T>
+__global__ __launch_bounds__(kThreads) void k_amax_items(const T* __restrict__ x, int64_t vec_per_item,
+                                                         uint32_t* __restrict__ amax_bits, int64_t item0) {
+  const int64_t item = item0 + blockIdx.y;
+  const uint4* p = reinterpret_cast<const uint4*>(x) + item * vec_per_item;
+  float m = 0.0f;
+  const int64_t stride = (int64_t)gridDim.x * kThreads;
+  int64_t i = (int64_t)blockIdx.x * kThreads + threadIdx.x;
+  for (; i + 3 * stride < vec_per_item; i += 4 * stride) {
+    const uint4 a = p[i], b = p[i + stride], c = p[i + 2 * stride], d = p[i + 3 * stride];
+    m = fmaxf(m, fmaxf(fmaxf(absmax16B<T>(a), absmax16B<T>(b)), fmaxf(absmax16B<T>(c), absmax16B<T>(d))));
+  }
+  for (; i < vec_per_item; i += stride) m = fmaxf(m, absmax16B<T>(p[i]));
+  m = wave_max(m);
+  __shared__ float red[kThreads / 64];
+  if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = m;
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    float r = red[0];
+#pragma unroll
+    for (int w = 1; w < kThreads / 64; ++w) r = fmaxf(r, red[w]);
+    atomicMax(amax_bits + item, __float_as_uint(r));
+  }
+}
+
+// NVFP4 round-to-nearest quantization of rows [row0, row_end). TPR threads
+// share a row; each owns up to MAXB blocks of 16 (block j = lane + k*TPR).
+template <typename T, int TPR, int MAXB, int MODE>
+__global__ __launch_bounds__(kThreads) void k_quant_nvfp4(
+    const T* __restrict__ x, int64_t row0, int64_t row_end, int64_t rows_per_item, int64_t C,
+    const float* __restrict__ outer_in, const uint32_t* __restrict__ amax_bits,
+    uint8_t* __restrict__ codes, uint8_t* __restrict__ scales, float* __restrict__ outer_out) {
+  constexpr int RPW = kThreads / TPR;
+  const int tr = threadIdx.x / TPR;
+  const int tl = threadIdx.x % TPR;
+  const int64_t row = row0 + (int64_t)blockIdx.x * RPW + tr;
+  const bool row_ok = row < row_end;
+  const int64_t nb = C >> 4;
+
+  Blk16<T> blk[MAXB];
+  float am[MAXB];
+  float rmax = 0.0f;
+#pragma unroll
+  for (int k = 0; k < MAXB; ++k) {
+    const int64_t j = tl + (int64_t)k * TPR;
+    am[k] = 0.0f;
+    if (row_ok && j < nb) {
+      blk[k].load(x + row * C + j * 16);
+      am[k] = blk[k].absmax();
+      rmax = fmaxf(rmax, am[k]);
+    }
+  }
+
+  float st;
+  if constexpr (MODE == BSQ_OUTER_ROW) {
+    if constexpr (TPR <= 64) {
+      rmax = group_max<TPR>(rmax);
+    } else {
+      __shared__ float red[kThreads / 64];
+      const float wm = wave_max(rmax);
+      if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = wm;
+      __syncthreads();
+      rmax = red[tr * (TPR / 64)];
+#pragma unroll
+      for (int w = 1; w < TPR / 64; ++w) rmax = fmaxf(rmax, red[tr * (TPR / 64) + w]);
+    }
+    st = rmax > 0.0f ? rmax / 2688.0f : 1.0f;
+    if (row_ok && tl == 0) outer_out[row] = st;
+  } else {
+    const int64_t item = (row_ok ? row : row_end - 1) / rows_per_item;
+    if constexpr (MODE == BSQ_OUTER_TENSOR) {
+      const float a = __uint_as_float(amax_bits[item]);
+      st = a > 0.0f ? a / 2688.0f : 1.0f;
+    } else {
+      st = outer_in[item];
+    }
+    if (row_ok && tl == 0 && row % rows_per_item == 0) outer_out[item] = st;
+  }
+
+  const float d = 6.0f * st;
+#pragma unroll
+  for (int k = 0; k < MAXB; ++k) {
+    const int64_t j = tl + (int64_t)k * TPR;
+    if (row_ok && j < nb) {
+      const float r = am[k] / d;
+      const uint32_t sc = e4m3_rne_sat(r);
+      const float D = e4m3_val(sc) * st;
+      const float inv = D >= kFltMinNormal ? 1.0f / D : 0.0f;
+      uint32_t w0 = 0, w1 = 0;
+      w0 = BSQ_CVT_FP4X2(w0, blk[k].get(0) * inv, blk[k].get(1) * inv, 0);
+      w0 = BSQ_CVT_FP4X2(w0, blk[k].get(2) * inv, blk[k].get(3) * inv, 1);
+      w0 = BSQ_CVT_FP4X2(w0, blk[k].get(4) * inv, blk[k].get(5) * inv, 2);
+      w0 = BSQ_CVT_FP4X2(w0, blk[k].get(6) * inv, blk[k].get(7) * inv, 3);
+      w1 = BSQ_CVT_FP4X2(w1, blk[k].get(8) * inv, blk[k].get(9) * inv, 0);
+      w1 = BSQ_CVT_FP4X2(w1, blk[k].get(10) * inv, blk[k].get(11) * inv, 1);
+      w1 = BSQ_CVT_FP4X2(w1, blk[k].get(12) * inv, blk[k].get(13) * inv, 2);
+      w1 = BSQ_CVT_FP4X2(w1, blk[k].get(14) * inv, blk[k].get(15) * inv, 3);
+      *reinterpret_cast<uint2*>(codes + row * (C >> 1) + j * 8) = make_uint2(w0, w1);
+      scales[row * nb + j] = (uint8_t)sc;
+    }
+  }
+}
+
+// Row-wise MXFP8: one thread per block of 32 (element index = blk*32 + i).
+template <typename T, int RND>
+__global__ __launch_bounds__(kThreads) void k_mxfp8_rows(const T* __restrict__ x, int64_t nblk, uint64_t seed,
+                                                         uint64_t stream_id, uint8_t* __restrict__ codes,
+                                                         uint8_t* __restrict__ scales) {
+  const int64_t blk = (int64_t)blockIdx.x * kThreads + threadIdx.x;
+  if (blk >= nblk) return;
+  Blk16<T> a, b;
+  a.load(x + blk * 32);
+  b.load(x + blk * 32 + 16);
+  const float amax = fmaxf(a.absmax(), b.absmax());
+  const int e = e8m0_exponent(amax);
+  const float pw = pow2_neg(e);
+  uint32_t out[8];
+  if constexpr (RND == BSQ_SR) {
+#pragma unroll
+    for (int g = 0; g < 4; ++g) {
+      const U32x4 w = sr_words(seed, stream_id, (uint64_t)blk * 4 + g);
+#pragma unroll
+      for (int h = 0; h < 2; ++h) {
+        float v[4];
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          const int i = 8 * g + 4 * h + q;
+          const float y = (i < 16 ? a.get(i) : b.get(i - 16)) * pw;
+          v[q] = sr_e4m3(y, r16_of(w, 4 * h + q));
+        }
+        out[2 * g + h] = e4m3_exact2(v[0], v[1]) | (e4m3_exact2(v[2], v[3]) << 16);
+      }
+    }
+  } else {
+#pragma unroll
+    for (int o = 0; o < 8; ++o) {
+      float v[4];
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const int i = 4 * o + q;
+        v[q] = (i < 16 ? a.get(i) : b.get(i - 16)) * pw;
+      }
+      out[o] = e4m3_exact2(v[0], v[1]) | (e4m3_exact2(v[2], v[3]) << 16);
+    }
+  }
+  uint4* dst = reinterpret_cast<uint4*>(codes + blk * 32);
+  dst[0] = make_uint4(out[0], out[1], out[2], out[3]);
+  dst[1] = make_uint4(out[4], out[5], out[6], out[7]);
+  scales[blk] = (uint8_t)(e + 127);
+}
+
+inline unsigned grid1(int64_t n, int t = kThreads) { return (unsigned)((n + t - 1) / t); }
+
+template <typename T, int MODE>
+int launch_quant(const T* x, int64_t row0, int64_t row_end, int64_t R, int64_t C, const float* outer_in,
+                 const uint32_t* amax, uint8_t* codes, uint8_t* scales, float* outer_out, hipStream_t s) {
+  const int64_t nb = C / 16;
+  const int64_t n = row_end - row0;
+  if (n <= 0) return BSQ_OK;
+#define BSQ_QL(TPR, MAXB)                                                                          \
+  hipLaunchKernelGGL((k_quant_nvfp4<T, TPR, MAXB, MODE>), dim3(grid1(n, kThreads / TPR)), dim3(kThreads), 0, s, \
+                     x, row0, row_end, R, C, outer_in, amax, codes, scales, outer_out)
+  if (nb <= 16) BSQ_QL(16, 1);
+  else if (nb <= 64) BSQ_QL(64, 1);
+  else if (nb <= 256) BSQ_QL(256, 1);
+  else if (nb <= 512) BSQ_QL(256, 2);
+  else if (nb <= 1024) BSQ_QL(256, 4);
+  else BSQ_QL(256, 8);
+#undef BSQ_QL
+  return bsqh::launch_status();
+}
+
+template <typename T>
+int quantize_nvfp4_t(const T* x, int64_t B, int64_t R, int64_t C, int mode, const float* outer_in,
+                     uint8_t* codes, uint8_t* scales, float* outer_out, uint32_t* ws, hipStream_t s) {
+  const int64_t rows = B * R;
+  if (mode == BSQ_OUTER_ROW) return launch_quant<T, BSQ_OUTER_ROW>(x, 0, rows, R, C, nullptr, nullptr, codes, scales, outer_out, s);
+  if (mode == BSQ_OUTER_GIVEN) return launch_quant<T, BSQ_OUTER_GIVEN>(x, 0, rows, R, C, outer_in, nullptr, codes, scales, outer_out, s);
+  hipLaunchKernelGGL(k_fill_u32, dim3(grid1(B)), dim3(kThreads), 0, s, ws, 0u, B);
+  const int64_t item_bytes = R * C * (int64_t)sizeof(T);
+  const int64_t chunk = item_bytes >= kTensorChunkBytes ? 1 : kTensorChunkBytes / item_bytes;
+  const int64_t vec = item_bytes / 16;
+  for (int64_t i0 = 0; i0 < B; i0 += chunk) {
+    const int64_t ni = (B - i0) < chunk ? (B - i0) : chunk;
+    int64_t gx = (vec + 4 * kThreads - 1) / (4 * kThreads);
+    if (gx > 4096) gx = 4096;
+    hipLaunchKernelGGL(k_amax_items<T>, dim3((unsigned)gx, (unsigned)ni), dim3(kThreads), 0, s, x, vec, ws, i0);
+    const int st = launch_quant<T, BSQ_OUTER_TENSOR>(x, i0 * R, (i0 + ni) * R, R, C, nullptr, ws, codes, scales, outer_out, s);
+    if (st != BSQ_OK) return st;
+  }
+  return bsqh::launch_status();
+}
+
+}  // namespace
+
+extern "C" size_t bsq_quantize_nvfp4_workspace(int64_t batch, int64_t rows, int64_t cols, int mode) {
+  (void)rows;
+  (void)cols;
+  if (mode != BSQ_OUTER_TENSOR || batch <= 0) return 0;
+  return (size_t)((batch * 4 + 255) / 256 * 256);
+}
+
+extern "C" int bsq_quantize_nvfp4(const void* x, int dtype, int64_t batch, int64_t rows, int64_t cols, int mode,
+                                  const float* outer_in, uint8_t* codes, uint8_t* scales, float* outer_out,
+                                  void* ws, size_t ws_bytes, bsq_stream_t stream) {
+  BSQ_REQUIRE(dtype == BSQ_F32 || dtype == BSQ_BF16, BSQ_E_DTYPE);
+  BSQ_REQUIRE(mode == BSQ_OUTER_TENSOR || mode == BSQ_OUTER_ROW || mode == BSQ_OUTER_GIVEN, BSQ_E_ENUM);
+  BSQ_REQUIRE(batch >= 0 && rows >= 0 && cols >= 0 && cols % 16 == 0 && cols <= 32768, BSQ_E_SHAPE);
+  if (batch == 0) return BSQ_OK;
+  const bool empty = rows == 0 || cols == 0;
+  BSQ_REQUIRE(outer_out && (mode != BSQ_OUTER_GIVEN || outer_in), BSQ_E_NULL);
+  BSQ_REQUIRE(empty || (x && codes && scales), BSQ_E_NULL);
+  BSQ_REQUIRE(bsqh::aligned16(x) && bsqh::aligned16(codes), BSQ_E_ALIGN);
+  BSQ_REQUIRE(((uintptr_t)outer_out & 3) == 0 && ((uintptr_t)outer_in & 3) == 0, BSQ_E_ALIGN);
+  const size_t need = empty ? 0 : bsq_quantize_nvfp4_workspace(batch, rows, cols, mode);
+  if (need) {
+    BSQ_REQUIRE(ws, BSQ_E_NULL);
+    BSQ_REQUIRE(((uintptr_t)ws & 3) == 0, BSQ_E_ALIGN);
+    BSQ_REQUIRE(ws_bytes >= need, BSQ_E_WORKSPACE);
+  }
+  hipStream_t s = bsqh::as_stream(stream);
+  if (empty) {  // empty groups: outer scale 1 (or the given one)
+    const int64_t n = mode == BSQ_OUTER_ROW ? batch * rows : batch;
+    if (n == 0) return BSQ_OK;
+    if (mode == BSQ_OUTER_GIVEN)
+      hipLaunchKernelGGL(k_copy_f32, dim3(grid1(n)), dim3(kThreads), 0, s, outer_in, outer_out, n);
+    else
+      hipLaunchKernelGGL(k_fill_u32, dim3(grid1(n)), dim3(kThreads), 0, s, reinterpret_cast<uint32_t*>(outer_out),
+                         0x3F800000u, n);
+    return bsqh::launch_status();
+  }
+  if (dtype == BSQ_BF16)
+    return quantize_nvfp4_t<uint16_t>(static_cast<const uint16_t*>(x), batch, rows, cols, mode, outer_in, codes,
+                                      scales, outer_out, static_cast<uint32_t*>(ws), s);
+  return quantize_nvfp4_t<float>(static_cast<const float*>(x), batch, rows, cols, mode, outer_in, codes, scales,
+                                 outer_out, static_cast<uint32_t*>(ws), s);
+}
+
+// Row-wise MXFP8 (transpose == 0); the transposed form lives with the
+// transpose kernels.
+int bsq_quantize_mxfp8_rows(const void* x, int dtype, int64_t rows, int64_t cols, int rnd, uint64_t seed,
+                            uint64_t stream_id, uint8_t* codes, uint8_t* scales, hipStream_t s) {
+  const int64_t nblk = rows * cols / 32;
+  if (nblk == 0) return BSQ_OK;
+  if (dtype == BSQ_BF16) {
+    if (rnd == BSQ_SR)
+      hipLaunchKernelGGL((k_mxfp8_rows<uint16_t, BSQ_SR>), dim3(grid1(nblk)), dim3(kThreads), 0, s,
+                         static_cast<const uint16_t*>(x), nblk, seed, stream_id, codes, scales);
+    else
+      hipLaunchKernelGGL((k_mxfp8_rows<uint16_t, BSQ_RN>), dim3(grid1(nblk)), dim3(kThreads), 0, s,
+                         static_cast<const uint16_t*>(x), nblk, seed, stream_id, codes, scales);
+  } else {
+    if (rnd == BSQ_SR)
+      hipLaunchKernelGGL((k_mxfp8_rows<float, BSQ_SR>), dim3(grid1(nblk)), dim3(kThreads), 0, s,
+                         static_cast<const float*>(x), nblk, seed, stream_id, codes, scales);
+    else
+      hipLaunchKernelGGL((k_mxfp8_rows<float, BSQ_RN>), dim3(grid1(nblk)), dim3(kThreads), 0, s,
+                         static_cast<const float*>(x), nblk, seed, stream_id, codes, scales);
+  }
+  return bsqh::launch_status();
+}

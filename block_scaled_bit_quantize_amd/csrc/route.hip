@@ -1,0 +1,138 @@
+// Routing of tokens to per-expert row segments.
+//
+// "End-to-End 4-Bit Training", section "Quantized communications": a small
+// router decides where each token goes and tokens are dispatched to the
+// routed experts. On one GPU the dispatch is a permutation: every (token,
+// slot) pair of the top-k routing becomes one row of the expert GEMMs, rows
+// grouped by expert and, inside an expert, ordered by token.
+//
+// Three deterministic passes over chunks of 256 tokens: per-chunk expert
+// counts, one scan that turns them into segment offsets and per-chunk bases,
+// and a scatter whose within-chunk rank comes from an LDS bitmap of the
+// tokens routed to each expert (a popcount of the earlier tokens).
+#include "bsq_device.h"
+#include "bsq_internal.h"
+
+namespace {
+
+constexpr int kChunk = 256;
+
+__global__ __launch_bounds__(kChunk) void k_route_count(const int32_t* __restrict__ ids, int64_t tokens, int k, int E,
+                                                        int32_t* __restrict__ counts) {
+  extern __shared__ int32_t cnt[];
+  for (int e = threadIdx.x; e < E; e += kChunk) cnt[e] = 0;
+  __syncthreads();
+  const int64_t t = (int64_t)blockIdx.x * kChunk + threadIdx.x;
+  if (t < tokens) {
+    for (int j = 0; j < k; ++j) {
+      const int e = ids[t * k + j];
+      if (e >= 0 && e < E) atomicAdd(&cnt[e], 1);
+    }
+  }
+  __syncthreads();
+  for (int e = threadIdx.x; e < E; e += kChunk) counts[(int64_t)blockIdx.x * E + e] = cnt[e];
+}
+
+// One workgroup of 1024 threads: thread e turns the chunk counts of expert e
+// into exclusive bases (in place), then a scan over experts gives the offsets.
+__global__ __launch_bounds__(1024) void k_route_scan(int32_t* __restrict__ counts, int64_t nchunks, int E,
+                                                     int64_t* __restrict__ seg_offsets) {
+  __shared__ int64_t tot[1024];
+  const int e = threadIdx.x;
+  int64_t run = 0;
+  if (e < E) {
+    for (int64_t c = 0; c < nchunks; ++c) {
+      const int32_t v = counts[c * E + e];
+      counts[c * E + e] = (int32_t)run;
+      run += v;
+    }
+  }
+  tot[e] = run;
+  __syncthreads();
+  for (int o = 1; o < 1024; o <<= 1) {
+    const int64_t a = e >= o ? tot[e - o] : 0;
+    __syncthreads();
+    tot[e] += a;
+    __syncthreads();
+  }
+  const int64_t start = tot[e] - run;
+  if (e < E) {
+    seg_offsets[e] = start;
+    for (int64_t c = 0; c < nchunks; ++c) counts[c * E + e] += (int32_t)start;
+  }
+  if (e == E - 1) seg_offsets[E] = tot[e];
+}
+
+__global__ __launch_bounds__(kChunk) void k_route_scatter(const int32_t* __restrict__ ids, int64_t tokens, int k, int E,
+                                                          const int32_t* __restrict__ bases, int32_t* __restrict__ row_index,
+                                                          int32_t* __restrict__ pair_row) {
+  extern __shared__ uint32_t bits[];  // [E][kChunk / 32]
+  constexpr int W = kChunk / 32;
+  for (int i = threadIdx.x; i < E * W; i += kChunk) bits[i] = 0;
+  __syncthreads();
+  const int tl = threadIdx.x;
+  const int64_t t = (int64_t)blockIdx.x * kChunk + tl;
+  if (t < tokens) {
+    for (int j = 0; j < k; ++j) {
+      const int e = ids[t * k + j];
+      if (e >= 0 && e < E) atomicOr(&bits[e * W + (tl >> 5)], 1u << (tl & 31));
+    }
+  }
+  __syncthreads();
+  if (t >= tokens) return;
+  for (int j = 0; j < k; ++j) {
+    const int e = ids[t * k + j];
+    if (e < 0 || e >= E) continue;
+    int rank = 0;
+    for (int w = 0; w < (tl >> 5); ++w) rank += __popc(bits[e * W + w]);
+    rank += __popc(bits[e * W + (tl >> 5)] & ((1u << (tl & 31)) - 1u));
+    const int32_t row = bases[(int64_t)blockIdx.x * E + e] + rank;
+    row_index[row] = (int32_t)t;
+    pair_row[t * k + j] = row;
+  }
+}
+
+}  // namespace
+
+extern "C" size_t bsq_route_workspace(int64_t tokens, int64_t E) {
+  if (tokens <= 0 || E <= 0) return 0;
+  const int64_t nchunks = (tokens + kChunk - 1) / kChunk;
+  return (size_t)((nchunks * E * 4 + 255) / 256 * 256);
+}
+
+extern "C" int bsq_route(const int32_t* topk_ids, int64_t tokens, int64_t k, int64_t E, int32_t* row_index,
+                         int64_t* seg_offsets, int32_t* pair_row, void* ws, size_t ws_bytes, bsq_stream_t stream) {
+  BSQ_REQUIRE(tokens >= 0 && k >= 1 && k <= 64 && E >= 1 && E <= 1024, BSQ_E_SHAPE);
+  BSQ_REQUIRE(tokens * k < (int64_t)1 << 31, BSQ_E_SHAPE);
+  BSQ_REQUIRE(seg_offsets, BSQ_E_NULL);
+  hipStream_t s = bsqh::as_stream(stream);
+  const int64_t nchunks = (tokens + kChunk - 1) / kChunk;
+  if (tokens > 0) {
+    BSQ_REQUIRE(topk_ids && row_index && pair_row && ws, BSQ_E_NULL);
+    BSQ_REQUIRE(((uintptr_t)ws & 3) == 0, BSQ_E_ALIGN);
+    BSQ_REQUIRE(ws_bytes >= bsq_route_workspace(tokens, E), BSQ_E_WORKSPACE);
+    hipLaunchKernelGGL(k_route_count, dim3((unsigned)nchunks), dim3(kChunk), E * sizeof(int32_t), s, topk_ids, tokens,
+                       (int)k, (int)E, static_cast<int32_t*>(ws));
+  }
+  hipLaunchKernelGGL(k_route_scan, dim3(1), dim3(1024), 0, s, static_cast<int32_t*>(ws), nchunks, (int)E, seg_offsets);
+  if (tokens > 0)
+    hipLaunchKernelGGL(k_route_scatter, dim3((unsigned)nchunks), dim3(kChunk), E * (kChunk / 32) * sizeof(uint32_t), s,
+                       topk_ids, tokens, (int)k, (int)E, static_cast<const int32_t*>(ws), row_index, pair_row);
+  return bsqh::launch_status();
+}
+
+extern "C" const char* bsq_status_string(int status) {
+  switch (status) {
+    case BSQ_OK: return "ok";
+    case BSQ_E_NULL: return "required pointer is NULL";
+    case BSQ_E_SHAPE: return "invalid size or shape";
+    case BSQ_E_ALIGN: return "pointer not sufficiently aligned";
+    case BSQ_E_DTYPE: return "unknown element type";
+    case BSQ_E_ENUM: return "unknown mode, rounding or format";
+    case BSQ_E_WORKSPACE: return "workspace too small";
+    case BSQ_E_LAUNCH: return "kernel launch failed";
+    default: return "unknown status";
+  }
+}
+
+extern "C" int bsq_version(void) { return 100; }

@@ -1,0 +1,242 @@
+"""PyTorch-facing wrappers of the bsq_* entry points (argument marshalling
+only: shapes, output allocation, device pointers, the current stream)."""
+import torch
+
+from ._lib import BsqError, check, load_library
+
+F32, BF16 = 0, 1
+OUTER_TENSOR, OUTER_ROW, OUTER_GIVEN = 0, 1, 2
+RN, SR = 0, 1
+NVFP4, MXFP8 = 0, 1
+
+_OUTER = {"tensor": OUTER_TENSOR, "row": OUTER_ROW, "given": OUTER_GIVEN}
+_RND = {"rn": RN, "sr": SR}
+_FMT = {"nvfp4": NVFP4, "mxfp8": MXFP8}
+
+
+def _enum(v, table):
+    return table[v] if isinstance(v, str) else int(v)
+
+
+def _ptr(t):
+    return None if t is None else t.data_ptr()
+
+
+def _stream():
+    return torch.cuda.current_stream().cuda_stream
+
+
+def _dev(*ts):
+    for t in ts:
+        if t is not None and (not t.is_cuda or not t.is_contiguous()):
+            raise BsqError("expected contiguous device tensors")
+
+
+def _ws(nbytes, device):
+    return torch.empty(max(int(nbytes), 1), dtype=torch.uint8, device=device)
+
+
+def quantize_nvfp4(x, mode="tensor", outer_in=None):
+    """Round-to-nearest NVFP4 of x [B, R, C] or [R, C] (float32 or bfloat16).
+    Returns (codes u8 [..., C/2], scales u8 [..., C/16], outer f32 [B] or [B*R])."""
+    lib = load_library()
+    _dev(x, outer_in)
+    squeeze = x.dim() == 2
+    x3 = x.unsqueeze(0) if squeeze else x
+    B, R, C = x3.shape
+    dt = {torch.float32: F32, torch.bfloat16: BF16}.get(x.dtype)
+    if dt is None:
+        raise BsqError("x must be float32 or bfloat16")
+    m = _enum(mode, _OUTER)
+    codes = torch.empty((B, R, C // 2), dtype=torch.uint8, device=x.device)
+    scales = torch.empty((B, R, C // 16), dtype=torch.uint8, device=x.device)
+    outer = torch.empty((B * R,) if m == OUTER_ROW else (B,), dtype=torch.float32, device=x.device)
+    wsb = lib.bsq_quantize_nvfp4_workspace(B, R, C, m)
+    ws = _ws(wsb, x.device) if wsb else None
+    check(lib.bsq_quantize_nvfp4(x3.data_ptr(), dt, B, R, C, m, _ptr(outer_in), codes.data_ptr(),
+                                 scales.data_ptr(), outer.data_ptr(), _ptr(ws), wsb, _stream()),
+          "bsq_quantize_nvfp4")
+    if squeeze:
+        return codes[0], scales[0], outer
+    return codes, scales, outer
+
+
+def padded_segment_layout(seg_offsets_host, cols):
+    """Host helper: (padded length of each segment, total elements) of the padded
+    per-segment transposed layout for a host list/array of segment offsets."""
+    seg = [int(v) for v in seg_offsets_host]
+    mp = [(seg[e + 1] - seg[e] + 31) // 32 * 32 for e in range(len(seg) - 1)]
+    return mp, cols * sum(mp)
+
+
+def _segmented_capacity(rows, nseg, cols):
+    # upper bound of cols * sum(pad32(M_e)); the exact size needs the offsets on the host
+    return cols * (rows + 31 * nseg)
+
+
+def quantize_mxfp8(x, rnd="sr", seed=0, stream_id=0, transpose=False, seg_offsets=None, out_elems=None):
+    """MXFP8 of x [R, C] (float32 or bfloat16). transpose=False: codes [R, C],
+    scales [R, C/32]. transpose=True: flat codes / scales in the padded
+    per-segment transposed layout (seg_offsets: int64 device [E+1] or None for
+    one segment); out_elems (optional) sets the exact output length."""
+    lib = load_library()
+    _dev(x, seg_offsets)
+    R, C = x.shape
+    dt = {torch.float32: F32, torch.bfloat16: BF16}.get(x.dtype)
+    if dt is None:
+        raise BsqError("x must be float32 or bfloat16")
+    r = _enum(rnd, _RND)
+    if not transpose:
+        codes = torch.empty((R, C), dtype=torch.uint8, device=x.device)
+        scales = torch.empty((R, C // 32), dtype=torch.uint8, device=x.device)
+        check(lib.bsq_quantize_mxfp8(x.data_ptr(), dt, R, C, 0, None, 0, r, seed, stream_id, codes.data_ptr(),
+                                     scales.data_ptr(), None, 0, _stream()), "bsq_quantize_mxfp8")
+        return codes, scales
+    nseg = seg_offsets.numel() - 1 if seg_offsets is not None else 1
+    n = out_elems if out_elems is not None else _segmented_capacity(R, nseg, C)
+    codes = torch.empty((n,), dtype=torch.uint8, device=x.device)
+    scales = torch.empty((n // 32,), dtype=torch.uint8, device=x.device)
+    wsb = lib.bsq_quantize_mxfp8_workspace(R, 1, nseg)
+    ws = _ws(wsb, x.device)
+    check(lib.bsq_quantize_mxfp8(x.data_ptr(), dt, R, C, 1, _ptr(seg_offsets), nseg if seg_offsets is not None else 0,
+                                 r, seed, stream_id, codes.data_ptr(), scales.data_ptr(), ws.data_ptr(), wsb,
+                                 _stream()), "bsq_quantize_mxfp8")
+    return codes, scales
+
+
+def requant_transpose_sr(codes, scales, outer, in_mode, out_fmt="mxfp8", seed=0, stream_id=0, rnd="sr",
+                         row_gather=None, seg_offsets=None, out_elems=None):
+    """Dequantize -> transpose -> requantize.
+    Batch mode: codes [B, R, C/2] (or [R, C/2]) -> output [B, C, R] codes
+    (MXFP8 [B, C, R] bytes, NVFP4 [B, C, R/2]) and scales; NVFP4 also returns
+    the new outer scales [B].
+    Gather mode (row_gather int32 [rows], seg_offsets int64 [E+1]): input
+    [T, C/2], output flat padded per-segment transposed MXFP8."""
+    lib = load_library()
+    _dev(codes, scales, outer, row_gather, seg_offsets)
+    im = _enum(in_mode, _OUTER)
+    fmt = _enum(out_fmt, _FMT)
+    r = _enum(rnd, _RND)
+    dev = codes.device
+    if row_gather is not None:
+        T, C2 = codes.shape
+        C = 2 * C2
+        rows = row_gather.numel()
+        nseg = seg_offsets.numel() - 1
+        n = out_elems if out_elems is not None else _segmented_capacity(rows, nseg, C)
+        oc = torch.empty((n,), dtype=torch.uint8, device=dev)
+        osc = torch.empty((n // 32,), dtype=torch.uint8, device=dev)
+        wsb = lib.bsq_requant_workspace(1, rows, nseg, fmt, 1)
+        ws = _ws(wsb, dev)
+        check(lib.bsq_requant_transpose_sr(codes.data_ptr(), scales.data_ptr(), outer.data_ptr(), im, 1, rows, C, T,
+                                           row_gather.data_ptr(), seg_offsets.data_ptr(), nseg, fmt, r, seed,
+                                           stream_id, oc.data_ptr(), osc.data_ptr(), None, ws.data_ptr(), wsb,
+                                           _stream()), "bsq_requant_transpose_sr")
+        return oc, osc
+    squeeze = codes.dim() == 2
+    c3 = codes.unsqueeze(0) if squeeze else codes
+    B, R, C2 = c3.shape
+    C = 2 * C2
+    if fmt == MXFP8:
+        oc = torch.empty((B, C, R), dtype=torch.uint8, device=dev)
+        osc = torch.empty((B, C, R // 32), dtype=torch.uint8, device=dev)
+        oo = None
+    else:
+        oc = torch.empty((B, C, R // 2), dtype=torch.uint8, device=dev)
+        osc = torch.empty((B, C, R // 16), dtype=torch.uint8, device=dev)
+        oo = torch.empty((B,), dtype=torch.float32, device=dev)
+    wsb = lib.bsq_requant_workspace(B, R, 0, fmt, 0)
+    ws = _ws(wsb, dev) if wsb else None
+    check(lib.bsq_requant_transpose_sr(c3.data_ptr(), scales.data_ptr(), outer.data_ptr(), im, B, R, C, B * R, None,
+                                       None, 0, fmt, r, seed, stream_id, oc.data_ptr(), osc.data_ptr(), _ptr(oo),
+                                       _ptr(ws), wsb, _stream()), "bsq_requant_transpose_sr")
+    if squeeze:
+        oc, osc = oc[0], osc[0]
+    return (oc, osc) if fmt == MXFP8 else (oc, osc, oo)
+
+
+_OUT = {torch.bfloat16: BF16, torch.float32: F32}
+
+
+def grouped_gemm_nvfp4(a_codes, a_scales, a_outer, b_codes, b_scales, b_outer, seg_offsets, M_total,
+                       row_index=None, out=None, out_dtype=torch.bfloat16):
+    """y [M_total, N] = per expert, gathered x_q rows times w_q^T with both
+    outer scales (bf16 or float32 output). a_*: [T, K/2], [T, K/16], a_outer
+    [T] (per token) or [1]; b_*: [E, N, K/2], [E, N, K/16], b_outer [E]."""
+    lib = load_library()
+    _dev(a_codes, a_scales, a_outer, b_codes, b_scales, b_outer, seg_offsets, row_index)
+    T, K2 = a_codes.shape
+    E, N, _ = b_codes.shape
+    per_row = 1 if a_outer.numel() == T and T > 1 else 0
+    if out is None:
+        out = torch.empty((M_total, N), dtype=out_dtype, device=a_codes.device)
+    check(lib.bsq_grouped_gemm_nvfp4(a_codes.data_ptr(), a_scales.data_ptr(), a_outer.data_ptr(), per_row, T,
+                                     _ptr(row_index), b_codes.data_ptr(), b_scales.data_ptr(), b_outer.data_ptr(),
+                                     seg_offsets.data_ptr(), E, M_total, N, 2 * K2, out.data_ptr(), _OUT[out.dtype],
+                                     _stream()), "bsq_grouped_gemm_nvfp4")
+    return out
+
+
+def grouped_gemm_mxfp8(wgrad, a_codes, a_scales, b_codes, b_scales, seg_offsets, M, N, K=0, out=None,
+                       out_dtype=None, native=False):
+    """wgrad=False (DGRAD): a [M_total(=M), K], b [E, N, K] -> [M, N] (bf16
+    by default). wgrad=True (WGRAD): a, b flat padded per-segment transposed
+    layouts with M and N rows per expert -> [E, M, N] (float32 by default).
+    native=True runs the scaled-FP8-MFMA variant (faster, less accurate
+    accumulation inside each instruction)."""
+    lib = load_library()
+    _dev(a_codes, a_scales, b_codes, b_scales, seg_offsets)
+    E = seg_offsets.numel() - 1
+    if out is None:
+        dt = out_dtype or (torch.float32 if wgrad else torch.bfloat16)
+        shape = (E, M, N) if wgrad else (M, N)
+        out = torch.empty(shape, dtype=dt, device=a_codes.device)
+    fn = lib.bsq_grouped_gemm_mxfp8_native if native else lib.bsq_grouped_gemm_mxfp8
+    check(fn(1 if wgrad else 0, a_codes.data_ptr(), a_scales.data_ptr(), b_codes.data_ptr(), b_scales.data_ptr(),
+             seg_offsets.data_ptr(), E, M, N, K, out.data_ptr(), _OUT[out.dtype], _stream()), "bsq_grouped_gemm_mxfp8")
+    return out
+
+
+def route(topk_ids, num_experts):
+    """topk_ids int32 [T, k] -> (row_index int32 [T*k], seg_offsets int64 [E+1], pair_row int32 [T*k])."""
+    lib = load_library()
+    _dev(topk_ids)
+    T, k = topk_ids.shape
+    dev = topk_ids.device
+    row_index = torch.empty((T * k,), dtype=torch.int32, device=dev)
+    pair_row = torch.empty((T * k,), dtype=torch.int32, device=dev)
+    seg = torch.empty((num_experts + 1,), dtype=torch.int64, device=dev)
+    wsb = lib.bsq_route_workspace(T, num_experts)
+    ws = _ws(wsb, dev) if wsb else None
+    check(lib.bsq_route(topk_ids.data_ptr(), T, k, num_experts, row_index.data_ptr(), seg.data_ptr(),
+                        pair_row.data_ptr(), _ptr(ws), wsb, _stream()), "bsq_route")
+    return row_index, seg, pair_row
+
+
+def dequantize_nvfp4(codes, scales, outer, mode="tensor"):
+    lib = load_library()
+    _dev(codes, scales, outer)
+    squeeze = codes.dim() == 2
+    c3 = codes.unsqueeze(0) if squeeze else codes
+    B, R, C2 = c3.shape
+    out = torch.empty((B, R, 2 * C2), dtype=torch.float32, device=codes.device)
+    check(lib.bsq_dequantize_nvfp4(c3.data_ptr(), scales.data_ptr(), outer.data_ptr(), _enum(mode, _OUTER), B, R,
+                                   2 * C2, out.data_ptr(), _stream()), "bsq_dequantize_nvfp4")
+    return out[0] if squeeze else out
+
+
+def dequantize_mxfp8(codes, scales):
+    lib = load_library()
+    _dev(codes, scales)
+    R, C = codes.shape
+    out = torch.empty((R, C), dtype=torch.float32, device=codes.device)
+    check(lib.bsq_dequantize_mxfp8(codes.data_ptr(), scales.data_ptr(), R, C, out.data_ptr(), _stream()),
+          "bsq_dequantize_mxfp8")
+    return out
+
+
+def rng_bits16(seed, stream_id, first, n, device="cuda"):
+    lib = load_library()
+    out = torch.empty((n,), dtype=torch.int16, device=device)
+    check(lib.bsq_rng_bits16(seed, stream_id, first, n, out.data_ptr(), _stream()), "bsq_rng_bits16")
+    return out

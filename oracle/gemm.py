@@ -32,23 +32,28 @@ def grouped_gemm_nvfp4_ref(a_packed, a_scales, a_outer, row_index, b_packed, b_s
     maps a dispatched row to its token (None = identity).  ``rows`` selects
     the output rows to compute (default all).  Returns (y_ref, sum|x w|)."""
     a_packed = np.asarray(a_packed)
+    a_scales = np.asarray(a_scales)
+    a_outer = np.asarray(a_outer, dtype=np.float32).reshape(-1)
     T = a_packed.shape[0]
-    xh = dequantize_nvfp4_f64(a_packed[None], np.asarray(a_scales)[None],
-                              np.asarray(a_outer).reshape(1, T), OUTER_ROW)[0]
-    wh = dequantize_nvfp4_f64(b_packed, b_scales, b_outer, OUTER_TENSOR)   # [E, N, K]
+    if a_outer.size == 1 and T > 1:                  # one outer scale for the whole activation tensor
+        a_outer = np.full(T, a_outer[0], dtype=np.float32)
     seg = np.asarray(seg_offsets, dtype=np.int64)
     M_total = int(seg[-1])
     rows = np.arange(M_total) if rows is None else np.asarray(rows, dtype=np.int64)
     tok = rows if row_index is None else np.asarray(row_index, dtype=np.int64)[rows]
     expert = np.searchsorted(seg, rows, side="right") - 1
-    N = wh.shape[1]
+    N = np.asarray(b_packed).shape[1]
     y = np.zeros((len(rows), N))
     ya = np.zeros((len(rows), N))
     for e in np.unique(expert):
         sel = expert == e
-        xa = xh[tok[sel]]
-        y[sel] = xa @ wh[e].T
-        ya[sel] = np.abs(xa) @ np.abs(wh[e]).T
+        t = tok[sel]
+        # dequantize only the rows and the expert this output block needs
+        xa = dequantize_nvfp4_f64(a_packed[t][None], a_scales[t][None], a_outer[t].reshape(1, -1), OUTER_ROW)[0]
+        we = dequantize_nvfp4_f64(np.asarray(b_packed)[e:e + 1], np.asarray(b_scales)[e:e + 1],
+                                  np.asarray(b_outer)[e:e + 1], OUTER_TENSOR)[0]
+        y[sel] = xa @ we.T
+        ya[sel] = np.abs(xa) @ np.abs(we).T
     return y, ya
 
 
@@ -56,18 +61,19 @@ def mxfp8_dgrad_ref(a_codes, a_scales, b_codes, b_scales, seg_offsets, rows=None
     """DGRAD dx[r, n] = sum_k g^[r, k] * w^T_e[n, k]: A = g MXFP8 [M_total, K]
     (blocks along K), B = w^T MXFP8 [E, N, K]; row r belongs to expert e by
     seg_offsets."""
-    g = dequantize_mxfp8_f64(a_codes, a_scales)
-    w = dequantize_mxfp8_f64(b_codes, b_scales)
+    a_codes = np.asarray(a_codes); a_scales = np.asarray(a_scales)
+    b_codes = np.asarray(b_codes); b_scales = np.asarray(b_scales)
     seg = np.asarray(seg_offsets, dtype=np.int64)
     rows = np.arange(int(seg[-1])) if rows is None else np.asarray(rows, dtype=np.int64)
     expert = np.searchsorted(seg, rows, side="right") - 1
-    y = np.zeros((len(rows), w.shape[1]))
+    y = np.zeros((len(rows), b_codes.shape[1]))
     ya = np.zeros_like(y)
     for e in np.unique(expert):
         sel = expert == e
-        ga = g[rows[sel]]
-        y[sel] = ga @ w[e].T
-        ya[sel] = np.abs(ga) @ np.abs(w[e]).T
+        ga = dequantize_mxfp8_f64(a_codes[rows[sel]], a_scales[rows[sel]])
+        we = dequantize_mxfp8_f64(b_codes[e], b_scales[e])
+        y[sel] = ga @ we.T
+        ya[sel] = np.abs(ga) @ np.abs(we).T
     return y, ya
 
 
@@ -95,10 +101,12 @@ def mxfp8_wgrad_ref(a_codes, a_scales, b_codes, b_scales, seg_offsets, M, N, exp
     return np.array(outs).reshape(-1, M, N), np.array(outa).reshape(-1, M, N)
 
 
-def within_tolerance(y, y_ref, y_abs):
-    """Element-wise accept rule; returns (all_ok, worst excess ratio)."""
+def within_tolerance(y, y_ref, y_abs, abs_floor=ABS_FLOOR):
+    """Element-wise accept rule; returns (all_ok, worst excess ratio).
+    ``abs_floor`` replaces 2^-20 for a product computed on hardware whose
+    accumulation is known to be coarser (stated where it is used)."""
     y = np.asarray(y, dtype=np.float64)
-    bound = REL_TOL * np.abs(y_ref) + ABS_FLOOR * y_abs
+    bound = REL_TOL * np.abs(y_ref) + abs_floor * y_abs
     err = np.abs(y - y_ref)
     ratio = np.max(err / np.maximum(bound, 1e-300)) if err.size else 0.0
     return bool(np.all(err <= bound)), float(ratio)

@@ -249,20 +249,24 @@ def segmented_layout(seg_offsets, C):
     return mp, base
 
 
-def _transposed_segments_to_mxfp8(rows_f32, seg_offsets, rnd, seed, stream):
+def _transposed_segments_to_mxfp8(rows_f32, seg_offsets, rnd, seed, stream, segments=None):
     """rows_f32 [M_total, C] in segment order -> for each segment e the
     transpose [C, Mp_e] zero-padded along the token axis, quantized to MXFP8
     with blocks of 32 along tokens starting at the segment start (reading:
     padding zeros do not change a block's largest magnitude).
-    Output index of element (e, c, m) = base_e + c * Mp_e + m."""
-    M_total, C = rows_f32.shape
+    Output index of element (e, c, m) = base_e + c * Mp_e + m.
+    ``segments`` (optional) limits the output to those segments, concatenated
+    in the given order; ``rows_f32`` may then be a callable returning the rows
+    of a segment's range [start, stop)."""
+    C = rows_f32(0, 0).shape[1] if callable(rows_f32) else rows_f32.shape[1]
     mp, base = segmented_layout(seg_offsets, C)
     seg = np.asarray(seg_offsets, dtype=np.int64)
     codes_out, scales_out = [], []
-    for e in range(len(seg) - 1):
+    for e in (range(len(seg) - 1) if segments is None else segments):
         Me = int(seg[e + 1] - seg[e])
         Z = np.zeros((C, mp[e]), dtype=F32)
-        Z[:, :Me] = rows_f32[seg[e]:seg[e + 1]].T
+        rows = rows_f32(seg[e], seg[e + 1]) if callable(rows_f32) else rows_f32[seg[e]:seg[e + 1]]
+        Z[:, :Me] = rows.T
         idx = (np.uint64(base[e]) + np.arange(C * mp[e], dtype=np.uint64)).reshape(C, mp[e])
         c, s = mxfp8_quantize(Z, idx, rnd, seed, stream)
         codes_out.append(c.reshape(-1))
@@ -271,19 +275,21 @@ def _transposed_segments_to_mxfp8(rows_f32, seg_offsets, rnd, seed, stream):
     return cat(codes_out, np.uint8), cat(scales_out, np.uint8)
 
 
-def quantize_mxfp8_transposed(x, seg_offsets, rnd, seed=0, stream=0):
+def quantize_mxfp8_transposed(x, seg_offsets, rnd, seed=0, stream=0, segments=None):
     """The WGRAD operand g^T: x [M_total, C] holds the dispatched rows in
     expert order; each expert's segment is transposed and quantized along the
     token axis (see _transposed_segments_to_mxfp8)."""
-    return _transposed_segments_to_mxfp8(_f32(x), seg_offsets, rnd, seed, stream)
+    x = np.asarray(x)
+    return _transposed_segments_to_mxfp8(lambda a, b: _f32(x[a:b]), seg_offsets, rnd, seed, stream, segments)
 
 
 # ----------------------------------------------------------------- requant
-def requant_transpose_sr(packed, scales, outer, in_mode, out_fmt, seed, stream, rnd=SR):
+def requant_transpose_sr(packed, scales, outer, in_mode, out_fmt, seed, stream, rnd=SR, item0=0):
     """Dequantize -> transpose -> requantize with stochastic rounding
     (section "Re-quantization with stochastic rounding").
     Input NVFP4 [B, R, C] (blocks along C); output [B, C, R] with blocks along
-    R, the old column axis.  Output index idx = b*C*R + c*R + r.
+    R, the old column axis.  Output index idx = b*C*R + c*R + r, where b
+    counts from ``item0`` (so a slice of the batch can be checked on its own).
 
     out_fmt MXFP8: mxfp8_quantize of Z = x^T.
     out_fmt NVFP4 (reading): a new outer scale s_t' = f32(max|Z| / 2688) per
@@ -297,7 +303,7 @@ def requant_transpose_sr(packed, scales, outer, in_mode, out_fmt, seed, stream, 
     C = 2 * C2
     xh = dequantize_nvfp4(packed, scales, outer, in_mode)
     Z = np.ascontiguousarray(np.transpose(xh, (0, 2, 1)))         # [B, C, R] float32
-    idx = np.arange(B * C * R, dtype=np.uint64).reshape(B, C, R)
+    idx = (np.uint64(int(item0) * C * R) + np.arange(B * C * R, dtype=np.uint64)).reshape(B, C, R)
     if out_fmt == MXFP8:
         assert R % MXFP8_BLOCK == 0
         return mxfp8_quantize(Z, idx, rnd, seed, stream)
@@ -325,16 +331,19 @@ def requant_transpose_sr(packed, scales, outer, in_mode, out_fmt, seed, stream, 
 
 
 def requant_transpose_sr_segmented(packed, scales, outer, in_mode, row_gather, seg_offsets,
-                                   seed, stream, rnd=SR):
+                                   seed, stream, rnd=SR, segments=None):
     """The WGRAD operand x_q^T: input NVFP4 [T, C] (one row per token, per-row
     or per-tensor outer scale); dispatched row m of the output is token
     row_gather[m]; rows are grouped into expert segments by seg_offsets; each
     segment is dequantized, transposed and requantized to MXFP8 along the
     token axis as in _transposed_segments_to_mxfp8."""
     packed = np.asarray(packed)
-    T, C2 = packed.shape
-    xh = dequantize_nvfp4(packed[None], np.asarray(scales)[None],
-                          np.asarray(outer).reshape(1, -1) if in_mode == OUTER_ROW else np.asarray(outer).reshape(1),
-                          in_mode)[0]
-    rows = xh[np.asarray(row_gather, dtype=np.int64)]
-    return _transposed_segments_to_mxfp8(rows, seg_offsets, rnd, seed, stream)
+    scales = np.asarray(scales)
+    outer = np.asarray(outer)
+    gather = np.asarray(row_gather, dtype=np.int64)
+
+    def rows(a, b):
+        tok = gather[a:b]
+        o = outer[tok].reshape(1, -1) if in_mode == OUTER_ROW else outer.reshape(1)
+        return dequantize_nvfp4(packed[tok][None], scales[tok][None], o, in_mode)[0]
+    return _transposed_segments_to_mxfp8(rows, seg_offsets, rnd, seed, stream, segments)

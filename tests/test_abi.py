@@ -1,0 +1,127 @@
+"""The C ABI without a GPU: the library loads, exports every entry point the
+header declares, and rejects invalid arguments on the host before any HIP
+call (the documented status codes)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+from block_scaled_bit_quantize_amd import _lib
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "bsq.h")
+
+OK, E_NULL, E_SHAPE, E_ALIGN, E_DTYPE, E_ENUM, E_WORKSPACE, E_LAUNCH = range(8)
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(_lib.library_path()):
+        from block_scaled_bit_quantize_amd.build import build
+        build()
+    return _lib.load_library()
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(bsq_\w+)\s*\(", text)))
+
+
+def test_every_declared_symbol_is_exported(lib):
+    names = declared_functions()
+    assert len(names) >= 14
+    for n in names:
+        assert hasattr(lib, n), n
+        assert n in _lib.SIGNATURES, f"binding lacks {n}"
+    assert set(_lib.SIGNATURES) == set(names)
+
+
+def test_status_strings_and_version(lib):
+    for s in range(8):
+        assert lib.bsq_status_string(s)
+    assert lib.bsq_status_string(99) == b"unknown status"
+    assert lib.bsq_version() == 100
+
+
+FAKE = 0x10000  # a 16-byte aligned non-null value; never dereferenced on these paths
+
+
+def test_quantize_nvfp4_validation(lib):
+    q = lib.bsq_quantize_nvfp4
+    assert q(FAKE, 7, 1, 1, 16, 0, None, FAKE, FAKE, FAKE, FAKE, 256, None) == E_DTYPE
+    assert q(FAKE, 1, 1, 1, 16, 9, None, FAKE, FAKE, FAKE, FAKE, 256, None) == E_ENUM
+    assert q(FAKE, 1, 1, 1, 24, 1, None, FAKE, FAKE, FAKE, None, 0, None) == E_SHAPE
+    assert q(FAKE, 1, 1, 1, 32784, 1, None, FAKE, FAKE, FAKE, None, 0, None) == E_SHAPE
+    assert q(FAKE, 1, -1, 1, 16, 1, None, FAKE, FAKE, FAKE, None, 0, None) == E_SHAPE
+    assert q(None, 1, 1, 1, 16, 1, None, FAKE, FAKE, FAKE, None, 0, None) == E_NULL
+    assert q(FAKE, 1, 1, 1, 16, 2, None, FAKE, FAKE, FAKE, None, 0, None) == E_NULL      # GIVEN needs outer_in
+    assert q(FAKE + 8, 1, 1, 1, 16, 1, None, FAKE, FAKE, FAKE, None, 0, None) == E_ALIGN
+    assert q(FAKE, 1, 1, 1, 16, 0, None, FAKE, FAKE, FAKE, None, 0, None) == E_NULL      # TENSOR needs ws
+    assert q(FAKE, 1, 1, 1, 16, 0, None, FAKE, FAKE, FAKE, FAKE, 4, None) == E_WORKSPACE
+    assert q(None, 1, 0, 1, 16, 1, None, None, None, None, None, 0, None) == OK          # empty batch: no work
+    assert lib.bsq_quantize_nvfp4_workspace(3, 4, 16, 0) >= 12
+    assert lib.bsq_quantize_nvfp4_workspace(3, 4, 16, 1) == 0
+
+
+def test_quantize_mxfp8_validation(lib):
+    q = lib.bsq_quantize_mxfp8
+    assert q(FAKE, 1, 4, 48, 0, None, 0, 1, 0, 0, FAKE, FAKE, None, 0, None) == E_SHAPE
+    assert q(FAKE, 1, 4, 64, 0, None, 0, 5, 0, 0, FAKE, FAKE, None, 0, None) == E_ENUM
+    assert q(FAKE, 3, 4, 64, 0, None, 0, 1, 0, 0, FAKE, FAKE, None, 0, None) == E_DTYPE
+    assert q(FAKE, 1, 4, 64, 2, None, 0, 1, 0, 0, FAKE, FAKE, None, 0, None) == E_ENUM
+    assert q(FAKE, 1, 4, 96, 1, None, 0, 1, 0, 0, FAKE, FAKE, FAKE, 1 << 20, None) == E_SHAPE   # cols % 64
+    assert q(FAKE, 1, 4, 64, 1, FAKE, 0, 1, 0, 0, FAKE, FAKE, FAKE, 1 << 20, None) == E_SHAPE   # 0 segments
+    assert q(FAKE, 1, 4, 64, 1, None, 0, 1, 0, 0, FAKE, FAKE, None, 0, None) == E_NULL
+    assert q(FAKE, 1, 4, 64, 1, None, 0, 1, 0, 0, FAKE, FAKE, FAKE, 8, None) == E_WORKSPACE
+    assert q(FAKE, 1, 4, 64, 0, None, 0, 1, 0, 0, FAKE + 4, FAKE, None, 0, None) == E_ALIGN
+
+
+def test_requant_validation(lib):
+    r = lib.bsq_requant_transpose_sr
+    args = lambda **kw: [kw.get(k, v) for k, v in [
+        ("codes", FAKE), ("scales", FAKE), ("outer", FAKE), ("in_mode", 0), ("batch", 1), ("rows", 64),
+        ("cols", 64), ("in_rows", 64), ("gather", None), ("seg", None), ("nseg", 0), ("fmt", 1), ("rnd", 1),
+        ("seed", 0), ("sid", 0), ("oc", FAKE), ("os", FAKE), ("oo", FAKE), ("ws", FAKE), ("wsb", 1 << 20),
+        ("stream", None)]]
+    assert r(*args(in_mode=2)) == E_ENUM
+    assert r(*args(fmt=3)) == E_ENUM
+    assert r(*args(rnd=4)) == E_ENUM
+    assert r(*args(cols=96)) == E_SHAPE
+    assert r(*args(rows=48)) == E_SHAPE                        # MXFP8 needs rows % 32
+    assert r(*args(in_rows=65)) == E_SHAPE
+    assert r(*args(codes=None)) == E_NULL
+    assert r(*args(oc=FAKE + 1)) == E_ALIGN
+    assert r(*args(fmt=0, oo=None)) == E_NULL
+    assert r(*args(fmt=0, wsb=0)) == E_WORKSPACE
+    assert r(*args(gather=FAKE)) == E_NULL                     # gather needs seg_offsets
+    assert r(*args(gather=FAKE, seg=FAKE, nseg=2, fmt=0)) == E_SHAPE
+    assert r(*args(gather=FAKE, seg=FAKE, nseg=2, wsb=16)) == E_WORKSPACE
+
+
+def test_gemm_and_route_validation(lib):
+    g = lib.bsq_grouped_gemm_nvfp4
+    base = [FAKE, FAKE, FAKE, 1, 8, None, FAKE, FAKE, FAKE, FAKE, 2, 16, 256, 256, FAKE, 1, None]
+    def call(i, v):
+        a = list(base); a[i] = v; return g(*a)
+    assert call(12, 200) == E_SHAPE          # N % 256
+    assert call(13, 96) == E_SHAPE           # K % 64
+    assert call(10, 0) == E_SHAPE            # E >= 1
+    assert call(0, None) == E_NULL
+    assert call(14, FAKE + 2) == E_ALIGN
+    assert call(15, 7) == E_DTYPE
+    m = lib.bsq_grouped_gemm_mxfp8
+    assert m(2, FAKE, FAKE, FAKE, FAKE, FAKE, 2, 256, 256, 128, FAKE, 1, None) == E_ENUM
+    assert m(0, FAKE, FAKE, FAKE, FAKE, FAKE, 2, 256, 256, 100, FAKE, 1, None) == E_SHAPE
+    mn = lib.bsq_grouped_gemm_mxfp8_native
+    assert mn(0, FAKE, FAKE, FAKE, FAKE, FAKE, 2, 256, 256, 64, FAKE, 1, None) == E_SHAPE   # K % 128
+    assert mn(0, FAKE, FAKE, FAKE, FAKE, FAKE, 2, 256, 256, 128, FAKE, 3, None) == E_DTYPE
+    assert m(1, FAKE, FAKE, FAKE, FAKE, FAKE, 2, 200, 256, 0, FAKE, 0, None) == E_SHAPE
+    assert m(0, FAKE, None, FAKE, FAKE, FAKE, 2, 256, 256, 128, FAKE, 1, None) == E_NULL
+    assert m(0, FAKE, FAKE, FAKE, FAKE, FAKE, 2, 256, 256, 128, FAKE, 5, None) == E_DTYPE
+    rt = lib.bsq_route
+    assert rt(FAKE, 10, 0, 4, FAKE, FAKE, FAKE, FAKE, 1 << 20, None) == E_SHAPE
+    assert rt(FAKE, 10, 2, 2000, FAKE, FAKE, FAKE, FAKE, 1 << 20, None) == E_SHAPE
+    assert rt(FAKE, 10, 2, 4, FAKE, None, FAKE, FAKE, 1 << 20, None) == E_NULL
+    assert rt(FAKE, 10, 2, 4, FAKE, FAKE, FAKE, FAKE, 4, None) == E_WORKSPACE

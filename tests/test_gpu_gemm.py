@@ -1,0 +1,239 @@
+"""GPU parity of the expert grouped GEMMs against the oracle's float64
+product of the same dequantized operands (accept rule of oracle.gemm), at
+small sizes with ragged and empty segments and at the workloads' full sizes on
+sampled output rows. Full-size operands hold oracle-quantized data wherever an
+output is checked and valid random bytes elsewhere."""
+import numpy as np
+import pytest
+import torch
+
+import block_scaled_bit_quantize_amd as bsq
+import synth
+from oracle import gemm as G
+from oracle import quant as Q
+from oracle.route import route as oroute
+
+from _gpu_util import DEV, filler_mxfp8, filler_nvfp4, h, log, t
+
+pytestmark = pytest.mark.gpu
+f32 = np.float32
+
+
+# The scaled-FP8 MFMA keeps about 15 bits below the largest product of each
+# instruction (measured on gfx950), so its variant of the MXFP8 GEMM is held
+# to a floor of 2^-14 * sum|x w| instead of 2^-20.
+NATIVE_FP8_FLOOR = 2.0 ** -14
+
+
+def _check(y, yref, yabs, what, floor=G.ABS_FLOOR):
+    """y: the float32 GEMM result (before output rounding) vs the float64 reference."""
+    ok, ratio = G.within_tolerance(y, yref, yabs, floor)
+    rel = G.max_rel_error(y, yref)
+    print(f"[{what}] worst bound ratio {ratio:.3f}, max rel err {rel:.2e}", flush=True)
+    assert ok, f"{what}: outside tolerance (ratio {ratio})"
+
+
+def _check_bf16(y16, y32, what):
+    """The bf16 output is the round-to-nearest-even of the float32 result."""
+    want = synth.bf16_bits(np.asarray(y32, dtype=f32))
+    got = np.asarray(y16).view(np.uint16)
+    assert np.array_equal(got, want), f"{what}: bf16 output differs from RNE(float32 output)"
+
+
+def _nvfp4(*args, **kw):
+    """Run the NVFP4 GEMM twice (float32 and bf16 outputs)."""
+    y32 = bsq.grouped_gemm_nvfp4(*args, out_dtype=torch.float32, **kw)
+    y16 = bsq.grouped_gemm_nvfp4(*args, out_dtype=torch.bfloat16, **kw)
+    return y32, y16
+
+
+@pytest.mark.parametrize("per_row", [True, False])
+def test_gemm_nvfp4_small_ragged(per_row):
+    log(f"gemm nvfp4 small per_row={per_row}")
+    rng = np.random.default_rng(5)
+    T, E, N, K = 400, 5, 512, 384
+    seg = np.array([0, 0, 300, 317, 830, 831], dtype=np.int64)
+    row_index = rng.integers(0, T, size=831).astype(np.int32)
+    x = rng.standard_t(3, (T, K)).astype(f32)
+    w = (rng.standard_normal((E, N, K)) * 0.02).astype(f32)
+    if per_row:
+        ap, as_, ao = Q.quantize_nvfp4(x[None], Q.OUTER_ROW)
+        ao = ao[0]
+    else:
+        ap, as_, ao = Q.quantize_nvfp4(x[None], Q.OUTER_TENSOR)
+    bp, bs, bo = Q.quantize_nvfp4(w, Q.OUTER_TENSOR)
+    y32, y16 = _nvfp4(t(ap[0]), t(as_[0]), t(ao), t(bp), t(bs), t(bo), t(seg), 831, row_index=t(row_index))
+    yref, yabs = G.grouped_gemm_nvfp4_ref(ap[0], as_[0], ao, row_index, bp, bs, bo, seg)
+    _check(h(y32), yref, yabs, "nvfp4 small")
+    _check_bf16(h(y16.view(torch.int16)), h(y32), "nvfp4 small")
+
+
+def test_gemm_nvfp4_workload1():
+    """256x256x256: A = the SR-requantized X^T (NVFP4, seed 0), B = W RTN."""
+    log("gemm nvfp4 workload1")
+    X, W = synth.workload1()
+    p, s, o = Q.quantize_nvfp4(X[None], Q.OUTER_TENSOR)
+    ac, as_, ao = Q.requant_transpose_sr(p, s, o, Q.OUTER_TENSOR, Q.NVFP4, 0, 0)
+    bp, bs, bo = Q.quantize_nvfp4(W[None], Q.OUTER_TENSOR)
+    seg = np.array([0, 256], dtype=np.int64)
+    y32, y16 = _nvfp4(t(ac[0]), t(as_[0]), t(ao), t(bp), t(bs), t(bo), t(seg), 256)
+    yref, yabs = G.grouped_gemm_nvfp4_ref(ac[0], as_[0], ao, None, bp, bs, bo, seg)
+    _check(h(y32), yref, yabs, "nvfp4 workload1 (X^T_sr W^T)")
+    _check_bf16(h(y16.view(torch.int16)), h(y32), "nvfp4 workload1")
+    # the forward product X_q W_q^T as well
+    y32, y16 = _nvfp4(t(p[0]), t(s[0]), t(o), t(bp), t(bs), t(bo), t(seg), 256)
+    yref, yabs = G.grouped_gemm_nvfp4_ref(p[0], s[0], o, None, bp, bs, bo, seg)
+    _check(h(y32), yref, yabs, "nvfp4 workload1 (X_q W_q^T)")
+    _check_bf16(h(y16.view(torch.int16)), h(y32), "nvfp4 workload1 forward")
+
+
+def _moe_full(wl, sample_experts):
+    """Full-size NVFP4 grouped GEMM of workload 2 or 5 with sampled rows."""
+    p = synth.WORKLOADS[wl]
+    T, K, E, N = p["tokens"], p["hidden"], p["experts"], p["ffn"]
+    log(f"gemm nvfp4 workload{wl}: generate inputs")
+    ids = synth.moe_routing(wl)
+    row_index, seg, _ = oroute(ids, E)
+    x = synth.moe_activations(wl)
+    w = synth.moe_weights(wl)
+    rng = np.random.default_rng(wl)
+    ac, as_ = filler_nvfp4(rng, (T,), K)
+    ao = np.full(T, 2e-3, f32)
+    bc, bs = filler_nvfp4(rng, (E, N), K)
+    bo = np.full(E, 1e-5, f32)
+    lens = np.diff(seg)
+    experts = sorted(set(sample_experts) | {int(np.argmax(lens)), int(np.argmin(np.where(lens > 0, lens, 1 << 30)))})
+    rows = []
+    for e in experts:
+        if lens[e] == 0:
+            continue
+        cand = np.r_[seg[e], seg[e + 1] - 1, rng.integers(seg[e], seg[e + 1], size=2)]
+        rows.extend(cand.tolist())
+    rows = np.unique(np.array(rows, dtype=np.int64))
+    toks = np.unique(row_index[rows])
+    qa, qs, qo = Q.quantize_nvfp4(synth.bf16_to_f32(x[toks])[None], Q.OUTER_ROW)
+    ac[toks], as_[toks], ao[toks] = qa[0], qs[0], qo[0]
+    for e in experts:
+        qb, qbs, qbo = Q.quantize_nvfp4(synth.bf16_to_f32(w[e])[None], Q.OUTER_TENSOR)
+        bc[e], bs[e], bo[e] = qb[0], qbs[0], qbo[0]
+    del x, w
+    log(f"gemm nvfp4 workload{wl}: run (M_total={seg[-1]}, N={N}, K={K}, E={E})")
+    y32, y16 = _nvfp4(t(ac), t(as_), t(ao), t(bc), t(bs), t(bo), t(seg), int(seg[-1]), row_index=t(row_index))
+    ys = h(y32[t(rows)])
+    yref, yabs = G.grouped_gemm_nvfp4_ref(ac, as_, ao, row_index, bc, bs, bo, seg, rows=rows)
+    _check(ys, yref, yabs, f"nvfp4 workload{wl} sampled {len(rows)} rows")
+    # bf16 output of the whole launch vs the float32 one, compared on the GPU
+    assert torch.equal(y16, y32.to(torch.bfloat16)), "bf16 output differs from RNE(float32 output)"
+
+
+def test_gemm_nvfp4_workload2_full():
+    _moe_full(2, [0, 21, 63])
+
+
+def test_gemm_nvfp4_workload5_full():
+    _moe_full(5, [0, 64, 127])
+
+
+def _mxfp8_from(rng, x, rnd=Q.SR):
+    return Q.quantize_mxfp8(x, rnd, int(rng.integers(1 << 30)), 1)
+
+
+@pytest.mark.parametrize("native", [False, True])
+def test_gemm_mxfp8_dgrad_small(native):
+    log(f"gemm mxfp8 dgrad small native={native}")
+    floor = NATIVE_FP8_FLOOR if native else G.ABS_FLOOR
+    rng = np.random.default_rng(6)
+    E, N, K = 4, 512, 384
+    seg = np.array([0, 100, 100, 357, 613], dtype=np.int64)
+    g = (rng.standard_normal((613, K)) * 1e-3).astype(f32)
+    wt = (rng.standard_normal((E * N, K)) * 0.02).astype(f32)
+    ac, as_ = _mxfp8_from(rng, g)
+    bc, bs = _mxfp8_from(rng, wt)
+    bc, bs = bc.reshape(E, N, K), bs.reshape(E, N, K // 32)
+    y = bsq.grouped_gemm_mxfp8(False, t(ac), t(as_), t(bc), t(bs), t(seg), 613, N, K, out_dtype=torch.float32,
+                               native=native)
+    y16 = bsq.grouped_gemm_mxfp8(False, t(ac), t(as_), t(bc), t(bs), t(seg), 613, N, K, native=native)
+    yref, yabs = G.mxfp8_dgrad_ref(ac, as_, bc, bs, seg)
+    _check(h(y), yref, yabs, f"mxfp8 dgrad small native={native}", floor)
+    _check_bf16(h(y16.view(torch.int16)), h(y), "mxfp8 dgrad small")
+
+
+@pytest.mark.parametrize("native", [False, True])
+def test_gemm_mxfp8_wgrad_small(native):
+    log(f"gemm mxfp8 wgrad small native={native}")
+    floor = NATIVE_FP8_FLOOR if native else G.ABS_FLOOR
+    rng = np.random.default_rng(7)
+    M, N = 256, 512
+    seg = np.array([0, 0, 45, 245, 245, 374], dtype=np.int64)       # Kp = 0, 64, 224, 0, 160
+    ga = (rng.standard_normal((374, M)) * 1e-3).astype(f32)
+    xb = rng.standard_normal((374, N)).astype(f32)
+    ac, as_ = Q.quantize_mxfp8_transposed(ga, seg, Q.SR, 1, 2)
+    bc, bs = Q.quantize_mxfp8_transposed(xb, seg, Q.SR, 1, 3)
+    y = bsq.grouped_gemm_mxfp8(True, t(ac), t(as_), t(bc), t(bs), t(seg), M, N, native=native)
+    yref, yabs = G.mxfp8_wgrad_ref(ac, as_, bc, bs, seg, M, N)
+    _check(h(y), yref, yabs, f"mxfp8 wgrad small native={native}", floor)
+    y16 = bsq.grouped_gemm_mxfp8(True, t(ac), t(as_), t(bc), t(bs), t(seg), M, N, native=native,
+                                 out_dtype=torch.bfloat16)
+    assert torch.equal(y16, y.to(torch.bfloat16))
+
+
+@pytest.mark.parametrize("native", [False, True])
+def test_gemm_mxfp8_workload4_full(native):
+    """DGRAD dx[131072, 4096] = g w_q and WGRAD dw[64, 1536, 4096] = g^T x_q at
+    full size with workload 2's routing; sampled rows / experts."""
+    log(f"gemm mxfp8 workload4 native={native}: setup")
+    floor = NATIVE_FP8_FLOOR if native else G.ABS_FLOOR
+    E, T, Kx, Ng = 64, 16384, 4096, 1536
+    ids = synth.moe_routing(2)
+    row_index, seg, _ = oroute(ids, E)
+    M_total = int(seg[-1])
+    rng = np.random.default_rng(44)
+    lens = np.diff(seg)
+    experts = [0, 33, 63]
+    # DGRAD: A = g rows [M_total, 1536], B = w_q^T [E, 4096, 1536]
+    ac, as_ = filler_mxfp8(rng, M_total * Ng)
+    ac, as_ = ac.reshape(M_total, Ng), as_.reshape(M_total, Ng // 32)
+    bc, bs = filler_mxfp8(rng, E * Kx * Ng)
+    bc, bs = bc.reshape(E, Kx, Ng), bs.reshape(E, Kx, Ng // 32)
+    rows = np.unique(np.concatenate([[seg[e], seg[e + 1] - 1, rng.integers(seg[e], seg[e + 1])] for e in experts]))
+    g = synth.output_grad(M_total, Ng)
+    gq, gs = Q.quantize_mxfp8(synth.bf16_to_f32(g[rows]), Q.SR, 42, 1)
+    ac[rows], as_[rows] = gq, gs
+    W = synth.moe_weights(2)
+    for e in experts:
+        p, s, o = Q.quantize_nvfp4(synth.bf16_to_f32(W[e])[None], Q.OUTER_TENSOR)
+        c, sc = Q.requant_transpose_sr(p, s, o, Q.OUTER_TENSOR, Q.MXFP8, 42, 0, item0=e)
+        bc[e], bs[e] = c[0], sc[0]
+    log("gemm mxfp8 workload4: dgrad")
+    y = bsq.grouped_gemm_mxfp8(False, t(ac), t(as_), t(bc), t(bs), t(seg), M_total, Kx, Ng, out_dtype=torch.float32,
+                               native=native)
+    ys = h(y[t(rows)])
+    del y
+    yref, yabs = G.mxfp8_dgrad_ref(ac, as_, bc, bs, seg, rows=rows)
+    _check(ys, yref, yabs, f"mxfp8 dgrad workload4 native={native}", floor)
+    # WGRAD: A = g^T per expert [1536, Kp_e], B = x_q^T per expert [4096, Kp_e]
+    log("gemm mxfp8 workload4: wgrad setup")
+    mpa, na = bsq.padded_segment_layout(seg, Ng)
+    mpb, nb = bsq.padded_segment_layout(seg, Kx)
+    A, As = filler_mxfp8(rng, na)
+    B, Bs = filler_mxfp8(rng, nb)
+    _, basea = Q.segmented_layout(seg, Ng)
+    _, baseb = Q.segmented_layout(seg, Kx)
+    gf = synth.bf16_to_f32(g).reshape(M_total, Ng)
+    x = synth.moe_activations(2)
+    for e in experts:
+        c, sc = Q.quantize_mxfp8_transposed(gf, seg, Q.SR, 42, 2, segments=[e])
+        A[basea[e]:basea[e] + c.size], As[basea[e] // 32:basea[e] // 32 + sc.size] = c, sc
+        toks = row_index[seg[e]:seg[e + 1]]
+        p, s, o = Q.quantize_nvfp4(synth.bf16_to_f32(x[toks])[None], Q.OUTER_ROW)
+        # the gathered rows of expert e as their own token table
+        c, sc = Q.requant_transpose_sr_segmented(p[0], s[0], o[0], Q.OUTER_ROW,
+                                                 np.arange(len(toks)), np.array([0, len(toks)]), 42, 3)
+        B[baseb[e]:baseb[e] + c.size], Bs[baseb[e] // 32:baseb[e] // 32 + sc.size] = c, sc
+    del gf, x, g
+    log("gemm mxfp8 workload4: wgrad")
+    dw = bsq.grouped_gemm_mxfp8(True, t(A), t(As), t(B), t(Bs), t(seg), Ng, Kx, native=native)
+    for e in experts:
+        ys = h(dw[e])
+        yref, yabs = G.mxfp8_wgrad_ref(A, As, B, Bs, seg, Ng, Kx, experts=[e])
+        _check(ys, yref[0], yabs[0], f"mxfp8 wgrad workload4 expert {e} native={native}", floor)

@@ -1,0 +1,366 @@
+"""GPU parity of the quantizers, requantization, RNG and routing against the
+CPU oracle (bit-exact bytes), at small sizes spanning several tiles with
+ragged tails and at the workloads' full sizes on sampled outputs."""
+import numpy as np
+import pytest
+import torch
+
+import block_scaled_bit_quantize_amd as bsq
+import synth
+from oracle import formats as F
+from oracle import quant as Q
+from oracle.rng import sr_bits16
+from oracle.route import route as oroute
+
+from _gpu_util import DEV, bf16_t, h, log, t
+
+pytestmark = pytest.mark.gpu
+f32 = np.float32
+
+
+def _data(rng, shape, kind):
+    if kind == "normal":
+        return rng.standard_normal(shape).astype(f32)
+    if kind == "wide":
+        return (rng.standard_normal(shape) * np.exp(rng.uniform(-30, 30, shape))).astype(f32)
+    if kind == "zeros_mix":
+        x = rng.standard_normal(shape).astype(f32)
+        x.reshape(-1, 16)[::3] = 0.0
+        x.reshape(-1, 16)[1::7] *= f32(1e-38)
+        return x
+    if kind == "t3":
+        return rng.standard_t(3, shape).astype(f32)
+    raise ValueError(kind)
+
+
+def test_rng_bits_match_oracle():
+    for seed, stream, first in [(0, 0, 0), (42, 1, 8 * 12345 + 3), (2**63 + 5, 2**40 + 7, 2**35 - 11)]:
+        log(f"rng seed={seed} stream={stream} first={first}")
+        g = h(bsq.rng_bits16(seed, stream, first, 4099)).astype(np.int64) & 0xFFFF
+        o = sr_bits16(seed, stream, np.arange(4099, dtype=np.uint64) + np.uint64(first))
+        assert np.array_equal(g, o)
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+@pytest.mark.parametrize("mode", ["tensor", "row", "given"])
+@pytest.mark.parametrize("shape,kind", [((1, 3, 48), "normal"), ((2, 5, 256), "wide"), ((3, 7, 1040), "zeros_mix"),
+                                        ((2, 33, 4096), "t3"), ((1, 2, 8192), "normal"), ((1, 3, 32768), "t3")])
+def test_quantize_nvfp4_small(dtype, mode, shape, kind):
+    log(f"quantize_nvfp4 {dtype} {mode} {shape} {kind}")
+    rng = np.random.default_rng(hash((dtype, mode, shape, kind)) % 2**32)
+    x = _data(rng, shape, kind)
+    if dtype == "bf16":
+        bits = synth.bf16_bits(x)
+        x = synth.bf16_to_f32(bits).reshape(shape)
+        xd = bf16_t(bits.reshape(shape))
+    else:
+        xd = t(x)
+    outer = (np.abs(rng.standard_normal(shape[0])) * 0.01 + 1e-3).astype(f32) if mode == "given" else None
+    m = {"tensor": Q.OUTER_TENSOR, "row": Q.OUTER_ROW, "given": Q.OUTER_GIVEN}[mode]
+    gc, gs, go = bsq.quantize_nvfp4(xd, mode, t(outer) if outer is not None else None)
+    oc, os_, oo = Q.quantize_nvfp4(x, m, outer)
+    assert np.array_equal(h(gc), oc)
+    assert np.array_equal(h(gs), os_)
+    assert np.array_equal(h(go), np.asarray(oo).reshape(-1))
+
+
+def test_quantize_nvfp4_edge_cases():
+    # empty tensors, all zeros, largest bf16 values, single block
+    log("quantize_nvfp4 edges")
+    c, s, o = bsq.quantize_nvfp4(torch.zeros((2, 0, 32), device=DEV), "tensor")
+    assert h(o).tolist() == [1.0, 1.0]
+    c, s, o = bsq.quantize_nvfp4(torch.zeros((0, 4, 32), device=DEV), "row")
+    assert c.numel() == 0
+    c, s, o = bsq.quantize_nvfp4(torch.zeros((3, 4, 32), device=DEV), "row")
+    assert not h(c).any() and not h(s).any() and np.all(h(o) == 1.0)
+    big = np.full((1, 2, 16), 3.3e38, f32)
+    big[0, 1, 3] = -1e-30
+    gc, gs, go = bsq.quantize_nvfp4(t(big), "row")
+    oc, os_, oo = Q.quantize_nvfp4(big, Q.OUTER_ROW)
+    assert np.array_equal(h(gc), oc) and np.array_equal(h(gs), os_) and np.array_equal(h(go), oo.reshape(-1))
+
+
+def test_pages_examples_on_gpu():
+    """The worked examples of the pages, through the GPU quantizer."""
+    log("pages examples")
+    row = np.zeros((1, 1, 32), f32)
+    row[0, 0, 0] = 593.7                       # Figure 1: scale 96, value 6
+    row[0, 0, 16] = -54.0                      # block max -54 -> -6 with scale 9
+    row[0, 0, 17] = 5.4                        # -> 0.6 -> 0.5 -> 4.5
+    c, s, o = bsq.quantize_nvfp4(t(row), "given", t(np.ones(1, f32)))
+    codes = F.unpack_fp4(h(c))[0, 0]
+    sc = F.e4m3_decode(h(s))[0, 0]
+    assert sc[0] == 96 and F.e2m1_decode(codes[0]) == 6
+    assert sc[1] == 9 and F.e2m1_decode(codes[16]) == -6 and F.e2m1_decode(codes[17]) * 9 == 4.5
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+@pytest.mark.parametrize("rnd", ["rn", "sr"])
+@pytest.mark.parametrize("shape,kind", [((3, 32), "normal"), ((67, 96), "wide"), ((130, 1536), "zeros_mix")])
+def test_quantize_mxfp8_rows_small(dtype, rnd, shape, kind):
+    log(f"quantize_mxfp8 rows {dtype} {rnd} {shape} {kind}")
+    rng = np.random.default_rng(7)
+    x = _data(rng, shape, kind)
+    if dtype == "bf16":
+        bits = synth.bf16_bits(x)
+        x = synth.bf16_to_f32(bits).reshape(shape)
+        xd = bf16_t(bits.reshape(shape))
+    else:
+        xd = t(x)
+    r = Q.RN if rnd == "rn" else Q.SR
+    gc, gs = bsq.quantize_mxfp8(xd, rnd, seed=11, stream_id=1)
+    oc, os_ = Q.quantize_mxfp8(x, r, 11, 1)
+    assert np.array_equal(h(gs), os_)
+    assert np.array_equal(h(gc), oc)
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+@pytest.mark.parametrize("rnd", ["rn", "sr"])
+def test_quantize_mxfp8_transposed_small(dtype, rnd):
+    log(f"quantize_mxfp8 transposed {dtype} {rnd}")
+    rng = np.random.default_rng(8)
+    seg = np.array([0, 0, 45, 245, 245, 374, 375, 631], dtype=np.int64)      # empty, ragged, 1-row segments
+    x = _data(rng, (631, 192), "wide")
+    if dtype == "bf16":
+        bits = synth.bf16_bits(x)
+        x = synth.bf16_to_f32(bits).reshape(x.shape)
+        xd = bf16_t(bits.reshape(x.shape))
+    else:
+        xd = t(x)
+    r = Q.RN if rnd == "rn" else Q.SR
+    _, n = bsq.padded_segment_layout(seg, 192)
+    gc, gs = bsq.quantize_mxfp8(xd, rnd, seed=5, stream_id=2, transpose=True, seg_offsets=t(seg), out_elems=n)
+    oc, os_ = Q.quantize_mxfp8_transposed(x, seg, r, 5, 2)
+    assert np.array_equal(h(gs), os_)
+    assert np.array_equal(h(gc), oc)
+    # no segment table: one segment of all rows
+    _, n1 = bsq.padded_segment_layout([0, 631], 192)
+    gc, gs = bsq.quantize_mxfp8(xd, rnd, seed=5, stream_id=2, transpose=True, out_elems=n1)
+    oc, os_ = Q.quantize_mxfp8_transposed(x, [0, 631], r, 5, 2)
+    assert np.array_equal(h(gc), oc) and np.array_equal(h(gs), os_)
+
+
+@pytest.mark.parametrize("fmt", ["mxfp8", "nvfp4"])
+@pytest.mark.parametrize("rnd", ["rn", "sr"])
+@pytest.mark.parametrize("in_mode", ["tensor", "row"])
+@pytest.mark.parametrize("B,R,C", [(2, 64, 128), (1, 160, 64), (3, 256, 192), (1, 48, 128)])
+def test_requant_batch_small(fmt, rnd, in_mode, B, R, C):
+    if fmt == "mxfp8" and R % 32:
+        pytest.skip("MXFP8 output needs rows % 32 == 0")
+    log(f"requant batch {fmt} {rnd} {in_mode} {(B, R, C)}")
+    rng = np.random.default_rng(B * 1000 + R + C)
+    x = _data(rng, (B, R, C), "t3")
+    im = Q.OUTER_TENSOR if in_mode == "tensor" else Q.OUTER_ROW
+    p, s, o = Q.quantize_nvfp4(x, im)
+    of = Q.MXFP8 if fmt == "mxfp8" else Q.NVFP4
+    r = Q.RN if rnd == "rn" else Q.SR
+    got = bsq.requant_transpose_sr(t(p), t(s), t(np.asarray(o).reshape(-1)), in_mode, fmt, seed=99, stream_id=3, rnd=rnd)
+    want = Q.requant_transpose_sr(p, s, o, im, of, 99, 3, rnd=r)
+    for g, w in zip(got, want):
+        assert np.array_equal(h(g), np.asarray(w).reshape(h(g).shape))
+
+
+def test_requant_workload1_nvfp4_seed0():
+    """Workload 1: 256x256 fp32 with outliers, NVFP4 quantize, dequantize,
+    transpose, SR requantize to NVFP4 with seed 0."""
+    log("requant workload1")
+    X, _ = synth.workload1()
+    p, s, o = Q.quantize_nvfp4(X[None], Q.OUTER_TENSOR)
+    gc, gs, go = bsq.quantize_nvfp4(t(X), "tensor")
+    assert np.array_equal(h(gc), p[0]) and np.array_equal(h(gs), s[0])
+    rc, rs, ro = bsq.requant_transpose_sr(t(p[0]), t(s[0]), t(o), "tensor", "nvfp4", seed=0, stream_id=0)
+    wc, ws, wo = Q.requant_transpose_sr(p, s, o, Q.OUTER_TENSOR, Q.NVFP4, 0, 0)
+    assert np.array_equal(h(rc), wc[0]) and np.array_equal(h(rs), ws[0]) and np.array_equal(h(ro), wo)
+
+
+@pytest.mark.parametrize("rnd", ["rn", "sr"])
+def test_requant_gather_small(rnd):
+    log(f"requant gather {rnd}")
+    rng = np.random.default_rng(21)
+    T, C, E, k = 300, 192, 6, 3
+    x = _data(rng, (1, T, C), "normal")
+    p, s, o = Q.quantize_nvfp4(x, Q.OUTER_ROW)
+    ids = np.argsort(rng.random((T, E)), axis=1)[:, :k]
+    ids[ids == 4] = 5                                  # expert 4 receives nothing
+    ids = np.sort(ids, axis=1)
+    ok = np.all(np.diff(ids, axis=1) > 0, axis=1)
+    ids = ids[ok]
+    Tk = ids.shape[0]
+    row_index, seg, _ = oroute(ids, E)
+    r = Q.RN if rnd == "rn" else Q.SR
+    _, n = bsq.padded_segment_layout(seg, C)
+    gc, gs = bsq.requant_transpose_sr(t(p[0]), t(s[0]), t(o.reshape(-1)), "row", "mxfp8", seed=3, stream_id=3,
+                                      rnd=rnd, row_gather=t(row_index), seg_offsets=t(seg), out_elems=n)
+    wc, ws = Q.requant_transpose_sr_segmented(p[0], s[0], o.reshape(-1), Q.OUTER_ROW, row_index, seg, 3, 3, rnd=r)
+    assert Tk > 0
+    assert np.array_equal(h(gs), ws)
+    assert np.array_equal(h(gc), wc)
+
+
+def test_route_small_and_full():
+    for T, E, k, wl in [(5, 4, 2, None), (1000, 16, 4, None), (16384, 64, 8, 2), (65536, 128, 8, 5)]:
+        log(f"route T={T} E={E} k={k}")
+        if wl is None:
+            rng = np.random.default_rng(T)
+            ids = np.argsort(rng.random((T, E)), axis=1)[:, :k].astype(np.int32)
+        else:
+            ids = synth.moe_routing(wl)
+        ri, seg, pr = bsq.route(t(ids), E)
+        ori, oseg, opr = oroute(ids, E)
+        assert np.array_equal(h(seg), oseg)
+        assert np.array_equal(h(ri), ori)
+        assert np.array_equal(h(pr), opr)
+
+
+# ---------------------------------------------------------------- full sizes, sampled outputs
+@pytest.fixture(scope="module")
+def wl2():
+    log("generate workload 2 inputs")
+    return dict(x=synth.moe_activations(2), w=synth.moe_weights(2), ids=synth.moe_routing(2))
+
+
+def test_quantize_nvfp4_workload2_full(wl2):
+    """Activations per token, weights per expert, at full size; sampled rows
+    (with the oracle's per-expert outer scale from the whole expert)."""
+    log("quantize workload2 activations")
+    x = wl2["x"]
+    gc, gs, go = bsq.quantize_nvfp4(bf16_t(x), "row")
+    rows = np.r_[0, 1, 777, 8191, 16383]
+    xf = synth.bf16_to_f32(x[rows])
+    oc, os_, oo = Q.quantize_nvfp4(xf[None], Q.OUTER_ROW)
+    assert np.array_equal(h(gc[rows]), oc[0]) and np.array_equal(h(gs[rows]), os_[0])
+    assert np.array_equal(h(go)[rows], oo[0])
+    del gc, gs, go
+    log("quantize workload2 weights")
+    w = wl2["w"]
+    gc, gs, go = bsq.quantize_nvfp4(bf16_t(w), "tensor")
+    go = h(go)
+    for e in (0, 31, 63):
+        we = synth.bf16_to_f32(w[e])
+        st = Q.outer_scale_from_amax(np.abs(we).max())
+        assert go[e] == st
+        rows = np.r_[0, 5, 1535]
+        oc, os_, _ = Q.quantize_nvfp4(we[rows][None], Q.OUTER_GIVEN, np.array([st], f32))
+        assert np.array_equal(h(gc[e][rows]), oc[0]) and np.array_equal(h(gs[e][rows]), os_[0])
+
+
+def test_requant_workload3_full(wl2):
+    """64 experts of NVFP4 [1536, 4096] -> MXFP8 [4096, 1536] with seed 42; the
+    input bytes come from the oracle for the checked experts."""
+    log("requant workload3")
+    E, N, K = 64, 1536, 4096
+    rng = np.random.default_rng(3)
+    from _gpu_util import filler_nvfp4
+    codes, scales = filler_nvfp4(rng, (E, N), K)
+    outer = np.full(E, 1e-4, f32)
+    check = (0, 17, 63)
+    for e in check:
+        we = synth.bf16_to_f32(wl2["w"][e])[None]
+        p, s, o = Q.quantize_nvfp4(we, Q.OUTER_TENSOR)
+        codes[e], scales[e], outer[e] = p[0], s[0], o[0]
+    gc, gs = bsq.requant_transpose_sr(t(codes), t(scales), t(outer), "tensor", "mxfp8", seed=42, stream_id=0)
+    for e in check:
+        wc, ws = Q.requant_transpose_sr(codes[e:e + 1], scales[e:e + 1], outer[e:e + 1], Q.OUTER_TENSOR, Q.MXFP8,
+                                        42, 0, item0=e)
+        assert np.array_equal(h(gs[e]), ws[0]) and np.array_equal(h(gc[e]), wc[0])
+
+
+def test_workload4_full_gradient_and_activation_requant(wl2):
+    """Workload 4 at full size: g [131072, 1536] SR-quantized row-wise (stream 1)
+    and transposed per expert (stream 2); x_q^T requantized per expert with a
+    gather (stream 3); sampled rows / experts against the oracle."""
+    ids = wl2["ids"]
+    row_index, seg, _ = oroute(ids, 64)
+    M, Cg = 131072, 1536
+    log("generate workload 4 gradient")
+    g = synth.output_grad(M, Cg)
+    gd = bf16_t(g)
+    log("quantize_mxfp8 rows workload4")
+    gc, gs = bsq.quantize_mxfp8(gd, "sr", seed=42, stream_id=1)
+    rows = np.r_[0, 3, 65535, 131071]
+    gf = synth.bf16_to_f32(g[rows])
+    idx = (rows[:, None].astype(np.uint64) * np.uint64(Cg) + np.arange(Cg, dtype=np.uint64)[None, :])
+    oc, os_ = Q.mxfp8_quantize(gf, idx, Q.SR, 42, 1)
+    assert np.array_equal(h(gc[rows]), oc) and np.array_equal(h(gs[rows]), os_)
+    del gc, gs
+    log("quantize_mxfp8 transposed workload4")
+    mp, n = bsq.padded_segment_layout(seg, Cg)
+    tc, ts = bsq.quantize_mxfp8(gd, "sr", seed=42, stream_id=2, transpose=True, seg_offsets=t(seg), out_elems=n)
+    tc, ts = h(tc), h(ts)
+    _, base = Q.segmented_layout(seg, Cg)
+    sel = [0, 40, 63]
+    gf = synth.bf16_to_f32(g).reshape(M, Cg)
+    for e in sel:
+        oc, os_ = Q.quantize_mxfp8_transposed(gf, seg, Q.SR, 42, 2, segments=[e])
+        assert np.array_equal(tc[base[e]:base[e] + Cg * mp[e]], oc)
+        assert np.array_equal(ts[base[e] // 32:(base[e] + Cg * mp[e]) // 32], os_)
+    del tc, ts, gd, gf
+    log("requant x_q^T gather workload4")
+    T, Kx = 16384, 4096
+    rng = np.random.default_rng(4)
+    from _gpu_util import filler_nvfp4
+    xc, xs = filler_nvfp4(rng, (T,), Kx)
+    xo = np.full(T, 1e-3, f32)
+    toks = np.unique(np.concatenate([row_index[seg[e]:seg[e + 1]] for e in sel]))
+    p, s, o = Q.quantize_nvfp4(synth.bf16_to_f32(wl2["x"][toks])[None], Q.OUTER_ROW)
+    xc[toks], xs[toks], xo[toks] = p[0], s[0], o[0]
+    mpx, nx = bsq.padded_segment_layout(seg, Kx)
+    rc, rs = bsq.requant_transpose_sr(t(xc), t(xs), t(xo), "row", "mxfp8", seed=42, stream_id=3, rnd="sr",
+                                      row_gather=t(row_index), seg_offsets=t(seg), out_elems=nx)
+    rc, rs = h(rc), h(rs)
+    _, basex = Q.segmented_layout(seg, Kx)
+    for e in sel:
+        wc, ws = Q.requant_transpose_sr_segmented(xc, xs, xo, Q.OUTER_ROW, row_index, seg, 42, 3, segments=[e])
+        assert np.array_equal(rc[basex[e]:basex[e] + Kx * mpx[e]], wc)
+        assert np.array_equal(rs[basex[e] // 32:(basex[e] + Kx * mpx[e]) // 32], ws)
+
+
+# ---------------------------------------------------------------- statistics and determinism
+def _sr_mean_test(vals_mean, z, step, n):
+    frac = np.clip((np.abs(z) - np.floor(np.abs(z) / step) * step) / step, 0, 1)
+    sigma = step * np.sqrt(frac * (1 - frac))
+    dev = np.abs(vals_mean - z)
+    bad = dev > 4 * sigma / np.sqrt(n) + step / n + step * 2.0 ** -17
+    pooled = np.sum(vals_mean - z) / np.sqrt(np.sum(sigma ** 2) / n)
+    return int(bad.sum()), float(pooled)
+
+
+def test_sr_unbiased_gpu_workload1():
+    """Workload 1 on the GPU: the mean of the SR requantization (NVFP4 target)
+    over 10^4 seeds lies within 4 sigma of the dequantized input."""
+    log("SR statistics workload1 (10^4 seeds)")
+    X, _ = synth.workload1()
+    p, s, o = Q.quantize_nvfp4(X[None], Q.OUTER_TENSOR)
+    z = Q.dequantize_nvfp4(p, s, o, Q.OUTER_TENSOR)[0].T.astype(np.float64)
+    pc, ps, po = t(p[0]), t(s[0]), t(o)
+    lut = torch.tensor(F.e2m1_decode(np.arange(16)), dtype=torch.float64, device=DEV)
+    slut = torch.tensor(np.nan_to_num(F.e4m3_decode(np.arange(256))), dtype=torch.float64, device=DEV)
+    acc = torch.zeros((256, 256), dtype=torch.float64, device=DEV)
+    n = 10_000
+    for seed in range(n):
+        rc, rs, ro = bsq.requant_transpose_sr(pc, ps, po, "tensor", "nvfp4", seed=seed, stream_id=0)
+        q = torch.stack([rc & 15, rc >> 4], dim=-1).reshape(256, 256).long()
+        acc += lut[q] * slut[rs.long()].repeat_interleave(16, dim=1) * ro.double()
+        if seed == 0:
+            s0, st0 = h(rs), float(h(ro)[0])
+    mean = h(acc) / n
+    step = np.repeat(F.e4m3_decode(s0), 16, axis=1) * st0
+    y = z / step
+    step = step * np.where(np.abs(y) < 2, 0.5, np.where(np.abs(y) < 4, 1.0, 2.0))
+    sat = np.abs(y) >= 6
+    bad, pooled = _sr_mean_test(mean[~sat], z[~sat], step[~sat], n)
+    assert bad <= 16, bad
+    assert abs(pooled) <= 4, pooled
+
+
+def test_determinism():
+    log("determinism")
+    rng = np.random.default_rng(1)
+    x = rng.standard_normal((4, 96, 4096)).astype(f32)
+    a = [h(v) for v in bsq.quantize_nvfp4(t(x), "row")]
+    b = [h(v) for v in bsq.quantize_nvfp4(t(x), "row")]
+    assert all(np.array_equal(u, v) for u, v in zip(a, b))
+    p, s, o = (t(v) for v in a)
+    r1 = [h(v) for v in bsq.requant_transpose_sr(p, s, o, "row", "mxfp8", seed=9, stream_id=1)]
+    r2 = [h(v) for v in bsq.requant_transpose_sr(p, s, o, "row", "mxfp8", seed=9, stream_id=1)]
+    assert all(np.array_equal(u, v) for u, v in zip(r1, r2))
