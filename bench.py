@@ -1,0 +1,311 @@
+"""Benchmark of the block-scaled MoE expert hot path on one MI355X.
+
+One step = the whole hot path of a quantized MoE expert up-projection layer
+("End-to-End 4-Bit Training": NVFP4 forward, MXFP8 backward with stochastic
+requantization) at the sizes of the MoE expert forward workload -- 16384
+tokens, hidden 4096, 64 experts of 4096 x 1536, top-8 routing -- and of its
+backward (weight requantization and backward GEMMs):
+
+  route          top-8 ids -> expert segments
+  quant_x        NVFP4 RTN of x [16384, 4096] bf16, per-token outer scale
+  quant_w        NVFP4 RTN of W [64, 1536, 4096] bf16, per-expert outer scale
+  fprop          NVFP4 grouped GEMM y [131072, 1536] (bf16 out)
+  requant_w      W_q -> MXFP8 W_q^T [64, 4096, 1536], SR seed 42
+  quant_g_rows   g [131072, 1536] bf16 -> MXFP8 rows, SR (stream 1)
+  quant_g_t      g -> MXFP8 g^T per expert, SR (stream 2)
+  requant_x      x_q gathered per expert -> MXFP8 x_q^T, SR (stream 3)
+  dgrad          MXFP8 grouped GEMM dx [131072, 4096] (bf16 out)
+  wgrad          MXFP8 grouped GEMM dw [64, 1536, 4096] (fp32 out)
+
+Inputs are seeded synthetic tensors resident in HBM before timing. Prints one
+JSON line; `value` is the step's GEMM work (FPROP + DGRAD + WGRAD FLOPs) per
+second of the whole step, quantization included.
+"""
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "quantize/requant GB/s (% HBM peak); NVFP4 expert grouped-GEMM TFLOPS (% MFMA)"
+HBM_PEAK_GBS = 8000.0            # MI355X HBM3E, published
+MFMA_PEAK_TFLOPS = {"f16": 2500.0, "bf16": 2500.0, "fp8": 5000.0}  # dense, published
+
+T, H, E, K_TOP, F = 16384, 4096, 64, 8, 1536
+M = T * K_TOP
+
+
+def parse():
+    p = argparse.ArgumentParser()
+    p.add_argument("--gpus", type=int, default=1)
+    p.add_argument("--steps", type=int, default=10)
+    p.add_argument("--warmup", type=int, default=3)
+    p.add_argument("--no-cpu-baseline", action="store_true")
+    p.add_argument("--native-fp8", action="store_true", help="backward GEMMs on the scaled-FP8 MFMA variant")
+    p.add_argument("--stages", default="", help="comma list of stages to run (profiling aid); default all")
+    return p.parse_args()
+
+
+def make_inputs(torch, dev):
+    import numpy as np
+
+    import synth
+    x = synth.moe_activations(2)
+    w = synth.moe_weights(2)
+    ids = synth.moe_routing(2)
+    g = synth.output_grad(M, F)
+    to_bf16 = lambda a: torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).to(dev).view(torch.bfloat16)
+    return dict(x=to_bf16(x), w=to_bf16(w), ids=torch.from_numpy(ids).to(dev), g=to_bf16(g))
+
+
+def algorithmic(seg_host):
+    """Algorithmic bytes (each input read once, each output written once) or
+    FLOPs of one call of each stage."""
+    mp = [(int(seg_host[e + 1] - seg_host[e]) + 31) // 32 * 32 for e in range(E)]
+    smp = sum(mp)
+    nv = lambda rows, cols: rows * (cols // 2 + cols // 16)          # NVFP4 codes + scales
+    mx = lambda elems: elems + elems // 32                            # MXFP8 codes + scales
+    gemm = 2.0 * M * F * H
+    return {
+        "route": ("GB/s", T * K_TOP * 4 + M * 4 * 2 + (E + 1) * 8),
+        "quant_x": ("GB/s", T * H * 2 + nv(T, H) + T * 4),
+        "quant_w": ("GB/s", E * F * H * 2 + nv(E * F, H) + E * 4),
+        "fprop": ("TFLOP/s", gemm),
+        "requant_w": ("GB/s", nv(E * F, H) + E * 4 + mx(E * H * F)),
+        "quant_g_rows": ("GB/s", M * F * 2 + mx(M * F)),
+        "quant_g_t": ("GB/s", M * F * 2 + mx(F * smp)),
+        "requant_x": ("GB/s", nv(T, H) + T * 4 + M * 4 + mx(H * smp)),
+        "dgrad": ("TFLOP/s", gemm),
+        "wgrad": ("TFLOP/s", gemm),
+    }
+
+
+def kernel_sha(*files):
+    h = hashlib.sha256()
+    for f in files:
+        h.update(open(os.path.join(ROOT, "block_scaled_bit_quantize_amd", "csrc", f), "rb").read())
+    return h.hexdigest()[:16]
+
+
+def read_traffic(stage, sha):
+    """HBM bytes per launch of `stage` from a committed rocprofv3 counter summary
+    (profiles/traffic_<stage>.txt, lines 'key: value'); None when absent or
+    taken on a different kernel source."""
+    path = os.path.join(ROOT, "profiles", f"traffic_{stage}.txt")
+    if not os.path.exists(path):
+        return None
+    kv = {}
+    for line in open(path):
+        if ":" in line:
+            k, v = line.split(":", 1)
+            kv[k.strip()] = v.strip()
+    if kv.get("kernel_source_sha") != sha:
+        return None
+    try:
+        return float(kv["hbm_bytes_per_launch"])
+    except (KeyError, ValueError):
+        return None
+
+
+def cpu_baseline(seg_host, row_index_host):
+    """The oracle on a bounded sample of every stage of the step, timed on this
+    host; each stage's time is scaled by (full work / sample work) to a
+    CPU-equivalent step time."""
+    import numpy as np
+
+    import synth
+    from oracle import gemm as G
+    from oracle import quant as Q
+    from oracle.route import route as oroute
+
+    try:
+        from threadpoolctl import threadpool_info
+        blas_threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+    except Exception:
+        blas_threads = os.cpu_count() or 1
+    rng = np.random.default_rng(0)
+    R = 2048                                     # rows per quantization sample
+    G_R, G_N = 512, 512                          # GEMM sample: rows x output columns
+    xs = synth.bf16_to_f32(synth.normal_bf16((R, H), 1.0, rng))
+    ws = synth.bf16_to_f32(synth.normal_bf16((1, R, H), 0.02, rng))
+    gs = synth.bf16_to_f32(synth.normal_bf16((R, F), 1e-3, rng))
+    times = {}
+
+    def timed(name, fn, scale):
+        t0 = time.perf_counter()
+        out = fn()
+        times[name] = (time.perf_counter() - t0) * scale
+        return out
+
+    ids = synth.moe_routing(2)
+    timed("route", lambda: oroute(ids, E), 1.0)
+    xq = timed("quant_x", lambda: Q.quantize_nvfp4(xs[None], Q.OUTER_ROW), T / R)
+    wq = timed("quant_w", lambda: Q.quantize_nvfp4(ws, Q.OUTER_TENSOR), E * F / R)
+    seg_g = np.array([0, G_R], dtype=np.int64)
+    wsub = (wq[0][:, :G_N], wq[1][:, :G_N], wq[2])
+    timed("fprop", lambda: G.grouped_gemm_nvfp4_ref(xq[0][0][:G_R], xq[1][0][:G_R], xq[2][0][:G_R], None, *wsub,
+                                                     seg_g), (M * F) / (G_R * G_N))
+    timed("requant_w", lambda: Q.requant_transpose_sr(wq[0], wq[1], wq[2], Q.OUTER_TENSOR, Q.MXFP8, 42, 0), E * F / R)
+    gq = timed("quant_g_rows", lambda: Q.quantize_mxfp8(gs, Q.SR, 42, 1), M / R)
+    seg_r = np.array([0, R], dtype=np.int64)
+    gt = timed("quant_g_t", lambda: Q.quantize_mxfp8_transposed(gs, seg_r, Q.SR, 42, 2), M / R)
+    xt = timed("requant_x", lambda: Q.requant_transpose_sr_segmented(xq[0][0], xq[1][0], xq[2][0], Q.OUTER_ROW,
+                                                                       np.arange(R), seg_r, 42, 3), M / R)
+    # DGRAD sample: G_R rows of g times G_N rows of w^T (K = F)
+    wt_c, wt_s = Q.quantize_mxfp8(synth.bf16_to_f32(synth.normal_bf16((G_N, F), 0.02, rng)), Q.RN)
+    timed("dgrad", lambda: G.mxfp8_dgrad_ref(gq[0][:G_R], gq[1][:G_R], wt_c[None], wt_s[None], seg_g),
+          (M * H) / (G_R * G_N))
+    # WGRAD sample: dw over R tokens of one expert, all of [F, H]
+    timed("wgrad", lambda: G.mxfp8_wgrad_ref(gt[0], gt[1], xt[0], xt[1], seg_r, F, H), M / R)
+    step_s = sum(times.values())
+    flops = 3 * 2.0 * M * F * H
+    return {"value": round(flops / step_s / 1e12, 6), "unit": "TFLOP/s", "cores": int(blas_threads), "kind": "oracle",
+            "sample": ("each stage on a slice of the step (2048 rows/tokens for quantize, requant and WGRAD; "
+                       "512 x 512 outputs for FPROP and DGRAD), NumPy oracle, time scaled by full/sample work; "
+                       "GEMM references are float64 BLAS"),
+            "step_seconds_equiv": round(step_s, 3),
+            "stage_seconds_equiv": {k: round(v, 3) for k, v in times.items()}}
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU: --gpus {args.gpus} is not supported (this path runs on a single "
+              "MI355X; multi-GPU expert parallelism is design-only).", file=sys.stderr)
+        sys.exit(2)
+    import numpy as np
+    import torch
+
+    import block_scaled_bit_quantize_amd as bsq
+    from block_scaled_bit_quantize_amd import _lib
+    if not os.path.exists(_lib.library_path()):
+        from block_scaled_bit_quantize_amd.build import build
+        build()
+    dev = torch.device("cuda:0")
+    inp = make_inputs(torch, dev)
+    outer_one = torch.ones(1, dtype=torch.float32, device=dev)
+
+    # routing is deterministic: read the segment sizes once (outside timing) for byte accounting
+    ri, seg, _ = bsq.route(inp["ids"], E)
+    torch.cuda.synchronize()
+    seg_host = seg.cpu().numpy()
+    n_gt = F * sum((int(seg_host[e + 1] - seg_host[e]) + 31) // 32 * 32 for e in range(E))
+    n_xt = H * (n_gt // F)
+    stages = [s for s in args.stages.split(",") if s] or None
+    run = lambda name: stages is None or name in stages
+    state = {}
+
+    def step(ev):
+        def mark(name):
+            if ev is not None:
+                e = torch.cuda.Event(enable_timing=True)
+                e.record()
+                ev.append((name, e))
+        mark("start")
+        if run("route"):
+            state["ri"], state["seg"], _ = bsq.route(inp["ids"], E)
+            mark("route")
+        ri_, seg_ = state.get("ri", ri), state.get("seg", seg)
+        if run("quant_x") or "xq" not in state:
+            state["xq"] = bsq.quantize_nvfp4(inp["x"], "row")
+            mark("quant_x")
+        if run("quant_w") or "wq" not in state:
+            state["wq"] = bsq.quantize_nvfp4(inp["w"], "tensor")
+            mark("quant_w")
+        xc, xs_, xo = state["xq"]
+        wc, ws_, wo = state["wq"]
+        if run("fprop"):
+            state["y"] = bsq.grouped_gemm_nvfp4(xc, xs_, xo, wc, ws_, wo, seg_, M, row_index=ri_)
+            mark("fprop")
+        if run("requant_w") or "wt" not in state:
+            state["wt"] = bsq.requant_transpose_sr(wc, ws_, wo, "tensor", "mxfp8", seed=42, stream_id=0)
+            mark("requant_w")
+        if run("quant_g_rows") or "gq" not in state:
+            state["gq"] = bsq.quantize_mxfp8(inp["g"], "sr", seed=42, stream_id=1)
+            mark("quant_g_rows")
+        if run("quant_g_t") or "gt" not in state:
+            state["gt"] = bsq.quantize_mxfp8(inp["g"], "sr", seed=42, stream_id=2, transpose=True, seg_offsets=seg_,
+                                             out_elems=n_gt)
+            mark("quant_g_t")
+        if run("requant_x") or "xt" not in state:
+            state["xt"] = bsq.requant_transpose_sr(xc, xs_, xo, "row", "mxfp8", seed=42, stream_id=3, row_gather=ri_,
+                                                   seg_offsets=seg_, out_elems=n_xt)
+            mark("requant_x")
+        wtc, wts = state["wt"]
+        if run("dgrad"):
+            state["dx"] = bsq.grouped_gemm_mxfp8(False, state["gq"][0], state["gq"][1], wtc, wts, seg_, M, H, F,
+                                                 native=args.native_fp8)
+            mark("dgrad")
+        if run("wgrad"):
+            state["dw"] = bsq.grouped_gemm_mxfp8(True, state["gt"][0], state["gt"][1], state["xt"][0], state["xt"][1],
+                                                 seg_, F, H, native=args.native_fp8)
+            mark("wgrad")
+
+    for _ in range(args.warmup):
+        step(None)
+    torch.cuda.synchronize()
+    events = []
+    t0 = time.perf_counter()
+    for _ in range(args.steps):
+        ev = []
+        step(ev)
+        events.append(ev)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    ms_per_step = wall * 1e3 / args.steps
+
+    per_stage = {}
+    for ev in events:
+        for (pname, pe), (name, e) in zip(ev[:-1], ev[1:]):
+            per_stage.setdefault(name, []).append(pe.elapsed_time(e))
+    algo = algorithmic(seg_host)
+    kernels = {}
+    for name, ts in per_stage.items():
+        ms = float(np.mean(ts))
+        unit, work = algo[name]
+        if unit == "GB/s":
+            ach = work / (ms * 1e-3) / 1e9
+            peak = HBM_PEAK_GBS
+        else:
+            ach = work / (ms * 1e-3) / 1e12
+            peak = MFMA_PEAK_TFLOPS["f16" if name == "fprop" else ("fp8" if args.native_fp8 else "bf16")]
+        kernels[name] = {"ms": round(ms, 4), "achieved": round(ach, 2), "unit": unit, "peak": peak,
+                         "frac": round(ach / peak, 4)}
+
+    gemm_flops = sum(algo[n][1] for n in ("fprop", "dgrad", "wgrad") if n in kernels)
+    value = gemm_flops / (ms_per_step * 1e-3) / 1e12
+    dom = max(kernels, key=lambda n: kernels[n]["ms"])
+    dk = kernels[dom]
+    src = {"fprop": ("gemm.hip",), "dgrad": ("gemm.hip",), "wgrad": ("gemm.hip",)}.get(
+        dom, ("quantize.hip", "transpose_quant.hip"))
+    if args.native_fp8 and dom in ("dgrad", "wgrad"):
+        src = ("gemm_mxfp8_native.hip",)
+    traffic = read_traffic(dom, kernel_sha(*src))
+    roofline = {"bound": "hbm" if dk["unit"] == "GB/s" else "mfma", "kernel": dom, "achieved": dk["achieved"],
+                "peak": dk["peak"], "unit": dk["unit"], "frac": dk["frac"], "traffic": traffic}
+
+    cpu = None
+    if not args.no_cpu_baseline and stages is None:
+        cpu = cpu_baseline(seg_host, None)
+
+    line = {
+        "metric": METRIC, "value": round(value, 3), "unit": "TFLOP/s", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": round(ms_per_step, 4), "higher_is_better": True, "scaling": "weak",
+        "vs_baseline": None, "dtype": "f16/bf16 MFMA (fp8 MFMA with --native-fp8), f32 accumulate",
+        "data": "synthetic (seeded; bf16 N(0,1) activations, N(0,0.02) weights, N(0,1e-3) gradients with 0.1% x50)",
+        "config": {"workload": "moe_expert_fwd_bwd", "tokens": T, "hidden": H, "experts": E, "topk": K_TOP,
+                   "ffn": F, "global_batch": T, "parallelism": "none (1 GPU)",
+                   "backward_gemm": "native-fp8" if args.native_fp8 else "exact-bf16"},
+        "kernels": kernels,
+        "roofline": roofline,
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(line))
+
+
+if __name__ == "__main__":
+    main()
