@@ -108,7 +108,7 @@ __device__ __forceinline__ float sr_e4m3(float y, uint32_t r16) {
   const uint32_t b = __float_as_uint(y);
   const uint32_t s = b & 0x80000000u;
   uint32_t a = b & 0x7FFFFFFFu;
-  if (a >= 0x3C800000u) {
+  if (a - 1u >= 0x3C7FFFFFu) {  // |y| >= 2^-6, or exactly 0 (t = 0 keeps it 0)
     const uint32_t t = a & 0xFFFFFu;
     a = (a & 0xFFF00000u) + (((r16 << 4) + 8u < t) ? 0x100000u : 0u);
   } else {

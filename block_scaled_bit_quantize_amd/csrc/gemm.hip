@@ -48,7 +48,6 @@ namespace {
 constexpr int BM = 256;
 constexpr int BN = 256;
 constexpr int BK = 64;
-constexpr int kThreads = 256;
 constexpr int kRow = BK * 2 + 16;  // LDS bytes per decoded row (16-bit values + pad)
 constexpr int kMaxE = 1024;
 constexpr int kXcds = 8;
@@ -94,51 +93,53 @@ __device__ __forceinline__ void load_row(RowData<FMT_MXFP8>& r, const uint8_t* c
   }
 }
 
-// Decode 64 elements into 128 bytes of LDS.
-__device__ __forceinline__ void decode_row(const RowData<FMT_NVFP4>& r, uint8_t* dst) {
-  const uint32_t w[8] = {r.c[0].x, r.c[0].y, r.c[0].z, r.c[0].w, r.c[1].x, r.c[1].y, r.c[1].z, r.c[1].w};
-#pragma unroll
-  for (int q = 0; q < 8; ++q) {
-    const _Float16 s = (_Float16)e4m3_val((r.sc >> (8 * (q >> 1))) & 0xFFu);
-    const h2 sv = {s, s};
-    const h2 v0 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w[q], 1.0f, 0) * sv;
-    const h2 v1 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w[q], 1.0f, 1) * sv;
-    const h2 v2 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w[q], 1.0f, 2) * sv;
-    const h2 v3 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w[q], 1.0f, 3) * sv;
-    *reinterpret_cast<uint4*>(dst + 16 * q) =
-        make_uint4(__builtin_bit_cast(uint32_t, v0), __builtin_bit_cast(uint32_t, v1), __builtin_bit_cast(uint32_t, v2),
-                   __builtin_bit_cast(uint32_t, v3));
-  }
+// Decode elements [16c, 16c+16) of a row's K step into 32 bytes at dst + 32c.
+__device__ __forceinline__ void decode_chunk(const RowData<FMT_NVFP4>& r, uint8_t* dst, int c) {
+  const uint32_t w0 = c < 2 ? (c == 0 ? r.c[0].x : r.c[0].z) : (c == 2 ? r.c[1].x : r.c[1].z);
+  const uint32_t w1 = c < 2 ? (c == 0 ? r.c[0].y : r.c[0].w) : (c == 2 ? r.c[1].y : r.c[1].w);
+  const _Float16 s = (_Float16)e4m3_val((r.sc >> (8 * c)) & 0xFFu);  // one E4M3 scale per 16
+  const h2 sv = {s, s};
+#define BSQ_DEC4(w, v0, v1, v2, v3)                                 \
+  const h2 v0 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, 1.0f, 0) * sv; \
+  const h2 v1 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, 1.0f, 1) * sv; \
+  const h2 v2 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, 1.0f, 2) * sv; \
+  const h2 v3 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, 1.0f, 3) * sv;
+  BSQ_DEC4(w0, a0, a1, a2, a3)
+  BSQ_DEC4(w1, b0, b1, b2, b3)
+#undef BSQ_DEC4
+  uint4* d = reinterpret_cast<uint4*>(dst + 32 * c);
+  d[0] = make_uint4(__builtin_bit_cast(uint32_t, a0), __builtin_bit_cast(uint32_t, a1), __builtin_bit_cast(uint32_t, a2),
+                    __builtin_bit_cast(uint32_t, a3));
+  d[1] = make_uint4(__builtin_bit_cast(uint32_t, b0), __builtin_bit_cast(uint32_t, b1), __builtin_bit_cast(uint32_t, b2),
+                    __builtin_bit_cast(uint32_t, b3));
 }
-__device__ __forceinline__ void decode_row(const RowData<FMT_MXFP8>& r, uint8_t* dst) {
-  const uint32_t w[16] = {r.c[0].x, r.c[0].y, r.c[0].z, r.c[0].w, r.c[1].x, r.c[1].y, r.c[1].z, r.c[1].w,
-                          r.c[2].x, r.c[2].y, r.c[2].z, r.c[2].w, r.c[3].x, r.c[3].y, r.c[3].z, r.c[3].w};
-  const float s0 = __uint_as_float((r.sc & 0xFFu) << 23);  // 2^(s-127): the convert applies its exponent
-  const float s1 = __uint_as_float(((r.sc >> 8) & 0xFFu) << 23);
-#pragma unroll
-  for (int q = 0; q < 16; q += 2) {
-    const float s = q < 8 ? s0 : s1;
-    const bf2 v0 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w[q], s, false);
-    const bf2 v1 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w[q], s, true);
-    const bf2 v2 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w[q + 1], s, false);
-    const bf2 v3 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w[q + 1], s, true);
-    *reinterpret_cast<uint4*>(dst + 8 * q) =
-        make_uint4(__builtin_bit_cast(uint32_t, v0), __builtin_bit_cast(uint32_t, v1), __builtin_bit_cast(uint32_t, v2),
-                   __builtin_bit_cast(uint32_t, v3));
-  }
+__device__ __forceinline__ void decode_chunk(const RowData<FMT_MXFP8>& r, uint8_t* dst, int c) {
+  const uint4 v = r.c[c];
+  // 2^(s-127) as a float: the scaled convert applies its exponent (one E8M0 scale per 32)
+  const float s = __uint_as_float(((r.sc >> (8 * (c >> 1))) & 0xFFu) << 23);
+#define BSQ_DEC2(w, p, q)                                              \
+  const bf2 p = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w, s, false); \
+  const bf2 q = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w, s, true);
+  BSQ_DEC2(v.x, a0, a1)
+  BSQ_DEC2(v.y, a2, a3)
+  BSQ_DEC2(v.z, b0, b1)
+  BSQ_DEC2(v.w, b2, b3)
+#undef BSQ_DEC2
+  uint4* d = reinterpret_cast<uint4*>(dst + 32 * c);
+  d[0] = make_uint4(__builtin_bit_cast(uint32_t, a0), __builtin_bit_cast(uint32_t, a1), __builtin_bit_cast(uint32_t, a2),
+                    __builtin_bit_cast(uint32_t, a3));
+  d[1] = make_uint4(__builtin_bit_cast(uint32_t, b0), __builtin_bit_cast(uint32_t, b1), __builtin_bit_cast(uint32_t, b2),
+                    __builtin_bit_cast(uint32_t, b3));
 }
 
-template <int FMT>
-__device__ __forceinline__ f32x16 mfma16(const uint8_t* pa, const uint8_t* pb, f32x16 acc);
-template <>
-__device__ __forceinline__ f32x16 mfma16<FMT_NVFP4>(const uint8_t* pb, const uint8_t* pa, f32x16 acc) {
-  return __builtin_amdgcn_mfma_f32_32x32x16_f16(*reinterpret_cast<const half8*>(pb),
-                                                *reinterpret_cast<const half8*>(pa), acc, 0, 0, 0);
+template <int FMT> struct Frag { typedef half8 type; };
+template <> struct Frag<FMT_MXFP8> { typedef bf16x8 type; };
+
+__device__ __forceinline__ f32x16 mfma16(half8 b, half8 a, f32x16 acc) {
+  return __builtin_amdgcn_mfma_f32_32x32x16_f16(b, a, acc, 0, 0, 0);
 }
-template <>
-__device__ __forceinline__ f32x16 mfma16<FMT_MXFP8>(const uint8_t* pb, const uint8_t* pa, f32x16 acc) {
-  return __builtin_amdgcn_mfma_f32_32x32x16_bf16(*reinterpret_cast<const bf16x8*>(pb),
-                                                 *reinterpret_cast<const bf16x8*>(pa), acc, 0, 0, 0);
+__device__ __forceinline__ f32x16 mfma16(bf16x8 b, bf16x8 a, f32x16 acc) {
+  return __builtin_amdgcn_mfma_f32_32x32x16_bf16(b, a, acc, 0, 0, 0);
 }
 
 struct GemmArgs {
@@ -159,43 +160,50 @@ struct GemmArgs {
   void* out;
 };
 
-template <int FMT, int WGRAD, int OUT_F32>
-__global__ __launch_bounds__(kThreads, 1) void k_gemm(const GemmArgs g) {
+// WN waves along N (2: 4 waves of 128 x 128, one wave per SIMD; 4: 8 waves of
+// 128 x 64, two waves per SIMD so one wave's LDS/VMEM/barrier waits are
+// covered by the other's MFMAs).
+template <int FMT, int WGRAD, int OUT_F32, int WN>
+__global__ __launch_bounds__(128 * WN) void k_gemm(const GemmArgs g) {
+  constexpr int NT = 128 * WN;            // threads
+  constexpr int TJ = 8 / WN;              // 32-wide n tiles per wave
+  constexpr int RPT = (BM + BN) / NT;     // operand rows loaded and decoded per thread
   __shared__ __attribute__((aligned(16))) uint8_t sA[2][BM * kRow];
   __shared__ __attribute__((aligned(16))) uint8_t sB[2][BN * kRow];
   __shared__ int64_t s_cum[kMaxE];  // inclusive m-tiles (along M) or padded tokens (WGRAD) per expert
-  __shared__ int64_t s_part[kThreads];
+  __shared__ int64_t s_part[256];
 
   const int t = threadIdx.x;
   const int E = g.E;
-  {
-    int64_t loc[4];
-    int64_t sum = 0;
-#pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const int e = 4 * t + j;
-      int64_t n = 0;
-      if (e < E) {
-        const int64_t len = g.seg_offsets[e + 1] - g.seg_offsets[e];
-        n = len <= 0 ? 0 : (WGRAD ? (len + 31) / 32 * 32 : (len + BM - 1) / BM);
-      }
-      sum += n;
-      loc[j] = sum;
-    }
-    s_part[t] = sum;
-    __syncthreads();
-    for (int o = 1; o < kThreads; o <<= 1) {
-      const int64_t v = t >= o ? s_part[t - o] : 0;
-      __syncthreads();
-      s_part[t] += v;
-      __syncthreads();
-    }
-    const int64_t before = s_part[t] - sum;
+  // per-expert unit count: m-tiles (segments along M) or padded tokens (WGRAD)
+  auto units = [&](int e) -> int64_t {
+    const int64_t len = g.seg_offsets[e + 1] - g.seg_offsets[e];
+    return len <= 0 ? 0 : (WGRAD ? (len + 31) / 32 * 32 : (len + BM - 1) / BM);
+  };
+  int64_t own = 0;  // units of experts 4t .. 4t+3
+  if (t < 256) {
 #pragma unroll
     for (int j = 0; j < 4; ++j)
-      if (4 * t + j < E) s_cum[4 * t + j] = before + loc[j];
+      if (4 * t + j < E) own += units(4 * t + j);
+    s_part[t] = own;
+  }
+  __syncthreads();
+  for (int o = 1; o < 256; o <<= 1) {  // inclusive scan over the 256 partial sums
+    const int64_t v = (t < 256 && t >= o) ? s_part[t - o] : 0;
+    __syncthreads();
+    if (t < 256) s_part[t] += v;
     __syncthreads();
   }
+  if (t < 256) {
+    int64_t run = s_part[t] - own;
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+      if (4 * t + j < E) {
+        run += units(4 * t + j);
+        s_cum[4 * t + j] = run;
+      }
+  }
+  __syncthreads();
   const int64_t ntn = g.N / BN;
   const int64_t ntm_w = g.M / BM;
   const int64_t total = WGRAD ? (int64_t)E * ntm_w * ntn : s_cum[E - 1] * ntn;
@@ -206,18 +214,12 @@ __global__ __launch_bounds__(kThreads, 1) void k_gemm(const GemmArgs g) {
 
   int e;
   int64_t m0, n0, Me = 0, seg0 = 0, klen;
-  const uint8_t *a_c, *a_s, *b_c, *b_s;
   if constexpr (WGRAD) {
     e = (int)(tile / (ntm_w * ntn));
     const int64_t r = tile % (ntm_w * ntn);
     m0 = (r / ntn) * BM;
     n0 = (r % ntn) * BN;
-    const int64_t kbase = e ? s_cum[e - 1] : 0;  // sum of earlier padded token counts
-    klen = s_cum[e] - kbase;
-    a_c = g.a_codes + g.M * kbase + (m0 + t) * klen;
-    a_s = g.a_scales + (g.M * kbase + (m0 + t) * klen) / 32;
-    b_c = g.b_codes + g.N * kbase + (n0 + t) * klen;
-    b_s = g.b_scales + (g.N * kbase + (n0 + t) * klen) / 32;
+    klen = s_cum[e] - (e ? s_cum[e - 1] : 0);  // Kp_e
   } else {
     const int64_t mtg = tile / ntn;
     n0 = (tile % ntn) * BN;
@@ -232,70 +234,115 @@ __global__ __launch_bounds__(kThreads, 1) void k_gemm(const GemmArgs g) {
     if (seg0 < 0 || seg0 + Me > g.M) return;  // malformed offsets: stay inside the buffers
     m0 = (mtg - (s_cum[e] - (Me + BM - 1) / BM)) * BM;
     klen = g.K;
-    const int64_t m = m0 + t < Me ? m0 + t : Me - 1;
-    int64_t arow = g.a_row_index ? (int64_t)g.a_row_index[seg0 + m] : seg0 + m;
-    arow = arow < 0 ? 0 : (arow >= g.a_rows ? g.a_rows - 1 : arow);
-    const int64_t brow = (int64_t)e * g.N + n0 + t;
-    constexpr int CB = FMT == FMT_NVFP4 ? 2 : 1;   // elements per code byte
-    constexpr int SB = FMT == FMT_NVFP4 ? 16 : 32;  // elements per scale
-    a_c = g.a_codes + arow * (g.K / CB);
-    a_s = g.a_scales + arow * (g.K / SB);
-    b_c = g.b_codes + brow * (g.K / CB);
-    b_s = g.b_scales + brow * (g.K / SB);
+  }
+
+  // ---- the operand rows this thread loads and decodes: tile row id = t + r*NT
+  // (ids below BM are A rows, the rest B rows)
+  const uint8_t* rcode[RPT];
+  const uint8_t* rscal[RPT];
+  int ldst[RPT];  // byte offset of the row in sA / sB
+  bool isA[RPT];
+#pragma unroll
+  for (int r = 0; r < RPT; ++r) {
+    const int id = t + r * NT;
+    isA[r] = id < BM;
+    const int lrow = isA[r] ? id : id - BM;
+    ldst[r] = lrow * kRow;
+    if constexpr (WGRAD) {
+      const int64_t kbase = e ? s_cum[e - 1] : 0;  // sum of earlier padded token counts
+      const int64_t off = isA[r] ? g.M * kbase + (m0 + lrow) * klen : g.N * kbase + (n0 + lrow) * klen;
+      rcode[r] = (isA[r] ? g.a_codes : g.b_codes) + off;
+      rscal[r] = (isA[r] ? g.a_scales : g.b_scales) + off / 32;
+    } else {
+      constexpr int CB = FMT == FMT_NVFP4 ? 2 : 1;   // elements per code byte
+      constexpr int SB = FMT == FMT_NVFP4 ? 16 : 32;  // elements per scale
+      int64_t row;
+      if (isA[r]) {
+        const int64_t m = m0 + lrow < Me ? m0 + lrow : Me - 1;
+        row = g.a_row_index ? (int64_t)g.a_row_index[seg0 + m] : seg0 + m;
+        row = row < 0 ? 0 : (row >= g.a_rows ? g.a_rows - 1 : row);
+      } else {
+        row = (int64_t)e * g.N + n0 + lrow;
+      }
+      rcode[r] = (isA[r] ? g.a_codes : g.b_codes) + row * (g.K / CB);
+      rscal[r] = (isA[r] ? g.a_scales : g.b_scales) + row * (g.K / SB);
+    }
   }
 
   const int wave = t >> 6;
   const int lane = t & 63;
-  const int wm = wave >> 1;  // 128-row half of the tile (m)
-  const int wn = wave & 1;   // 128-col half of the tile (n)
+  const int wm = wave / WN;  // 128-row half of the tile (m)
+  const int wn = wave % WN;  // (256/WN)-column slice of the tile (n)
 
-  f32x16 acc[4][4];
+  f32x16 acc[4][TJ];
 #pragma unroll
   for (int i = 0; i < 4; ++i)
 #pragma unroll
-    for (int j = 0; j < 4; ++j)
+    for (int j = 0; j < TJ; ++j)
 #pragma unroll
-      for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.0f;
+      for (int q = 0; q < 16; ++q) acc[i][j][q] = 0.0f;
 
   const int nk = (int)((klen + BK - 1) / BK);
-  RowData<FMT> ra, rb;
-  if (nk > 0) {
-    load_row(ra, a_c, a_s, 0, klen);
-    load_row(rb, b_c, b_s, 0, klen);
-    decode_row(ra, &sA[0][t * kRow]);
-    decode_row(rb, &sB[0][t * kRow]);
-    if (nk > 1) {
-      load_row(ra, a_c, a_s, BK, klen);
-      load_row(rb, b_c, b_s, BK, klen);
-    }
-  }
-  __syncthreads();
-
+  typedef typename Frag<FMT>::type V8;
   // fragment: lane -> row (lane & 31), k offset 8 * (lane >> 5) within each 16-wide k slice
   const int frag_off = (lane & 31) * kRow + (lane >> 5) * 16;
+  const int a_off = wm * 128 * kRow + frag_off;
+  const int b_off = wn * (256 / WN) * kRow + frag_off;
+  V8 fa[2][4], fb[2][TJ];
+#define BSQ_LOAD_FRAGS(slot, buf, ks)                                                              \
+  _Pragma("unroll") for (int i_ = 0; i_ < 4; ++i_) fa[slot][i_] =                                  \
+      *reinterpret_cast<const V8*>(&sA[buf][a_off + i_ * 32 * kRow + (ks) * 32]);                  \
+  _Pragma("unroll") for (int j_ = 0; j_ < TJ; ++j_) fb[slot][j_] =                                 \
+      *reinterpret_cast<const V8*>(&sB[buf][b_off + j_ * 32 * kRow + (ks) * 32]);
+#define BSQ_DST(buf, r) (isA[r] ? &sA[buf][ldst[r]] : &sB[buf][ldst[r]])
+  RowData<FMT> rd[RPT];
+  if (nk > 0) {
+#pragma unroll
+    for (int r = 0; r < RPT; ++r) {
+      load_row(rd[r], rcode[r], rscal[r], 0, klen);
+#pragma unroll
+      for (int c = 0; c < 4; ++c) decode_chunk(rd[r], BSQ_DST(0, r), c);
+      load_row(rd[r], rcode[r], rscal[r], nk > 1 ? BK : 0, klen);
+    }
+    __syncthreads();
+    BSQ_LOAD_FRAGS(0, 0, 0)
+  }
+
+  // Software pipeline per K step (one scheduling region, no branches): for each
+  // 16-wide k slice, read the next slice's fragments, run this slice's MFMAs
+  // and decode one quarter of the next K step into the other LDS buffer; then
+  // fetch the K step after next (clamped: the last iteration decodes and loads
+  // a duplicate that is never read) and swap buffers at the barrier.
   for (int kt = 0; kt < nk; ++kt) {
     const int buf = kt & 1;
-    const uint8_t* pa = &sA[buf][(wm * 128) * kRow + frag_off];
-    const uint8_t* pb = &sB[buf][(wn * 128) * kRow + frag_off];
 #pragma unroll
-    for (int ks = 0; ks < BK / 16; ++ks) {
-      // D = B A^T: output rows are n, columns m (a lane keeps 4 consecutive n)
+    for (int ks = 0; ks < 4; ++ks) {
+      if (ks < 3) {
+        BSQ_LOAD_FRAGS((ks + 1) & 1, buf, ks + 1)
+      }
 #pragma unroll
       for (int i = 0; i < 4; ++i)
 #pragma unroll
-        for (int j = 0; j < 4; ++j)
-          acc[i][j] = mfma16<FMT>(pb + j * 32 * kRow + ks * 32, pa + i * 32 * kRow + ks * 32, acc[i][j]);
-    }
-    if (kt + 1 < nk) {
-      decode_row(ra, &sA[buf ^ 1][t * kRow]);
-      decode_row(rb, &sB[buf ^ 1][t * kRow]);
-      if (kt + 2 < nk) {
-        load_row(ra, a_c, a_s, (int64_t)(kt + 2) * BK, klen);
-        load_row(rb, b_c, b_s, (int64_t)(kt + 2) * BK, klen);
+        for (int j = 0; j < TJ; ++j) acc[i][j] = mfma16(fb[ks & 1][j], fa[ks & 1][i], acc[i][j]);
+#pragma unroll
+      for (int r = 0; r < RPT; ++r) decode_chunk(rd[r], BSQ_DST(buf ^ 1, r), ks);
+      // interleave each MFMA with a few decode VALU ops, the fragment reads and the decode stores
+#pragma unroll
+      for (int m = 0; m < 4 * TJ; ++m) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);                         // MFMA
+        __builtin_amdgcn_sched_group_barrier(0x002, 12 * RPT / TJ, 0);             // VALU
+        if (m < 4 + TJ) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);         // DS read
+        if (m >= 4 * TJ - 2 * RPT) __builtin_amdgcn_sched_group_barrier(0x200, 1, 0);  // DS write
       }
     }
+    const int64_t knext = (int64_t)(kt + 2 < nk ? kt + 2 : nk - 1) * BK;
+#pragma unroll
+    for (int r = 0; r < RPT; ++r) load_row(rd[r], rcode[r], rscal[r], knext, klen);
     __syncthreads();
+    BSQ_LOAD_FRAGS(0, buf ^ 1, 0)
   }
+#undef BSQ_LOAD_FRAGS
+#undef BSQ_DST
 
   // ---- epilogue
   const float sw = FMT == FMT_NVFP4 ? g.b_outer[e] : 1.0f;
@@ -313,9 +360,9 @@ __global__ __launch_bounds__(kThreads, 1) void k_gemm(const GemmArgs g) {
       }
       s = sx * sw;
     }
-    const int64_t obase = (WGRAD ? ((int64_t)e * g.M + m) : (seg0 + m)) * g.N + n0 + wn * 128;
+    const int64_t obase = (WGRAD ? ((int64_t)e * g.M + m) : (seg0 + m)) * g.N + n0 + wn * (256 / WN);
 #pragma unroll
-    for (int j = 0; j < 4; ++j)
+    for (int j = 0; j < TJ; ++j)
 #pragma unroll
       for (int q = 0; q < 4; ++q) {
         const int n = j * 32 + q * 8 + (lane >> 5) * 4;
@@ -335,13 +382,18 @@ __global__ __launch_bounds__(kThreads, 1) void k_gemm(const GemmArgs g) {
   }
 }
 
+#ifndef BSQ_GEMM_WN
+#define BSQ_GEMM_WN 4
+#endif
+
 template <int FMT, int WGRAD>
 int launch(const GemmArgs& a, int64_t slots, int out_dtype, hipStream_t s) {
+  constexpr int WN = BSQ_GEMM_WN;
   const int64_t grid = (slots + kXcds - 1) / kXcds * kXcds;
   if (out_dtype == BSQ_F32)
-    hipLaunchKernelGGL((k_gemm<FMT, WGRAD, 1>), dim3((unsigned)grid), dim3(kThreads), 0, s, a);
+    hipLaunchKernelGGL((k_gemm<FMT, WGRAD, 1, WN>), dim3((unsigned)grid), dim3(128 * WN), 0, s, a);
   else
-    hipLaunchKernelGGL((k_gemm<FMT, WGRAD, 0>), dim3((unsigned)grid), dim3(kThreads), 0, s, a);
+    hipLaunchKernelGGL((k_gemm<FMT, WGRAD, 0, WN>), dim3((unsigned)grid), dim3(128 * WN), 0, s, a);
   return bsqh::launch_status();
 }
 

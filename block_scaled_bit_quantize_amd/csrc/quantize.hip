@@ -22,7 +22,13 @@ using namespace bsqd;
 namespace {
 
 constexpr int kThreads = 256;
-constexpr int64_t kTensorChunkBytes = 64ll << 20;
+#ifndef BSQ_TENSOR_CHUNK_MB
+#define BSQ_TENSOR_CHUNK_MB 64
+#endif
+// per-tensor outer scales need the group maximum before any block can round:
+// the max pass and the quantize pass alternate over chunks of this size so
+// that the second read can come from the 256 MB Infinity Cache
+constexpr int64_t kTensorChunkBytes = (int64_t)BSQ_TENSOR_CHUNK_MB << 20;
 
 // 16 consecutive elements of type T (bf16 bit patterns or float).
 template <typename T> struct Blk16;
@@ -92,20 +98,27 @@ __global__ void k_copy_f32(const float* __restrict__ s, float* __restrict__ d, i
 
 // Largest magnitude of each batch item [item0, item0 + gridDim.y), merged
 // into amax_bits[item] with an atomic max on the bit pattern (non-negative
-// floats order like their bits).
+// floats order like their bits). Workgroup x of item y reduces the 16-byte
+// vectors [x*per_wg, (x+1)*per_wg) of the item with 8 loads in flight per
+// thread and issues one atomic.
 template <typename T>
 __global__ __launch_bounds__(kThreads) void k_amax_items(const T* __restrict__ x, int64_t vec_per_item,
-                                                         uint32_t* __restrict__ amax_bits, int64_t item0) {
+                                                         int64_t per_wg, uint32_t* __restrict__ amax_bits,
+                                                         int64_t item0) {
   const int64_t item = item0 + blockIdx.y;
   const uint4* p = reinterpret_cast<const uint4*>(x) + item * vec_per_item;
+  const int64_t lo = (int64_t)blockIdx.x * per_wg;
+  const int64_t hi = lo + per_wg < vec_per_item ? lo + per_wg : vec_per_item;
   float m = 0.0f;
-  const int64_t stride = (int64_t)gridDim.x * kThreads;
-  int64_t i = (int64_t)blockIdx.x * kThreads + threadIdx.x;
-  for (; i + 3 * stride < vec_per_item; i += 4 * stride) {
-    const uint4 a = p[i], b = p[i + stride], c = p[i + 2 * stride], d = p[i + 3 * stride];
-    m = fmaxf(m, fmaxf(fmaxf(absmax16B<T>(a), absmax16B<T>(b)), fmaxf(absmax16B<T>(c), absmax16B<T>(d))));
+  int64_t i = lo + threadIdx.x;
+  for (; i + 7 * kThreads < hi; i += 8 * kThreads) {
+    uint4 v[8];
+#pragma unroll
+    for (int u = 0; u < 8; ++u) v[u] = p[i + u * kThreads];
+#pragma unroll
+    for (int u = 0; u < 8; ++u) m = fmaxf(m, absmax16B<T>(v[u]));
   }
-  for (; i < vec_per_item; i += stride) m = fmaxf(m, absmax16B<T>(p[i]));
+  for (; i < hi; i += kThreads) m = fmaxf(m, absmax16B<T>(p[i]));
   m = wave_max(m);
   __shared__ float red[kThreads / 64];
   if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = m;
@@ -114,7 +127,7 @@ __global__ __launch_bounds__(kThreads) void k_amax_items(const T* __restrict__ x
     float r = red[0];
 #pragma unroll
     for (int w = 1; w < kThreads / 64; ++w) r = fmaxf(r, red[w]);
-    atomicMax(amax_bits + item, __float_as_uint(r));
+    if (r > 0.0f) atomicMax(amax_bits + item, __float_as_uint(r));
   }
 }
 
@@ -275,11 +288,12 @@ int quantize_nvfp4_t(const T* x, int64_t B, int64_t R, int64_t C, int mode, cons
   const int64_t item_bytes = R * C * (int64_t)sizeof(T);
   const int64_t chunk = item_bytes >= kTensorChunkBytes ? 1 : kTensorChunkBytes / item_bytes;
   const int64_t vec = item_bytes / 16;
+  const int64_t per_wg = 8 * kThreads * 4;  // 32 vectors (512 bytes) per thread
+  const int64_t gx = (vec + per_wg - 1) / per_wg;
   for (int64_t i0 = 0; i0 < B; i0 += chunk) {
     const int64_t ni = (B - i0) < chunk ? (B - i0) : chunk;
-    int64_t gx = (vec + 4 * kThreads - 1) / (4 * kThreads);
-    if (gx > 4096) gx = 4096;
-    hipLaunchKernelGGL(k_amax_items<T>, dim3((unsigned)gx, (unsigned)ni), dim3(kThreads), 0, s, x, vec, ws, i0);
+    hipLaunchKernelGGL(k_amax_items<T>, dim3((unsigned)gx, (unsigned)ni), dim3(kThreads), 0, s, x, vec, per_wg, ws,
+                       i0);
     const int st = launch_quant<T, BSQ_OUTER_TENSOR>(x, i0 * R, (i0 + ni) * R, R, C, nullptr, ws, codes, scales, outer_out, s);
     if (st != BSQ_OK) return st;
   }

@@ -28,7 +28,7 @@ namespace {
 
 constexpr int kThreads = 256;
 constexpr int TM = 128;  // tokens per tile (input rows)
-constexpr int TC = 64;   // channels per tile
+constexpr int TC = 64;   // column granularity of the transposed layouts
 enum { SRC_BF16 = 0, SRC_F32 = 1, SRC_NVFP4 = 2 };
 
 typedef _Float16 h2 __attribute__((ext_vector_type(2)));
@@ -115,20 +115,25 @@ __global__ __launch_bounds__(kThreads) void k_nvfp4_item_amax(const uint8_t* __r
 
 template <int SRC> struct TileT { typedef uint16_t type; };
 template <> struct TileT<SRC_F32> { typedef float type; };
+template <int SRC> constexpr int tile_channels() { return SRC == SRC_F32 ? 64 : 128; }
 
 // The transposing quantizer. SEG: tiles come from the segment plan (gather
 // and per-segment padded layout); otherwise batch item e covers input rows
-// [e*R, (e+1)*R) and is written as [cols, R].
+// [e*R, (e+1)*R) and is written as [cols, R]. A workgroup covers 128 tokens x
+// TCH channels (128 for 16-bit tiles, 64 for float tiles); in phase 2 a
+// thread owns CPT = TCH/64 adjacent channels x 32 tokens.
 template <int SRC, int OUTF, int RND, bool SEG>
 __global__ __launch_bounds__(kThreads) void k_tq(
     const void* __restrict__ src, const uint8_t* __restrict__ in_scales, const float* __restrict__ in_outer,
     int in_mode, int64_t C, int64_t R, const int32_t* __restrict__ gather, const int64_t* __restrict__ seg_start_p,
     const int64_t* __restrict__ seg_len_p, const int32_t* __restrict__ slot_seg, const int32_t* __restrict__ slot_mt,
-    const int64_t* __restrict__ seg_base,
-    const uint32_t* __restrict__ amax_bits, uint64_t seed, uint64_t stream_id, uint8_t* __restrict__ out_codes,
-    uint8_t* __restrict__ out_scales, float* __restrict__ out_outer) {
+    const int64_t* __restrict__ seg_base, const uint32_t* __restrict__ amax_bits, uint64_t seed, uint64_t stream_id,
+    uint8_t* __restrict__ out_codes, uint8_t* __restrict__ out_scales, float* __restrict__ out_outer) {
   typedef typename TileT<SRC>::type TT;
-  __shared__ TT tile[TM][TC];
+  constexpr int TCH = tile_channels<SRC>();
+  constexpr int CPT = TCH / 64;
+  constexpr int LROW = TCH * (int)sizeof(TT) + 16;  // padded LDS row (bytes): conflict-free writes
+  __shared__ __attribute__((aligned(16))) uint8_t tile[TM * LROW];
   __shared__ float rowmul[TM];
 
   int64_t e, mt, seg_start, Me, Mp, base;
@@ -150,20 +155,20 @@ __global__ __launch_bounds__(kThreads) void k_tq(
     Mp = R;
     base = e * C * R;
   }
-  const int64_t c0 = (int64_t)blockIdx.y * TC;
+  const int64_t c0 = (int64_t)blockIdx.y * TCH;
   const int64_t m0 = mt * TM;
   const int t = threadIdx.x;
 
-  // ---- phase 1: rows m0 .. m0+127 of the segment, channels c0 .. c0+63
+  // ---- phase 1: rows m0 .. m0+127 of the segment, channels c0 .. c0+TCH-1
   if constexpr (SRC == SRC_BF16) {
     const uint16_t* x = static_cast<const uint16_t*>(src);
 #pragma unroll
-    for (int p = 0; p < 4; ++p) {
-      const int m = p * 32 + (t >> 3);
-      const int cc = (t & 7) * 8;
+    for (int p = 0; p < 8; ++p) {
+      const int m = p * 16 + (t >> 4);
+      const int cc = (t & 15) * 8;
       uint4 v = make_uint4(0, 0, 0, 0);
-      if (m0 + m < Me) v = *reinterpret_cast<const uint4*>(x + (seg_start + m0 + m) * C + c0 + cc);
-      *reinterpret_cast<uint4*>(&tile[m][cc]) = v;
+      if (m0 + m < Me && c0 + cc < C) v = *reinterpret_cast<const uint4*>(x + (seg_start + m0 + m) * C + c0 + cc);
+      *reinterpret_cast<uint4*>(&tile[m * LROW + cc * 2]) = v;
     }
   } else if constexpr (SRC == SRC_F32) {
     const float* x = static_cast<const float*>(src);
@@ -172,139 +177,149 @@ __global__ __launch_bounds__(kThreads) void k_tq(
       const int m = p * 16 + (t >> 4);
       const int cc = (t & 15) * 4;
       float4 v = make_float4(0.f, 0.f, 0.f, 0.f);
-      if (m0 + m < Me) v = *reinterpret_cast<const float4*>(x + (seg_start + m0 + m) * C + c0 + cc);
-      *reinterpret_cast<float4*>(&tile[m][cc]) = v;
+      if (m0 + m < Me && c0 + cc < C) v = *reinterpret_cast<const float4*>(x + (seg_start + m0 + m) * C + c0 + cc);
+      *reinterpret_cast<float4*>(&tile[m * LROW + cc * 4]) = v;
     }
   } else {
     const uint8_t* codes = static_cast<const uint8_t*>(src);
-    const int m = t >> 1;          // 2 threads per row, 32 channels each
+    const int m = t >> 1;          // 2 threads per row, 64 channels each
     const int half = t & 1;
-    uint4 w = make_uint4(0, 0, 0, 0);
-    float s0 = 0.0f, s1 = 0.0f, mul = 0.0f;
-    if (m0 + m < Me) {
+    uint4 w0 = make_uint4(0, 0, 0, 0), w1 = make_uint4(0, 0, 0, 0);
+    uint32_t sc = 0;
+    float mul = 0.0f;
+    if (m0 + m < Me && c0 + 64 * half < C) {
       const int64_t g = seg_start + m0 + m;
       int64_t row = g;
       if (gather) {  // segment mode: R is the number of input rows the indices point into
         row = (int64_t)gather[g];
         row = row < 0 ? 0 : (row >= R ? R - 1 : row);
       }
-      w = *reinterpret_cast<const uint4*>(codes + row * (C >> 1) + (c0 >> 1) + half * 16);
-      const uint8_t* sp = in_scales + row * (C >> 4) + (c0 >> 4) + half * 2;
-      s0 = e4m3_val(sp[0]);
-      s1 = e4m3_val(sp[1]);
+      const uint4* cp = reinterpret_cast<const uint4*>(codes + row * (C >> 1) + (c0 >> 1) + half * 32);
+      w0 = cp[0];
+      w1 = cp[1];
+      const uint8_t* sp = in_scales + row * (C >> 4) + (c0 >> 4) + half * 4;
+      sc = (uint32_t)sp[0] | ((uint32_t)sp[1] << 8) | ((uint32_t)sp[2] << 16) | ((uint32_t)sp[3] << 24);
       mul = in_mode == BSQ_OUTER_ROW ? in_outer[row] : in_outer[SEG ? 0 : e];
     }
     if (half == 0) rowmul[m] = mul;
-    const h2 sa = {(_Float16)s0, (_Float16)s0};
-    const h2 sb = {(_Float16)s1, (_Float16)s1};
-    const uint32_t wv[4] = {w.x, w.y, w.z, w.w};
-    uint32_t o[16];
+    const uint32_t wv[8] = {w0.x, w0.y, w0.z, w0.w, w1.x, w1.y, w1.z, w1.w};
     // q * s_b is exact in fp16: at most 6 significant bits, within [2^-10, 2688]
-#define BSQ_DEC(q, b) o[(q) * 4 + (b)] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(wv[q], 1.0f, b) * ((q) < 2 ? sa : sb))
 #pragma unroll
-    for (int q = 0; q < 4; ++q) {
-      BSQ_DEC(q, 0);
-      BSQ_DEC(q, 1);
-      BSQ_DEC(q, 2);
-      BSQ_DEC(q, 3);
+    for (int q = 0; q < 8; ++q) {
+      const _Float16 s16 = (_Float16)e4m3_val((sc >> (8 * (q >> 1))) & 0xFFu);
+      const h2 sv = {s16, s16};
+      const h2 v0 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(wv[q], 1.0f, 0) * sv;
+      const h2 v1 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(wv[q], 1.0f, 1) * sv;
+      const h2 v2 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(wv[q], 1.0f, 2) * sv;
+      const h2 v3 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(wv[q], 1.0f, 3) * sv;
+      *reinterpret_cast<uint4*>(&tile[m * LROW + half * 128 + q * 16]) =
+          make_uint4(__builtin_bit_cast(uint32_t, v0), __builtin_bit_cast(uint32_t, v1),
+                     __builtin_bit_cast(uint32_t, v2), __builtin_bit_cast(uint32_t, v3));
     }
-#undef BSQ_DEC
-    uint4* dst = reinterpret_cast<uint4*>(&tile[m][half * 32]);
-    dst[0] = make_uint4(o[0], o[1], o[2], o[3]);
-    dst[1] = make_uint4(o[4], o[5], o[6], o[7]);
-    dst[2] = make_uint4(o[8], o[9], o[10], o[11]);
-    dst[3] = make_uint4(o[12], o[13], o[14], o[15]);
   }
   __syncthreads();
 
-  // ---- phase 2: thread -> (channel c0 + lane, tokens m0 + 32*wave .. +31)
-  const int cl = t & 63;
+  // ---- phase 2: thread -> channels c0 + CPT*lane .. +CPT-1, tokens m0 + 32*wave .. +31
+  const int cl = CPT * (t & 63);
   const int tb = t >> 6;
   const int64_t mb = m0 + 32 * tb;
-  if (mb >= Mp) return;
-  const int64_t c = c0 + cl;
-  float z[32];
+  if (mb >= Mp || c0 + cl >= C) return;
+  float z[CPT][32];
 #pragma unroll
   for (int i = 0; i < 32; ++i) {
     const int m = 32 * tb + i;
-    if constexpr (SRC == SRC_BF16) z[i] = __uint_as_float((uint32_t)tile[m][cl] << 16);
-    else if constexpr (SRC == SRC_F32) z[i] = tile[m][cl];
-    else z[i] = (float)__builtin_bit_cast(_Float16, tile[m][cl]) * rowmul[m];
-  }
-  const int64_t obase = base + c * Mp + mb;  // output index of z[0]
-
-  if constexpr (OUTF == BSQ_MXFP8) {
-    float amax = 0.0f;
-#pragma unroll
-    for (int i = 0; i < 32; ++i) amax = fmaxf(amax, fabsf(z[i]));
-    const int ex = e8m0_exponent(amax);
-    const float pw = pow2_neg(ex);
-    uint32_t out[8];
-    if constexpr (RND == BSQ_SR) {
-#pragma unroll
-      for (int g = 0; g < 4; ++g) {
-        const U32x4 w = sr_words(seed, stream_id, (uint64_t)(obase >> 3) + g);
-#pragma unroll
-        for (int h = 0; h < 2; ++h) {
-          float v[4];
-#pragma unroll
-          for (int q = 0; q < 4; ++q) v[q] = sr_e4m3(z[8 * g + 4 * h + q] * pw, r16_of(w, 4 * h + q));
-          out[2 * g + h] = e4m3_exact2(v[0], v[1]) | (e4m3_exact2(v[2], v[3]) << 16);
-        }
+    if constexpr (SRC == SRC_F32) {
+      z[0][i] = *reinterpret_cast<const float*>(&tile[m * LROW + cl * 4]);
+    } else {
+      const uint32_t w = *reinterpret_cast<const uint32_t*>(&tile[m * LROW + cl * 2]);  // 2 channels
+      if constexpr (SRC == SRC_BF16) {
+        z[0][i] = __uint_as_float(w << 16);
+        z[1][i] = __uint_as_float(w & 0xFFFF0000u);
+      } else {
+        const h2 hv = __builtin_bit_cast(h2, w);
+        z[0][i] = (float)hv[0] * rowmul[m];
+        z[1][i] = (float)hv[1] * rowmul[m];
       }
-    } else {  // |y| <= 448: the hardware convert is the nearest-even rounding
-#pragma unroll
-      for (int o = 0; o < 8; ++o)
-        out[o] = e4m3_exact2(z[4 * o] * pw, z[4 * o + 1] * pw) | (e4m3_exact2(z[4 * o + 2] * pw, z[4 * o + 3] * pw) << 16);
     }
-    uint4* dst = reinterpret_cast<uint4*>(out_codes + obase);
-    dst[0] = make_uint4(out[0], out[1], out[2], out[3]);
-    dst[1] = make_uint4(out[4], out[5], out[6], out[7]);
-    out_scales[obase >> 5] = (uint8_t)(ex + 127);
-  } else {
-    // NVFP4 target: outer s_t' from the item maximum, round-up block scales.
-    const float am = __uint_as_float(amax_bits[e]);
-    const float st = am > 0.0f ? am / 2688.0f : 1.0f;
-    if (mt == 0 && blockIdx.y == 0 && t == 0) out_outer[e] = st;
-    const float d = 6.0f * st;
-    uint32_t cw[4];
-    uint32_t sc2[2];
+  }
+
 #pragma unroll
-    for (int hb = 0; hb < 2; ++hb) {
-      float a = 0.0f;
+  for (int ch = 0; ch < CPT; ++ch) {
+    const int64_t c = c0 + cl + ch;
+    const int64_t obase = base + c * Mp + mb;  // output index of z[ch][0]
+    if constexpr (OUTF == BSQ_MXFP8) {
+      float amax = 0.0f;
 #pragma unroll
-      for (int i = 0; i < 16; ++i) a = fmaxf(a, fabsf(z[16 * hb + i]));
-      const uint32_t sc = e4m3_ru_cap(a / d);
-      const float D = e4m3_val(sc) * st;
-      const float inv = D >= kFltMinNormal ? 1.0f / D : 0.0f;
-      sc2[hb] = sc;
+      for (int i = 0; i < 32; ++i) amax = fmaxf(amax, fabsf(z[ch][i]));
+      const int ex = e8m0_exponent(amax);
+      const float pw = pow2_neg(ex);
+      uint32_t out[8];
+      if constexpr (RND == BSQ_SR) {
 #pragma unroll
-      for (int g2 = 0; g2 < 2; ++g2) {
-        const int g = 2 * hb + g2;
-        uint32_t word = 0;
-        float y[8];
-        if constexpr (RND == BSQ_SR) {
+        for (int g = 0; g < 4; ++g) {
           const U32x4 w = sr_words(seed, stream_id, (uint64_t)(obase >> 3) + g);
 #pragma unroll
-          for (int q = 0; q < 4; ++q) y[2 * q] = sr_e2m1(z[8 * g + 2 * q] * inv, r16_of(w, 2 * q)),
-                                      y[2 * q + 1] = sr_e2m1(z[8 * g + 2 * q + 1] * inv, r16_of(w, 2 * q + 1));
-        } else {
+          for (int h = 0; h < 2; ++h) {
+            float v[4];
 #pragma unroll
-          for (int q = 0; q < 8; ++q) y[q] = z[8 * g + q] * inv;
+            for (int q = 0; q < 4; ++q) v[q] = sr_e4m3(z[ch][8 * g + 4 * h + q] * pw, r16_of(w, 4 * h + q));
+            out[2 * g + h] = e4m3_exact2(v[0], v[1]) | (e4m3_exact2(v[2], v[3]) << 16);
+          }
         }
-        word = BSQ_CVT_FP4X2(word, y[0], y[1], 0);
-        word = BSQ_CVT_FP4X2(word, y[2], y[3], 1);
-        word = BSQ_CVT_FP4X2(word, y[4], y[5], 2);
-        word = BSQ_CVT_FP4X2(word, y[6], y[7], 3);
-        cw[g] = word;
+      } else {  // |y| <= 448: the hardware convert is the nearest-even rounding
+#pragma unroll
+        for (int o = 0; o < 8; ++o)
+          out[o] = e4m3_exact2(z[ch][4 * o] * pw, z[ch][4 * o + 1] * pw) |
+                   (e4m3_exact2(z[ch][4 * o + 2] * pw, z[ch][4 * o + 3] * pw) << 16);
       }
-    }
-    // 8-byte stores: with rows % 32 == 16 an output row starts on an 8-byte boundary only
-    *reinterpret_cast<uint2*>(out_codes + (obase >> 1)) = make_uint2(cw[0], cw[1]);
-    out_scales[obase >> 4] = (uint8_t)sc2[0];
-    if (mb + 16 < Mp) {  // else a trailing half block
-      *reinterpret_cast<uint2*>(out_codes + (obase >> 1) + 8) = make_uint2(cw[2], cw[3]);
-      out_scales[(obase >> 4) + 1] = (uint8_t)sc2[1];
+      uint4* dst = reinterpret_cast<uint4*>(out_codes + obase);
+      dst[0] = make_uint4(out[0], out[1], out[2], out[3]);
+      dst[1] = make_uint4(out[4], out[5], out[6], out[7]);
+      out_scales[obase >> 5] = (uint8_t)(ex + 127);
+    } else {
+      // NVFP4 target: outer s_t' from the item maximum, round-up block scales.
+      const float am = __uint_as_float(amax_bits[e]);
+      const float st = am > 0.0f ? am / 2688.0f : 1.0f;
+      if (mt == 0 && blockIdx.y == 0 && t == 0 && ch == 0) out_outer[e] = st;
+      const float d = 6.0f * st;
+      uint32_t cw[4];
+      uint32_t sc2[2];
+#pragma unroll
+      for (int hb = 0; hb < 2; ++hb) {
+        float a = 0.0f;
+#pragma unroll
+        for (int i = 0; i < 16; ++i) a = fmaxf(a, fabsf(z[ch][16 * hb + i]));
+        const uint32_t sc = e4m3_ru_cap(a / d);
+        const float D = e4m3_val(sc) * st;
+        const float inv = D >= kFltMinNormal ? 1.0f / D : 0.0f;
+        sc2[hb] = sc;
+#pragma unroll
+        for (int g2 = 0; g2 < 2; ++g2) {
+          const int g = 2 * hb + g2;
+          uint32_t word = 0;
+          float y[8];
+          if constexpr (RND == BSQ_SR) {
+            const U32x4 w = sr_words(seed, stream_id, (uint64_t)(obase >> 3) + g);
+#pragma unroll
+            for (int q = 0; q < 8; ++q) y[q] = sr_e2m1(z[ch][8 * g + q] * inv, r16_of(w, q));
+          } else {
+#pragma unroll
+            for (int q = 0; q < 8; ++q) y[q] = z[ch][8 * g + q] * inv;
+          }
+          word = BSQ_CVT_FP4X2(word, y[0], y[1], 0);
+          word = BSQ_CVT_FP4X2(word, y[2], y[3], 1);
+          word = BSQ_CVT_FP4X2(word, y[4], y[5], 2);
+          word = BSQ_CVT_FP4X2(word, y[6], y[7], 3);
+          cw[g] = word;
+        }
+      }
+      // 8-byte stores: with rows % 32 == 16 an output row starts on an 8-byte boundary only
+      *reinterpret_cast<uint2*>(out_codes + (obase >> 1)) = make_uint2(cw[0], cw[1]);
+      out_scales[obase >> 4] = (uint8_t)sc2[0];
+      if (mb + 16 < Mp) {  // else a trailing half block
+        *reinterpret_cast<uint2*>(out_codes + (obase >> 1) + 8) = make_uint2(cw[2], cw[3]);
+        out_scales[(obase >> 4) + 1] = (uint8_t)sc2[1];
+      }
     }
   }
 }
@@ -377,7 +392,8 @@ int launch_tq_seg(const void* src, const uint8_t* in_scales, const float* in_out
   const Plan p = make_plan(ws, rows, nseg);
   hipLaunchKernelGGL(k_seg_plan, dim3(1), dim3(1024), 0, s, seg, (int)nseg, rows, C, TM, p.nslots, p.slot_seg,
                      p.slot_mt, p.seg_base, p.seg_start, p.seg_len);
-  const dim3 grid((unsigned)p.nslots, (unsigned)(C / TC));
+  constexpr int TCH = tile_channels<SRC>();
+  const dim3 grid((unsigned)p.nslots, (unsigned)((C + TCH - 1) / TCH));
   if (rnd == BSQ_SR)
     hipLaunchKernelGGL((k_tq<SRC, BSQ_MXFP8, BSQ_SR, true>), grid, dim3(kThreads), 0, s, src, in_scales, in_outer,
                        in_mode, C, in_rows, gather, p.seg_start, p.seg_len, p.slot_seg, p.slot_mt, p.seg_base, nullptr,
@@ -477,7 +493,8 @@ extern "C" int bsq_requant_transpose_sr(const uint8_t* codes, const uint8_t* sca
   BSQ_REQUIRE(codes && scales && outer && out_codes && out_scales, BSQ_E_NULL);
   BSQ_REQUIRE(bsqh::aligned16(codes) && bsqh::aligned16(out_codes), BSQ_E_ALIGN);
   const int64_t tiles_per = (rows + TM - 1) / TM;
-  const dim3 grid((unsigned)(batch * tiles_per), (unsigned)(cols / TC));
+  constexpr int TCH = tile_channels<SRC_NVFP4>();
+  const dim3 grid((unsigned)(batch * tiles_per), (unsigned)((cols + TCH - 1) / TCH));
   if (out_fmt == BSQ_MXFP8) {
     if (rnd == BSQ_SR)
       hipLaunchKernelGGL((k_tq<SRC_NVFP4, BSQ_MXFP8, BSQ_SR, false>), grid, dim3(kThreads), 0, s, codes, scales, outer,
