@@ -47,6 +47,8 @@ def parse():
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--native-fp8", action="store_true", help="backward GEMMs on the scaled-FP8 MFMA variant")
     p.add_argument("--stages", default="", help="comma list of stages to run (profiling aid); default all")
+    p.add_argument("--copy-calibration", action="store_true",
+                   help="after timing, run a plain 512 MiB device copy three times (reference for HBM byte counters)")
     return p.parse_args()
 
 
@@ -287,6 +289,14 @@ def main():
     traffic = read_traffic(dom, kernel_sha(*src))
     roofline = {"bound": "hbm" if dk["unit"] == "GB/s" else "mfma", "kernel": dom, "achieved": dk["achieved"],
                 "peak": dk["peak"], "unit": dk["unit"], "frac": dk["frac"], "traffic": traffic}
+
+    if args.copy_calibration:
+        src_buf = torch.empty(512 << 20, dtype=torch.uint8, device=dev).fill_(1)
+        dst_buf = torch.empty_like(src_buf)
+        for _ in range(3):
+            dst_buf.copy_(src_buf)
+        torch.cuda.synchronize()
+        del src_buf, dst_buf
 
     cpu = None
     if not args.no_cpu_baseline and stages is None:

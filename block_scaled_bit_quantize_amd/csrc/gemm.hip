@@ -15,25 +15,29 @@
 // K-values: that cannot express NVFP4's E4M3 scale per 16, and (measured) the
 // FP8 dot product inside one instruction keeps only about 15 bits below its
 // largest product, which loses the small products of wide-range blocks. Both
-// formats therefore decode each element once per workgroup tile into LDS as
-// an exactly representable 16-bit value and contract on the dense 16-bit
-// MFMA (v_mfma_f32_32x32x16_{f16,bf16}) with fp32 accumulation:
+// formats therefore contract exactly representable 16-bit values on the
+// dense 16-bit MFMA (v_mfma_f32_32x32x16_{f16,bf16}) with fp32 accumulation:
 //   NVFP4: q * s_b (E2M1 x E4M3: at most 6 significant bits, within
 //          [2^-10, 2688]) is exact in fp16; the two FP32 outer scales multiply
-//          the fp32 sum in the epilogue.
+//          the fp32 sum in the epilogue. Decoding costs two VALU ops per two
+//          values, so each element is decoded once per workgroup into LDS.
 //   MXFP8: q * 2^(s-127) (E4M3 x E8M0) is exact in bf16 for scale codes
-//          10..246 (hardware scaled convert, which applies a power-of-two
-//          scale); no epilogue scaling.
+//          10..246; the hardware scaled convert (which applies a power-of-two
+//          scale) makes two bf16 values per VALU op, so the raw E4M3 codes
+//          stay in LDS (half the LDS bytes of decoded values) and each wave
+//          converts its own fragments in registers; no epilogue scaling.
 // Every product is exact; the only roundings are the fp32 accumulation and
 // the output conversion (bf16 round-to-nearest-even, or fp32).
 //
-// Tiles: 256 x 256 outputs per workgroup of 4 waves (each wave 128 x 128 =
-// 4 x 4 MFMAs of 32 x 32 x 16), K steps of 64 double-buffered in LDS (rows
-// padded to 144 bytes: conflict-free 16-byte fragment reads), global loads
-// one step ahead in registers. Tiles map to (expert, m-tile, n-tile) through
-// an in-workgroup scan of the segment offsets; workgroups are remapped so each
-// XCD (workgroup w runs on XCD w % 8) works on a contiguous range of tiles,
-// keeping an expert's weights and its token rows in that XCD's L2.
+// Tiles: 256 x 256 outputs per workgroup of 8 waves (2 along m x 4 along n,
+// each wave 128 x 64 = 4 x 2 MFMAs of 32 x 32 x 16; two waves per SIMD so one
+// wave's LDS, memory and barrier waits are covered by the other's MFMAs), K
+// steps of 64 double-buffered in LDS (row pitches chosen so 16-byte fragment
+// reads and row writes are bank-conflict free), global loads one step ahead in
+// registers. Tiles map to (expert, m-tile, n-tile) through an in-workgroup
+// scan of the segment offsets; workgroups are remapped so each XCD (workgroup
+// w runs on XCD w % 8) works on a contiguous range of tiles, keeping an
+// expert's weights and its token rows in that XCD's L2.
 //   FPROP/DGRAD (segments along M): row r of expert e reads A row a_row(r)
 //     (gathered token for FPROP) and B[e]; out[r, n].
 //   WGRAD (segments along K): A_e [M, Kp_e], B_e [N, Kp_e] in the padded
@@ -48,10 +52,15 @@ namespace {
 constexpr int BM = 256;
 constexpr int BN = 256;
 constexpr int BK = 64;
-constexpr int kRow = BK * 2 + 16;  // LDS bytes per decoded row (16-bit values + pad)
+constexpr int kRow = BK * 2 + 16;   // LDS bytes per row of decoded 16-bit values (+ pad)
 constexpr int kMaxE = 1024;
 constexpr int kXcds = 8;
-enum { FMT_NVFP4 = 0, FMT_MXFP8 = 1 };
+constexpr int kThreads = 512;       // 8 waves
+constexpr int TJ = 2;               // 32-wide n tiles per wave
+#ifndef BSQ_GEMM_NGROUP
+#define BSQ_GEMM_NGROUP 0
+#endif
+constexpr int kNGroup = BSQ_GEMM_NGROUP;  // tile order within an expert (segments along M)
 
 typedef _Float16 half8 __attribute__((ext_vector_type(8)));
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
@@ -59,88 +68,6 @@ typedef _Float16 h2 __attribute__((ext_vector_type(2)));
 typedef __bf16 bf2 __attribute__((ext_vector_type(2)));
 typedef float f2 __attribute__((ext_vector_type(2)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
-
-// One row's operand data for one K step of 64 elements.
-template <int FMT> struct RowData;
-template <> struct RowData<FMT_NVFP4> {
-  uint4 c[2];   // 64 E2M1 codes
-  uint32_t sc;  // 4 E4M3 scales (one per 16)
-};
-template <> struct RowData<FMT_MXFP8> {
-  uint4 c[4];   // 64 E4M3 codes
-  uint32_t sc;  // 2 E8M0 scales (one per 32) in the low 16 bits
-};
-
-// Load K elements [k0, k0+64) of a row; elements at or past klen read as zero.
-__device__ __forceinline__ void load_row(RowData<FMT_NVFP4>& r, const uint8_t* codes, const uint8_t* scales,
-                                         int64_t k0, int64_t) {
-  const uint4* p = reinterpret_cast<const uint4*>(codes + (k0 >> 1));
-  r.c[0] = p[0];
-  r.c[1] = p[1];
-  r.sc = *reinterpret_cast<const uint32_t*>(scales + (k0 >> 4));
-}
-__device__ __forceinline__ void load_row(RowData<FMT_MXFP8>& r, const uint8_t* codes, const uint8_t* scales,
-                                         int64_t k0, int64_t klen) {
-  const uint4* p = reinterpret_cast<const uint4*>(codes + k0);
-  if (k0 + BK <= klen) {
-#pragma unroll
-    for (int i = 0; i < 4; ++i) r.c[i] = p[i];
-    r.sc = (uint32_t)scales[k0 >> 5] | ((uint32_t)scales[(k0 >> 5) + 1] << 8);
-  } else {  // a segment's last 32 tokens (padded lengths are multiples of 32)
-#pragma unroll
-    for (int i = 0; i < 4; ++i) r.c[i] = k0 + 16 * i < klen ? p[i] : make_uint4(0, 0, 0, 0);
-    r.sc = (uint32_t)scales[k0 >> 5] | (k0 + 32 < klen ? (uint32_t)scales[(k0 >> 5) + 1] << 8 : (127u << 8));
-  }
-}
-
-// Decode elements [16c, 16c+16) of a row's K step into 32 bytes at dst + 32c.
-__device__ __forceinline__ void decode_chunk(const RowData<FMT_NVFP4>& r, uint8_t* dst, int c) {
-  const uint32_t w0 = c < 2 ? (c == 0 ? r.c[0].x : r.c[0].z) : (c == 2 ? r.c[1].x : r.c[1].z);
-  const uint32_t w1 = c < 2 ? (c == 0 ? r.c[0].y : r.c[0].w) : (c == 2 ? r.c[1].y : r.c[1].w);
-  const _Float16 s = (_Float16)e4m3_val((r.sc >> (8 * c)) & 0xFFu);  // one E4M3 scale per 16
-  const h2 sv = {s, s};
-#define BSQ_DEC4(w, v0, v1, v2, v3)                                 \
-  const h2 v0 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, 1.0f, 0) * sv; \
-  const h2 v1 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, 1.0f, 1) * sv; \
-  const h2 v2 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, 1.0f, 2) * sv; \
-  const h2 v3 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, 1.0f, 3) * sv;
-  BSQ_DEC4(w0, a0, a1, a2, a3)
-  BSQ_DEC4(w1, b0, b1, b2, b3)
-#undef BSQ_DEC4
-  uint4* d = reinterpret_cast<uint4*>(dst + 32 * c);
-  d[0] = make_uint4(__builtin_bit_cast(uint32_t, a0), __builtin_bit_cast(uint32_t, a1), __builtin_bit_cast(uint32_t, a2),
-                    __builtin_bit_cast(uint32_t, a3));
-  d[1] = make_uint4(__builtin_bit_cast(uint32_t, b0), __builtin_bit_cast(uint32_t, b1), __builtin_bit_cast(uint32_t, b2),
-                    __builtin_bit_cast(uint32_t, b3));
-}
-__device__ __forceinline__ void decode_chunk(const RowData<FMT_MXFP8>& r, uint8_t* dst, int c) {
-  const uint4 v = r.c[c];
-  // 2^(s-127) as a float: the scaled convert applies its exponent (one E8M0 scale per 32)
-  const float s = __uint_as_float(((r.sc >> (8 * (c >> 1))) & 0xFFu) << 23);
-#define BSQ_DEC2(w, p, q)                                              \
-  const bf2 p = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w, s, false); \
-  const bf2 q = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w, s, true);
-  BSQ_DEC2(v.x, a0, a1)
-  BSQ_DEC2(v.y, a2, a3)
-  BSQ_DEC2(v.z, b0, b1)
-  BSQ_DEC2(v.w, b2, b3)
-#undef BSQ_DEC2
-  uint4* d = reinterpret_cast<uint4*>(dst + 32 * c);
-  d[0] = make_uint4(__builtin_bit_cast(uint32_t, a0), __builtin_bit_cast(uint32_t, a1), __builtin_bit_cast(uint32_t, a2),
-                    __builtin_bit_cast(uint32_t, a3));
-  d[1] = make_uint4(__builtin_bit_cast(uint32_t, b0), __builtin_bit_cast(uint32_t, b1), __builtin_bit_cast(uint32_t, b2),
-                    __builtin_bit_cast(uint32_t, b3));
-}
-
-template <int FMT> struct Frag { typedef half8 type; };
-template <> struct Frag<FMT_MXFP8> { typedef bf16x8 type; };
-
-__device__ __forceinline__ f32x16 mfma16(half8 b, half8 a, f32x16 acc) {
-  return __builtin_amdgcn_mfma_f32_32x32x16_f16(b, a, acc, 0, 0, 0);
-}
-__device__ __forceinline__ f32x16 mfma16(bf16x8 b, bf16x8 a, f32x16 acc) {
-  return __builtin_amdgcn_mfma_f32_32x32x16_bf16(b, a, acc, 0, 0, 0);
-}
 
 struct GemmArgs {
   const uint8_t* a_codes;
@@ -160,25 +87,25 @@ struct GemmArgs {
   void* out;
 };
 
-// WN waves along N (2: 4 waves of 128 x 128, one wave per SIMD; 4: 8 waves of
-// 128 x 64, two waves per SIMD so one wave's LDS/VMEM/barrier waits are
-// covered by the other's MFMAs).
-template <int FMT, int WGRAD, int OUT_F32, int WN>
-__global__ __launch_bounds__(128 * WN) void k_gemm(const GemmArgs g) {
-  constexpr int NT = 128 * WN;            // threads
-  constexpr int TJ = 8 / WN;              // 32-wide n tiles per wave
-  constexpr int RPT = (BM + BN) / NT;     // operand rows loaded and decoded per thread
-  __shared__ __attribute__((aligned(16))) uint8_t sA[2][BM * kRow];
-  __shared__ __attribute__((aligned(16))) uint8_t sB[2][BN * kRow];
-  __shared__ int64_t s_cum[kMaxE];  // inclusive m-tiles (along M) or padded tokens (WGRAD) per expert
-  __shared__ int64_t s_part[256];
+struct Tile {
+  int e;
+  int64_t m0, n0;
+  int64_t Me, seg0;  // segment rows and first row (segments along M)
+  int64_t klen;      // K extent (WGRAD: the expert's padded token count)
+  int64_t kbase;     // WGRAD: padded tokens of the experts before e
+};
 
+// Per-expert unit counts (m-tiles for segments along M, padded tokens for
+// WGRAD) scanned inside the workgroup, then the XCD-aware remap of the
+// workgroup index to a tile. Every thread calls it; false means this
+// workgroup has no tile (uniform across the workgroup).
+template <int WGRAD, int TBM>
+__device__ bool map_tile(const GemmArgs& g, int64_t* s_cum, int64_t* s_part, Tile& tl) {
   const int t = threadIdx.x;
   const int E = g.E;
-  // per-expert unit count: m-tiles (segments along M) or padded tokens (WGRAD)
   auto units = [&](int e) -> int64_t {
     const int64_t len = g.seg_offsets[e + 1] - g.seg_offsets[e];
-    return len <= 0 ? 0 : (WGRAD ? (len + 31) / 32 * 32 : (len + BM - 1) / BM);
+    return len <= 0 ? 0 : (WGRAD ? (len + 31) / 32 * 32 : (len + TBM - 1) / TBM);
   };
   int64_t own = 0;  // units of experts 4t .. 4t+3
   if (t < 256) {
@@ -205,169 +132,87 @@ __global__ __launch_bounds__(128 * WN) void k_gemm(const GemmArgs g) {
   }
   __syncthreads();
   const int64_t ntn = g.N / BN;
-  const int64_t ntm_w = g.M / BM;
+  const int64_t ntm_w = g.M / TBM;
   const int64_t total = WGRAD ? (int64_t)E * ntm_w * ntn : s_cum[E - 1] * ntn;
   const int64_t per_xcd = (total + kXcds - 1) / kXcds;
   const int64_t w = blockIdx.x;
   const int64_t tile = (w % kXcds) * per_xcd + w / kXcds;
-  if (w / kXcds >= per_xcd || tile >= total) return;
+  if (w / kXcds >= per_xcd || tile >= total) return false;
 
-  int e;
-  int64_t m0, n0, Me = 0, seg0 = 0, klen;
+  tl.Me = 0;
+  tl.seg0 = 0;
+  tl.kbase = 0;
   if constexpr (WGRAD) {
-    e = (int)(tile / (ntm_w * ntn));
+    tl.e = (int)(tile / (ntm_w * ntn));
     const int64_t r = tile % (ntm_w * ntn);
-    m0 = (r / ntn) * BM;
-    n0 = (r % ntn) * BN;
-    klen = s_cum[e] - (e ? s_cum[e - 1] : 0);  // Kp_e
+    tl.m0 = (r / ntn) * TBM;
+    tl.n0 = (r % ntn) * BN;
+    tl.kbase = tl.e ? s_cum[tl.e - 1] : 0;
+    tl.klen = s_cum[tl.e] - tl.kbase;  // Kp_e
   } else {
-    const int64_t mtg = tile / ntn;
-    n0 = (tile % ntn) * BN;
+    // expert of the tile: tiles run expert by expert, ntn per m-tile
     int lo = 0, hi = E - 1;
     while (lo < hi) {
       const int mid = (lo + hi) >> 1;
-      if (s_cum[mid] > mtg) hi = mid; else lo = mid + 1;
+      if (s_cum[mid] * ntn > tile) hi = mid; else lo = mid + 1;
     }
-    e = lo;
-    seg0 = g.seg_offsets[e];
-    Me = g.seg_offsets[e + 1] - seg0;
-    if (seg0 < 0 || seg0 + Me > g.M) return;  // malformed offsets: stay inside the buffers
-    m0 = (mtg - (s_cum[e] - (Me + BM - 1) / BM)) * BM;
-    klen = g.K;
-  }
-
-  // ---- the operand rows this thread loads and decodes: tile row id = t + r*NT
-  // (ids below BM are A rows, the rest B rows)
-  const uint8_t* rcode[RPT];
-  const uint8_t* rscal[RPT];
-  int ldst[RPT];  // byte offset of the row in sA / sB
-  bool isA[RPT];
-#pragma unroll
-  for (int r = 0; r < RPT; ++r) {
-    const int id = t + r * NT;
-    isA[r] = id < BM;
-    const int lrow = isA[r] ? id : id - BM;
-    ldst[r] = lrow * kRow;
-    if constexpr (WGRAD) {
-      const int64_t kbase = e ? s_cum[e - 1] : 0;  // sum of earlier padded token counts
-      const int64_t off = isA[r] ? g.M * kbase + (m0 + lrow) * klen : g.N * kbase + (n0 + lrow) * klen;
-      rcode[r] = (isA[r] ? g.a_codes : g.b_codes) + off;
-      rscal[r] = (isA[r] ? g.a_scales : g.b_scales) + off / 32;
-    } else {
-      constexpr int CB = FMT == FMT_NVFP4 ? 2 : 1;   // elements per code byte
-      constexpr int SB = FMT == FMT_NVFP4 ? 16 : 32;  // elements per scale
-      int64_t row;
-      if (isA[r]) {
-        const int64_t m = m0 + lrow < Me ? m0 + lrow : Me - 1;
-        row = g.a_row_index ? (int64_t)g.a_row_index[seg0 + m] : seg0 + m;
-        row = row < 0 ? 0 : (row >= g.a_rows ? g.a_rows - 1 : row);
+    tl.e = lo;
+    tl.seg0 = g.seg_offsets[lo];
+    tl.Me = g.seg_offsets[lo + 1] - tl.seg0;
+    if (tl.seg0 < 0 || tl.seg0 + tl.Me > g.M) return false;  // malformed offsets: stay inside the buffers
+    const int64_t mt_e = (tl.Me + TBM - 1) / TBM;
+    const int64_t li = tile - (s_cum[lo] - mt_e) * ntn;  // tile index within the expert
+    int64_t mt, nt;
+    if constexpr (kNGroup <= 1) {  // m-tile major
+      mt = li / ntn;
+      nt = li % ntn;
+    } else {  // groups of kNGroup n-tiles, each swept over all of the expert's m-tiles
+      const int64_t full = ntn / kNGroup;
+      if (li < full * mt_e * kNGroup) {
+        const int64_t r = li % (mt_e * kNGroup);
+        mt = r / kNGroup;
+        nt = li / (mt_e * kNGroup) * kNGroup + r % kNGroup;
       } else {
-        row = (int64_t)e * g.N + n0 + lrow;
-      }
-      rcode[r] = (isA[r] ? g.a_codes : g.b_codes) + row * (g.K / CB);
-      rscal[r] = (isA[r] ? g.a_scales : g.b_scales) + row * (g.K / SB);
-    }
-  }
-
-  const int wave = t >> 6;
-  const int lane = t & 63;
-  const int wm = wave / WN;  // 128-row half of the tile (m)
-  const int wn = wave % WN;  // (256/WN)-column slice of the tile (n)
-
-  f32x16 acc[4][TJ];
-#pragma unroll
-  for (int i = 0; i < 4; ++i)
-#pragma unroll
-    for (int j = 0; j < TJ; ++j)
-#pragma unroll
-      for (int q = 0; q < 16; ++q) acc[i][j][q] = 0.0f;
-
-  const int nk = (int)((klen + BK - 1) / BK);
-  typedef typename Frag<FMT>::type V8;
-  // fragment: lane -> row (lane & 31), k offset 8 * (lane >> 5) within each 16-wide k slice
-  const int frag_off = (lane & 31) * kRow + (lane >> 5) * 16;
-  const int a_off = wm * 128 * kRow + frag_off;
-  const int b_off = wn * (256 / WN) * kRow + frag_off;
-  V8 fa[2][4], fb[2][TJ];
-#define BSQ_LOAD_FRAGS(slot, buf, ks)                                                              \
-  _Pragma("unroll") for (int i_ = 0; i_ < 4; ++i_) fa[slot][i_] =                                  \
-      *reinterpret_cast<const V8*>(&sA[buf][a_off + i_ * 32 * kRow + (ks) * 32]);                  \
-  _Pragma("unroll") for (int j_ = 0; j_ < TJ; ++j_) fb[slot][j_] =                                 \
-      *reinterpret_cast<const V8*>(&sB[buf][b_off + j_ * 32 * kRow + (ks) * 32]);
-#define BSQ_DST(buf, r) (isA[r] ? &sA[buf][ldst[r]] : &sB[buf][ldst[r]])
-  RowData<FMT> rd[RPT];
-  if (nk > 0) {
-#pragma unroll
-    for (int r = 0; r < RPT; ++r) {
-      load_row(rd[r], rcode[r], rscal[r], 0, klen);
-#pragma unroll
-      for (int c = 0; c < 4; ++c) decode_chunk(rd[r], BSQ_DST(0, r), c);
-      load_row(rd[r], rcode[r], rscal[r], nk > 1 ? BK : 0, klen);
-    }
-    __syncthreads();
-    BSQ_LOAD_FRAGS(0, 0, 0)
-  }
-
-  // Software pipeline per K step (one scheduling region, no branches): for each
-  // 16-wide k slice, read the next slice's fragments, run this slice's MFMAs
-  // and decode one quarter of the next K step into the other LDS buffer; then
-  // fetch the K step after next (clamped: the last iteration decodes and loads
-  // a duplicate that is never read) and swap buffers at the barrier.
-  for (int kt = 0; kt < nk; ++kt) {
-    const int buf = kt & 1;
-#pragma unroll
-    for (int ks = 0; ks < 4; ++ks) {
-      if (ks < 3) {
-        BSQ_LOAD_FRAGS((ks + 1) & 1, buf, ks + 1)
-      }
-#pragma unroll
-      for (int i = 0; i < 4; ++i)
-#pragma unroll
-        for (int j = 0; j < TJ; ++j) acc[i][j] = mfma16(fb[ks & 1][j], fa[ks & 1][i], acc[i][j]);
-#pragma unroll
-      for (int r = 0; r < RPT; ++r) decode_chunk(rd[r], BSQ_DST(buf ^ 1, r), ks);
-      // interleave each MFMA with a few decode VALU ops, the fragment reads and the decode stores
-#pragma unroll
-      for (int m = 0; m < 4 * TJ; ++m) {
-        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);                         // MFMA
-        __builtin_amdgcn_sched_group_barrier(0x002, 12 * RPT / TJ, 0);             // VALU
-        if (m < 4 + TJ) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);         // DS read
-        if (m >= 4 * TJ - 2 * RPT) __builtin_amdgcn_sched_group_barrier(0x200, 1, 0);  // DS write
+        const int64_t r = li - full * mt_e * kNGroup, gs = ntn - full * kNGroup;
+        mt = r / gs;
+        nt = full * kNGroup + r % gs;
       }
     }
-    const int64_t knext = (int64_t)(kt + 2 < nk ? kt + 2 : nk - 1) * BK;
-#pragma unroll
-    for (int r = 0; r < RPT; ++r) load_row(rd[r], rcode[r], rscal[r], knext, klen);
-    __syncthreads();
-    BSQ_LOAD_FRAGS(0, buf ^ 1, 0)
+    tl.m0 = mt * TBM;
+    tl.n0 = nt * BN;
+    tl.klen = g.K;
   }
-#undef BSQ_LOAD_FRAGS
-#undef BSQ_DST
+  return true;
+}
 
-  // ---- epilogue
-  const float sw = FMT == FMT_NVFP4 ? g.b_outer[e] : 1.0f;
+// Writes the wave's 128 x 64 outputs. acc[i][j] holds rows 32i + (lane & 31)
+// and, in element 4q + u, column 32j + 8q + 4(lane >> 5) + u.
+template <int NVFP4, int WGRAD, int OUT_F32>
+__device__ __forceinline__ void store_tile(const GemmArgs& g, const Tile& tl, const f32x16 (&acc)[4][TJ], int wm,
+                                           int wn, int lane) {  // wave rows 128 wm .., columns 64 wn ..
+  const float sw = NVFP4 ? g.b_outer[tl.e] : 1.0f;
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
-    const int64_t m = m0 + wm * 128 + i * 32 + (lane & 31);
-    if (!WGRAD && m >= Me) continue;
+    const int64_t m = tl.m0 + wm * 128 + i * 32 + (lane & 31);
+    if (!WGRAD && m >= tl.Me) continue;
     float s = 1.0f;
-    if constexpr (FMT == FMT_NVFP4) {
+    if constexpr (NVFP4) {
       float sx = g.a_outer[0];
       if (g.a_outer_per_row) {
-        int64_t tok = g.a_row_index ? (int64_t)g.a_row_index[seg0 + m] : seg0 + m;
+        int64_t tok = g.a_row_index ? (int64_t)g.a_row_index[tl.seg0 + m] : tl.seg0 + m;
         tok = tok < 0 ? 0 : (tok >= g.a_rows ? g.a_rows - 1 : tok);
         sx = g.a_outer[tok];
       }
       s = sx * sw;
     }
-    const int64_t obase = (WGRAD ? ((int64_t)e * g.M + m) : (seg0 + m)) * g.N + n0 + wn * (256 / WN);
+    const int64_t obase = (WGRAD ? ((int64_t)tl.e * g.M + m) : (tl.seg0 + m)) * g.N + tl.n0 + wn * 64;
 #pragma unroll
     for (int j = 0; j < TJ; ++j)
 #pragma unroll
       for (int q = 0; q < 4; ++q) {
         const int n = j * 32 + q * 8 + (lane >> 5) * 4;
         float v0 = acc[i][j][4 * q], v1 = acc[i][j][4 * q + 1], v2 = acc[i][j][4 * q + 2], v3 = acc[i][j][4 * q + 3];
-        if constexpr (FMT == FMT_NVFP4) {
+        if constexpr (NVFP4) {
           v0 *= s; v1 *= s; v2 *= s; v3 *= s;
         }
         if constexpr (OUT_F32) {
@@ -382,18 +227,258 @@ __global__ __launch_bounds__(128 * WN) void k_gemm(const GemmArgs g) {
   }
 }
 
-#ifndef BSQ_GEMM_WN
-#define BSQ_GEMM_WN 4
-#endif
+// ============================================================== operand loads
+
+enum { FMT_NVFP4 = 0, FMT_MXFP8 = 1 };
+
+// Byte offset of the codes of row `lrow` of the tile's A (isA) or B operand.
+// A row's scales start at offset / (elements per scale / elements per byte).
+template <int WGRAD, int CB>
+__device__ __forceinline__ int64_t row_off(const GemmArgs& g, const Tile& tl, bool isA, int lrow) {
+  if constexpr (WGRAD) {
+    return isA ? g.M * tl.kbase + (tl.m0 + lrow) * tl.klen : g.N * tl.kbase + (tl.n0 + lrow) * tl.klen;
+  } else {
+    int64_t row;
+    if (isA) {
+      const int64_t m = tl.m0 + lrow < tl.Me ? tl.m0 + lrow : tl.Me - 1;
+      row = g.a_row_index ? (int64_t)g.a_row_index[tl.seg0 + m] : tl.seg0 + m;
+      row = row < 0 ? 0 : (row >= g.a_rows ? g.a_rows - 1 : row);
+    } else {
+      row = (int64_t)tl.e * g.N + tl.n0 + lrow;
+    }
+    return row * (g.K / CB);
+  }
+}
+
+// The K step's codes are fetched in 16-byte chunks with the four (MXFP8) or
+// two (NVFP4) lanes of a row side by side, so one wave instruction reads
+// whole 64- or 32-byte row segments (16 or 32 rows) instead of one chunk of
+// 64 rows. A thread holds one chunk position c of several rows:
+//   NVFP4 (32 codes per row): c = t & 1 of A row t/2 and B row t/2;
+//   MXFP8 (64 codes per row): c = t & 3 of A rows t/4, t/4 + 128 and
+//   B rows t/4, t/4 + 128.
+// The loads never branch and nothing combines loaded values before the
+// decode, so a step's loads stay in flight while the previous step computes.
+template <int FMT> struct Slab;
+template <> struct Slab<FMT_NVFP4> {
+  static constexpr int R = 2;  // rows per thread
+  uint4 c[2];                  // 32 E2M1 codes of each row
+  uint32_t sc[2];              // their two E4M3 scales (low 16 bits)
+};
+template <> struct Slab<FMT_MXFP8> {
+  static constexpr int R = 4;
+  uint4 c[4];      // 16 E4M3 codes of each row
+  uint32_t sc[4];  // their E8M0 scale
+  uint32_t m;      // all ones, or 0 when the chunk lies past the K extent
+};
+
+template <int FMT>
+__device__ __forceinline__ constexpr int slab_chunk(int t) { return FMT == FMT_NVFP4 ? (t & 1) : (t & 3); }
+template <int FMT>
+__device__ __forceinline__ constexpr int slab_row(int t, int i) {  // tile row of row i of the slab
+  return FMT == FMT_NVFP4 ? (t >> 1) : (t >> 2) + 128 * (i & 1);
+}
+template <int FMT>
+__device__ __forceinline__ constexpr bool slab_is_a(int i) { return FMT == FMT_NVFP4 ? i == 0 : i < 2; }
+
+__device__ __forceinline__ void load_slab(Slab<FMT_NVFP4>& r, const GemmArgs& g, const int64_t (&off)[4], int c,
+                                          int64_t k0, int64_t) {
+#pragma unroll
+  for (int i = 0; i < 2; ++i) {
+    const uint8_t* codes = i == 0 ? g.a_codes : g.b_codes;
+    const uint8_t* scales = i == 0 ? g.a_scales : g.b_scales;
+    r.c[i] = *reinterpret_cast<const uint4*>(codes + off[i] + (k0 >> 1) + 16 * c);
+    r.sc[i] = *reinterpret_cast<const uint16_t*>(scales + (off[i] >> 3) + (k0 >> 4) + 2 * c);
+  }
+}
+// MXFP8 rows of WGRAD end where the expert's padded token count ends, a
+// multiple of 32: a last step can hold one 32-wide half, and the chunks of
+// its second half then read a duplicate of the first that the decode masks.
+__device__ __forceinline__ void load_slab(Slab<FMT_MXFP8>& r, const GemmArgs& g, const int64_t (&off)[4], int c,
+                                          int64_t k0, int64_t klen) {
+  const bool in = k0 + 16 * c < klen;
+  const int64_t k = in ? k0 + 16 * c : k0 + 16 * (c & 1);
+  r.m = in ? 0xFFFFFFFFu : 0u;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const uint8_t* codes = i < 2 ? g.a_codes : g.b_codes;
+    const uint8_t* scales = i < 2 ? g.a_scales : g.b_scales;
+    r.c[i] = *reinterpret_cast<const uint4*>(codes + off[i] + k);
+    r.sc[i] = scales[(off[i] >> 5) + (k >> 5)];
+  }
+}
+
+// Decode quarter q of the slab (16 values) into 32 bytes of LDS.
+//   NVFP4: row q / 2, values 16 (q & 1) .. of its chunk, at byte 64c + 32(q & 1);
+//   MXFP8: row q, at byte 32c.
+__device__ __forceinline__ void decode_quarter(const Slab<FMT_NVFP4>& r, uint8_t* dst, int q) {
+  const int i = q >> 1, h = q & 1;
+  const uint32_t w0 = h ? r.c[i].z : r.c[i].x;
+  const uint32_t w1 = h ? r.c[i].w : r.c[i].y;
+  const _Float16 s = (_Float16)e4m3_val((r.sc[i] >> (8 * h)) & 0xFFu);  // one E4M3 scale per 16
+  const h2 sv = {s, s};
+#define BSQ_DEC4(w, v0, v1, v2, v3)                                 \
+  const h2 v0 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, 1.0f, 0) * sv; \
+  const h2 v1 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, 1.0f, 1) * sv; \
+  const h2 v2 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, 1.0f, 2) * sv; \
+  const h2 v3 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, 1.0f, 3) * sv;
+  BSQ_DEC4(w0, a0, a1, a2, a3)
+  BSQ_DEC4(w1, b0, b1, b2, b3)
+#undef BSQ_DEC4
+  uint4* d = reinterpret_cast<uint4*>(dst);
+  d[0] = make_uint4(__builtin_bit_cast(uint32_t, a0), __builtin_bit_cast(uint32_t, a1), __builtin_bit_cast(uint32_t, a2),
+                    __builtin_bit_cast(uint32_t, a3));
+  d[1] = make_uint4(__builtin_bit_cast(uint32_t, b0), __builtin_bit_cast(uint32_t, b1), __builtin_bit_cast(uint32_t, b2),
+                    __builtin_bit_cast(uint32_t, b3));
+}
+__device__ __forceinline__ void decode_quarter(const Slab<FMT_MXFP8>& r, uint8_t* dst, int q) {
+  const uint4 v = make_uint4(r.c[q].x & r.m, r.c[q].y & r.m, r.c[q].z & r.m, r.c[q].w & r.m);
+  // 2^(s-127) as a float: the scaled convert applies its exponent (code 127,
+  // a factor of one, for a masked chunk)
+  const uint32_t code = (r.sc[q] & r.m) | (127u & ~r.m);
+  const float s = __uint_as_float(code << 23);
+#define BSQ_DEC2(w, p, q_)                                              \
+  const bf2 p = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w, s, false); \
+  const bf2 q_ = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w, s, true);
+  BSQ_DEC2(v.x, a0, a1)
+  BSQ_DEC2(v.y, a2, a3)
+  BSQ_DEC2(v.z, b0, b1)
+  BSQ_DEC2(v.w, b2, b3)
+#undef BSQ_DEC2
+  uint4* d = reinterpret_cast<uint4*>(dst);
+  d[0] = make_uint4(__builtin_bit_cast(uint32_t, a0), __builtin_bit_cast(uint32_t, a1), __builtin_bit_cast(uint32_t, a2),
+                    __builtin_bit_cast(uint32_t, a3));
+  d[1] = make_uint4(__builtin_bit_cast(uint32_t, b0), __builtin_bit_cast(uint32_t, b1), __builtin_bit_cast(uint32_t, b2),
+                    __builtin_bit_cast(uint32_t, b3));
+}
+
+template <int FMT> struct Frag { typedef half8 type; };
+template <> struct Frag<FMT_MXFP8> { typedef bf16x8 type; };
+__device__ __forceinline__ f32x16 mfma16(half8 b, half8 a, f32x16 acc) {
+  return __builtin_amdgcn_mfma_f32_32x32x16_f16(b, a, acc, 0, 0, 0);
+}
+__device__ __forceinline__ f32x16 mfma16(bf16x8 b, bf16x8 a, f32x16 acc) {
+  return __builtin_amdgcn_mfma_f32_32x32x16_bf16(b, a, acc, 0, 0, 0);
+}
+
+// ============================================================== kernel
+
+template <int FMT, int WGRAD, int OUT_F32>
+__global__ __launch_bounds__(kThreads) void k_gemm(const GemmArgs g) {
+  static_assert(BM == BN, "A and B LDS buffers share one layout");
+  __shared__ __attribute__((aligned(16))) uint8_t s_ab[4][BM * kRow];  // A buffers 0, 1; B buffers 0, 1
+  uint8_t (*sA)[BM * kRow] = s_ab;
+  uint8_t (*sB)[BM * kRow] = s_ab + 2;
+  __shared__ int64_t s_cum[kMaxE];
+  __shared__ int64_t s_part[256];
+  Tile tl;
+  if (!map_tile<WGRAD, BM>(g, s_cum, s_part, tl)) return;
+
+  // ---- the slab this thread loads and decodes each K step
+  const int t = threadIdx.x;
+  constexpr int SR = Slab<FMT>::R;
+  const int chunk = slab_chunk<FMT>(t);
+  int64_t off[4] = {0, 0, 0, 0};
+  int ldst[SR];  // LDS offset of each slab row's decoded chunk in buffer 0 (A rows: sA, B rows: sB)
+#pragma unroll
+  for (int i = 0; i < SR; ++i) {
+    const int row = slab_row<FMT>(t, i);
+    off[i] = row_off<WGRAD, FMT == FMT_NVFP4 ? 2 : 1>(g, tl, slab_is_a<FMT>(i), row);
+    ldst[i] = (slab_is_a<FMT>(i) ? 0 : 2 * BM * kRow) + row * kRow + chunk * (FMT == FMT_NVFP4 ? 64 : 32);
+  }
+  uint8_t* const lds0 = sA[0];  // sA[0], sA[1], sB[0], sB[1] are contiguous
+  // LDS destination of quarter q in buffer b
+  auto qdst = [&](int b, int q) -> uint8_t* {
+    return FMT == FMT_NVFP4 ? lds0 + ldst[q >> 1] + b * (BM * kRow) + 32 * (q & 1) : lds0 + ldst[q] + b * (BM * kRow);
+  };
+
+  const int wave = t >> 6;
+  const int lane = t & 63;
+  const int wm = wave >> 2;  // 128-row half of the tile (m)
+  const int wn = wave & 3;   // 64-column slice of the tile (n)
+
+  f32x16 acc[4][TJ];
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int j = 0; j < TJ; ++j)
+#pragma unroll
+      for (int q = 0; q < 16; ++q) acc[i][j][q] = 0.0f;
+
+  const int nk = (int)((tl.klen + BK - 1) / BK);
+  typedef typename Frag<FMT>::type V8;
+  // fragment: lane -> row (lane & 31), k offset 8 * (lane >> 5) within each 16-wide k slice
+  const int frag_off = (lane & 31) * kRow + (lane >> 5) * 16;
+  const int a_off = wm * 128 * kRow + frag_off;
+  const int b_off = wn * 64 * kRow + frag_off;
+  V8 fa[2][4], fb[2][TJ];
+#define BSQ_LOAD_FRAGS(slot, buf, ks)                                                              \
+  _Pragma("unroll") for (int i_ = 0; i_ < 4; ++i_) fa[slot][i_] =                                  \
+      *reinterpret_cast<const V8*>(&sA[buf][a_off + i_ * 32 * kRow + (ks) * 32]);                  \
+  _Pragma("unroll") for (int j_ = 0; j_ < TJ; ++j_) fb[slot][j_] =                                 \
+      *reinterpret_cast<const V8*>(&sB[buf][b_off + j_ * 32 * kRow + (ks) * 32]);
+
+  // Software pipeline. At the start of step kt, `cur` holds step kt + 1 as
+  // loaded and the loads of step kt + 2 go out into `nxt` (clamped: the last
+  // steps load and decode a duplicate that is never read). Each 16-wide k
+  // slice then reads the next slice's fragments, runs this slice's MFMAs and
+  // decodes one quarter of `cur` into the other LDS buffer; the barrier at the
+  // end of the step publishes that buffer (every read of it from the previous
+  // step finished before the previous barrier). The two register sets swap
+  // roles every step (the loop body is unrolled twice).
+  Slab<FMT> r0, r1;
+  auto step = [&](int kt, Slab<FMT>& cur, Slab<FMT>& nxt) {
+    const int buf = kt & 1;
+    load_slab(nxt, g, off, chunk, (int64_t)(kt + 2 < nk ? kt + 2 : nk - 1) * BK, tl.klen);
+    __builtin_amdgcn_sched_barrier(0);  // keep the loads here: a whole step ahead of their use
+#pragma unroll
+    for (int ks = 0; ks < 4; ++ks) {
+      if (ks < 3) {
+        BSQ_LOAD_FRAGS((ks + 1) & 1, buf, ks + 1)
+      }
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int j = 0; j < TJ; ++j) acc[i][j] = mfma16(fb[ks & 1][j], fa[ks & 1][i], acc[i][j]);
+      decode_quarter(cur, qdst(buf ^ 1, ks), ks);
+      // interleave each MFMA with a few decode VALU ops, the fragment reads and the decode stores
+#pragma unroll
+      for (int m = 0; m < 4 * TJ; ++m) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);                     // MFMA
+        __builtin_amdgcn_sched_group_barrier(0x002, 12 / TJ, 0);               // VALU
+        if (m < 4 + TJ) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);     // DS read
+        if (m >= 4 * TJ - 2) __builtin_amdgcn_sched_group_barrier(0x200, 1, 0);  // DS write
+      }
+    }
+    __syncthreads();
+    BSQ_LOAD_FRAGS(0, buf ^ 1, 0)
+  };
+  if (nk > 0) {
+    load_slab(r0, g, off, chunk, 0, tl.klen);
+#pragma unroll
+    for (int q = 0; q < 4; ++q) decode_quarter(r0, qdst(0, q), q);
+    load_slab(r0, g, off, chunk, nk > 1 ? BK : 0, tl.klen);
+    __syncthreads();
+    BSQ_LOAD_FRAGS(0, 0, 0)
+  }
+  int kt = 0;
+  for (; kt + 1 < nk; kt += 2) {
+    step(kt, r0, r1);
+    step(kt + 1, r1, r0);
+  }
+  if (kt < nk) step(kt, r0, r1);
+#undef BSQ_LOAD_FRAGS
+
+  store_tile<FMT == FMT_NVFP4, WGRAD, OUT_F32>(g, tl, acc, wm, wn, lane);
+}
 
 template <int FMT, int WGRAD>
 int launch(const GemmArgs& a, int64_t slots, int out_dtype, hipStream_t s) {
-  constexpr int WN = BSQ_GEMM_WN;
   const int64_t grid = (slots + kXcds - 1) / kXcds * kXcds;
   if (out_dtype == BSQ_F32)
-    hipLaunchKernelGGL((k_gemm<FMT, WGRAD, 1, WN>), dim3((unsigned)grid), dim3(128 * WN), 0, s, a);
+    hipLaunchKernelGGL((k_gemm<FMT, WGRAD, 1>), dim3((unsigned)grid), dim3(kThreads), 0, s, a);
   else
-    hipLaunchKernelGGL((k_gemm<FMT, WGRAD, 0, WN>), dim3((unsigned)grid), dim3(128 * WN), 0, s, a);
+    hipLaunchKernelGGL((k_gemm<FMT, WGRAD, 0>), dim3((unsigned)grid), dim3(kThreads), 0, s, a);
   return bsqh::launch_status();
 }
 
