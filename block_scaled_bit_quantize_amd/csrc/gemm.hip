@@ -55,8 +55,15 @@ constexpr int BK = 64;
 constexpr int kRow = BK * 2 + 16;   // LDS bytes per row of decoded 16-bit values (+ pad)
 constexpr int kMaxE = 1024;
 constexpr int kXcds = 8;
-constexpr int kThreads = 512;       // 8 waves
-constexpr int TJ = 2;               // 32-wide n tiles per wave
+#ifndef BSQ_GEMM_WN
+#define BSQ_GEMM_WN 4
+#endif
+// Waves along n. 4: 8 waves of 128 x 64 outputs, two per SIMD, so one wave's
+// LDS, memory and barrier waits are covered by the other's MFMAs. 2: 4 waves
+// of 128 x 128, one per SIMD (a third fewer LDS bytes per MFMA).
+constexpr int WN = BSQ_GEMM_WN;
+constexpr int kThreads = 128 * WN;
+constexpr int TJ = 8 / WN;          // 32-wide n tiles per wave
 #ifndef BSQ_GEMM_NGROUP
 #define BSQ_GEMM_NGROUP 0
 #endif
@@ -185,11 +192,11 @@ __device__ bool map_tile(const GemmArgs& g, int64_t* s_cum, int64_t* s_part, Til
   return true;
 }
 
-// Writes the wave's 128 x 64 outputs. acc[i][j] holds rows 32i + (lane & 31)
+// Writes the wave's 128 x 32TJ outputs. acc[i][j] holds rows 32i + (lane & 31)
 // and, in element 4q + u, column 32j + 8q + 4(lane >> 5) + u.
 template <int NVFP4, int WGRAD, int OUT_F32>
 __device__ __forceinline__ void store_tile(const GemmArgs& g, const Tile& tl, const f32x16 (&acc)[4][TJ], int wm,
-                                           int wn, int lane) {  // wave rows 128 wm .., columns 64 wn ..
+                                           int wn, int lane) {  // wave rows 128 wm .., columns 32 TJ wn ..
   const float sw = NVFP4 ? g.b_outer[tl.e] : 1.0f;
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
@@ -205,7 +212,7 @@ __device__ __forceinline__ void store_tile(const GemmArgs& g, const Tile& tl, co
       }
       s = sx * sw;
     }
-    const int64_t obase = (WGRAD ? ((int64_t)tl.e * g.M + m) : (tl.seg0 + m)) * g.N + tl.n0 + wn * 64;
+    const int64_t obase = (WGRAD ? ((int64_t)tl.e * g.M + m) : (tl.seg0 + m)) * g.N + tl.n0 + wn * 32 * TJ;
 #pragma unroll
     for (int j = 0; j < TJ; ++j)
 #pragma unroll
@@ -250,43 +257,28 @@ __device__ __forceinline__ int64_t row_off(const GemmArgs& g, const Tile& tl, bo
   }
 }
 
-// The K step's codes are fetched in 16-byte chunks with the four (MXFP8) or
-// two (NVFP4) lanes of a row side by side, so one wave instruction reads
-// whole 64- or 32-byte row segments (16 or 32 rows) instead of one chunk of
-// 64 rows. A thread holds one chunk position c of several rows:
-//   NVFP4 (32 codes per row): c = t & 1 of A row t/2 and B row t/2;
-//   MXFP8 (64 codes per row): c = t & 3 of A rows t/4, t/4 + 128 and
-//   B rows t/4, t/4 + 128.
+// The K step's codes are fetched in 16-byte chunks with the lanes of a row
+// side by side (CPR chunks per row: 2 for NVFP4's 32 bytes, 4 for MXFP8's
+// 64), so one wave instruction reads whole row segments instead of one chunk
+// of 64 rows. Thread t holds chunk c = t % CPR of tile rows
+// t / CPR + (kThreads / CPR) i, i < R; rows below BM (i < R/2) are A rows.
 // The loads never branch and nothing combines loaded values before the
 // decode, so a step's loads stay in flight while the previous step computes.
-template <int FMT> struct Slab;
-template <> struct Slab<FMT_NVFP4> {
-  static constexpr int R = 2;  // rows per thread
-  uint4 c[2];                  // 32 E2M1 codes of each row
-  uint32_t sc[2];              // their two E4M3 scales (low 16 bits)
-};
-template <> struct Slab<FMT_MXFP8> {
-  static constexpr int R = 4;
-  uint4 c[4];      // 16 E4M3 codes of each row
-  uint32_t sc[4];  // their E8M0 scale
-  uint32_t m;      // all ones, or 0 when the chunk lies past the K extent
+template <int FMT> struct Slab {
+  static constexpr int CPR = FMT == FMT_NVFP4 ? 2 : 4;
+  static constexpr int R = (BM + BN) * CPR / kThreads;  // rows per thread
+  uint4 c[R];      // NVFP4: 32 E2M1 codes; MXFP8: 16 E4M3 codes of each row
+  uint32_t sc[R];  // NVFP4: the chunk's two E4M3 scales; MXFP8: its E8M0 scale
+  uint32_t m;      // MXFP8: all ones, or 0 when the chunk lies past the K extent
 };
 
-template <int FMT>
-__device__ __forceinline__ constexpr int slab_chunk(int t) { return FMT == FMT_NVFP4 ? (t & 1) : (t & 3); }
-template <int FMT>
-__device__ __forceinline__ constexpr int slab_row(int t, int i) {  // tile row of row i of the slab
-  return FMT == FMT_NVFP4 ? (t >> 1) : (t >> 2) + 128 * (i & 1);
-}
-template <int FMT>
-__device__ __forceinline__ constexpr bool slab_is_a(int i) { return FMT == FMT_NVFP4 ? i == 0 : i < 2; }
-
-__device__ __forceinline__ void load_slab(Slab<FMT_NVFP4>& r, const GemmArgs& g, const int64_t (&off)[4], int c,
+__device__ __forceinline__ void load_slab(Slab<FMT_NVFP4>& r, const GemmArgs& g, const int64_t* off, int c,
                                           int64_t k0, int64_t) {
+  constexpr int R = Slab<FMT_NVFP4>::R;
 #pragma unroll
-  for (int i = 0; i < 2; ++i) {
-    const uint8_t* codes = i == 0 ? g.a_codes : g.b_codes;
-    const uint8_t* scales = i == 0 ? g.a_scales : g.b_scales;
+  for (int i = 0; i < R; ++i) {
+    const uint8_t* codes = i < R / 2 ? g.a_codes : g.b_codes;
+    const uint8_t* scales = i < R / 2 ? g.a_scales : g.b_scales;
     r.c[i] = *reinterpret_cast<const uint4*>(codes + off[i] + (k0 >> 1) + 16 * c);
     r.sc[i] = *reinterpret_cast<const uint16_t*>(scales + (off[i] >> 3) + (k0 >> 4) + 2 * c);
   }
@@ -294,15 +286,16 @@ __device__ __forceinline__ void load_slab(Slab<FMT_NVFP4>& r, const GemmArgs& g,
 // MXFP8 rows of WGRAD end where the expert's padded token count ends, a
 // multiple of 32: a last step can hold one 32-wide half, and the chunks of
 // its second half then read a duplicate of the first that the decode masks.
-__device__ __forceinline__ void load_slab(Slab<FMT_MXFP8>& r, const GemmArgs& g, const int64_t (&off)[4], int c,
+__device__ __forceinline__ void load_slab(Slab<FMT_MXFP8>& r, const GemmArgs& g, const int64_t* off, int c,
                                           int64_t k0, int64_t klen) {
+  constexpr int R = Slab<FMT_MXFP8>::R;
   const bool in = k0 + 16 * c < klen;
   const int64_t k = in ? k0 + 16 * c : k0 + 16 * (c & 1);
   r.m = in ? 0xFFFFFFFFu : 0u;
 #pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const uint8_t* codes = i < 2 ? g.a_codes : g.b_codes;
-    const uint8_t* scales = i < 2 ? g.a_scales : g.b_scales;
+  for (int i = 0; i < R; ++i) {
+    const uint8_t* codes = i < R / 2 ? g.a_codes : g.b_codes;
+    const uint8_t* scales = i < R / 2 ? g.a_scales : g.b_scales;
     r.c[i] = *reinterpret_cast<const uint4*>(codes + off[i] + k);
     r.sc[i] = scales[(off[i] >> 5) + (k >> 5)];
   }
@@ -311,6 +304,7 @@ __device__ __forceinline__ void load_slab(Slab<FMT_MXFP8>& r, const GemmArgs& g,
 // Decode quarter q of the slab (16 values) into 32 bytes of LDS.
 //   NVFP4: row q / 2, values 16 (q & 1) .. of its chunk, at byte 64c + 32(q & 1);
 //   MXFP8: row q, at byte 32c.
+template <int FMT> constexpr int quarters() { return FMT == FMT_NVFP4 ? 2 * Slab<FMT>::R : Slab<FMT>::R; }
 __device__ __forceinline__ void decode_quarter(const Slab<FMT_NVFP4>& r, uint8_t* dst, int q) {
   const int i = q >> 1, h = q & 1;
   const uint32_t w0 = h ? r.c[i].z : r.c[i].x;
@@ -366,6 +360,7 @@ __device__ __forceinline__ f32x16 mfma16(bf16x8 b, bf16x8 a, f32x16 acc) {
 template <int FMT, int WGRAD, int OUT_F32>
 __global__ __launch_bounds__(kThreads) void k_gemm(const GemmArgs g) {
   static_assert(BM == BN, "A and B LDS buffers share one layout");
+  static_assert(2 * BM % (kThreads / Slab<FMT>::CPR) == 0, "whole slab rows per thread");
   __shared__ __attribute__((aligned(16))) uint8_t s_ab[4][BM * kRow];  // A buffers 0, 1; B buffers 0, 1
   uint8_t (*sA)[BM * kRow] = s_ab;
   uint8_t (*sB)[BM * kRow] = s_ab + 2;
@@ -377,14 +372,17 @@ __global__ __launch_bounds__(kThreads) void k_gemm(const GemmArgs g) {
   // ---- the slab this thread loads and decodes each K step
   const int t = threadIdx.x;
   constexpr int SR = Slab<FMT>::R;
-  const int chunk = slab_chunk<FMT>(t);
-  int64_t off[4] = {0, 0, 0, 0};
+  constexpr int CPR = Slab<FMT>::CPR;
+  constexpr int QK = quarters<FMT>() / 4;  // quarters decoded per 16-wide k slice
+  const int chunk = t % CPR;
+  int64_t off[SR];
   int ldst[SR];  // LDS offset of each slab row's decoded chunk in buffer 0 (A rows: sA, B rows: sB)
 #pragma unroll
   for (int i = 0; i < SR; ++i) {
-    const int row = slab_row<FMT>(t, i);
-    off[i] = row_off<WGRAD, FMT == FMT_NVFP4 ? 2 : 1>(g, tl, slab_is_a<FMT>(i), row);
-    ldst[i] = (slab_is_a<FMT>(i) ? 0 : 2 * BM * kRow) + row * kRow + chunk * (FMT == FMT_NVFP4 ? 64 : 32);
+    const int row = t / CPR + (kThreads / CPR) * i;  // tile row: A rows below BM, then B rows
+    const bool isA = i < SR / 2;
+    off[i] = row_off<WGRAD, FMT == FMT_NVFP4 ? 2 : 1>(g, tl, isA, row & (BM - 1));
+    ldst[i] = (isA ? 0 : 2 * BM * kRow) + (row & (BM - 1)) * kRow + chunk * (FMT == FMT_NVFP4 ? 64 : 32);
   }
   uint8_t* const lds0 = sA[0];  // sA[0], sA[1], sB[0], sB[1] are contiguous
   // LDS destination of quarter q in buffer b
@@ -394,8 +392,8 @@ __global__ __launch_bounds__(kThreads) void k_gemm(const GemmArgs g) {
 
   const int wave = t >> 6;
   const int lane = t & 63;
-  const int wm = wave >> 2;  // 128-row half of the tile (m)
-  const int wn = wave & 3;   // 64-column slice of the tile (n)
+  const int wm = wave / WN;  // 128-row half of the tile (m)
+  const int wn = wave % WN;  // 32 TJ-column slice of the tile (n)
 
   f32x16 acc[4][TJ];
 #pragma unroll
@@ -410,7 +408,7 @@ __global__ __launch_bounds__(kThreads) void k_gemm(const GemmArgs g) {
   // fragment: lane -> row (lane & 31), k offset 8 * (lane >> 5) within each 16-wide k slice
   const int frag_off = (lane & 31) * kRow + (lane >> 5) * 16;
   const int a_off = wm * 128 * kRow + frag_off;
-  const int b_off = wn * 64 * kRow + frag_off;
+  const int b_off = wn * 32 * TJ * kRow + frag_off;
   V8 fa[2][4], fb[2][TJ];
 #define BSQ_LOAD_FRAGS(slot, buf, ks)                                                              \
   _Pragma("unroll") for (int i_ = 0; i_ < 4; ++i_) fa[slot][i_] =                                  \
@@ -440,14 +438,15 @@ __global__ __launch_bounds__(kThreads) void k_gemm(const GemmArgs g) {
       for (int i = 0; i < 4; ++i)
 #pragma unroll
         for (int j = 0; j < TJ; ++j) acc[i][j] = mfma16(fb[ks & 1][j], fa[ks & 1][i], acc[i][j]);
-      decode_quarter(cur, qdst(buf ^ 1, ks), ks);
+#pragma unroll
+      for (int q = ks * QK; q < (ks + 1) * QK; ++q) decode_quarter(cur, qdst(buf ^ 1, q), q);
       // interleave each MFMA with a few decode VALU ops, the fragment reads and the decode stores
 #pragma unroll
       for (int m = 0; m < 4 * TJ; ++m) {
         __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);                     // MFMA
         __builtin_amdgcn_sched_group_barrier(0x002, 12 / TJ, 0);               // VALU
         if (m < 4 + TJ) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);     // DS read
-        if (m >= 4 * TJ - 2) __builtin_amdgcn_sched_group_barrier(0x200, 1, 0);  // DS write
+        if (m >= 4 * TJ - 2 * QK) __builtin_amdgcn_sched_group_barrier(0x200, 1, 0);  // DS write
       }
     }
     __syncthreads();
@@ -456,7 +455,7 @@ __global__ __launch_bounds__(kThreads) void k_gemm(const GemmArgs g) {
   if (nk > 0) {
     load_slab(r0, g, off, chunk, 0, tl.klen);
 #pragma unroll
-    for (int q = 0; q < 4; ++q) decode_quarter(r0, qdst(0, q), q);
+    for (int q = 0; q < quarters<FMT>(); ++q) decode_quarter(r0, qdst(0, q), q);
     load_slab(r0, g, off, chunk, nk > 1 ? BK : 0, tl.klen);
     __syncthreads();
     BSQ_LOAD_FRAGS(0, 0, 0)
