@@ -120,6 +120,30 @@ __device__ __forceinline__ float sr_e4m3(float y, uint32_t r16) {
   }
   return __uint_as_float(a | s);
 }
+// Eight values at once, y[i] drawing half i & 1 of word i >> 1 of one Philox
+// call (the same draws and decisions as sr_e4m3). When every value is 0 or at
+// least 2^-6 in magnitude, rounding away from zero adds one unit at mantissa
+// bit 20: adding K = 0xFFFF7 - 16 r to the low 20 bits t carries into bit 20
+// exactly when t > 16 r + 8, and K = ((~r) << 4) | 7. The sign bit and zeros
+// pass through unchanged. Otherwise every value takes sr_e4m3.
+__device__ __forceinline__ void sr_e4m3_x8(float (&y)[8], const U32x4& w) {
+  uint32_t mn = 0xFFFFFFFFu;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) mn = min(mn, (__float_as_uint(y[i]) & 0x7FFFFFFFu) - 1u);
+  if (mn >= 0x3C7FFFFFu) {
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      const uint32_t nw = ~w.v[q];
+      const uint32_t k0 = ((nw << 4) & 0xFFFF0u) | 7u;
+      const uint32_t k1 = ((nw >> 12) & 0xFFFF0u) | 7u;
+      y[2 * q] = __uint_as_float((__float_as_uint(y[2 * q]) + k0) & 0xFFF00000u);
+      y[2 * q + 1] = __uint_as_float((__float_as_uint(y[2 * q + 1]) + k1) & 0xFFF00000u);
+    }
+  } else {
+#pragma unroll
+    for (int i = 0; i < 8; ++i) y[i] = sr_e4m3(y[i], r16_of(w, i));
+  }
+}
 // E2M1 target: steps 0.5 below 2, 1 in [2, 4), 2 in [4, 6); 6 and above -> 6.
 __device__ __forceinline__ float sr_e2m1(float y, uint32_t r16) {
   const float m = fabsf(y);

@@ -227,17 +227,15 @@ __global__ __launch_bounds__(kThreads) void k_mxfp8_rows(const T* __restrict__ x
 #pragma unroll
     for (int g = 0; g < 4; ++g) {
       const U32x4 w = sr_words(seed, stream_id, (uint64_t)blk * 4 + g);
+      float v[8];
 #pragma unroll
-      for (int h = 0; h < 2; ++h) {
-        float v[4];
-#pragma unroll
-        for (int q = 0; q < 4; ++q) {
-          const int i = 8 * g + 4 * h + q;
-          const float y = (i < 16 ? a.get(i) : b.get(i - 16)) * pw;
-          v[q] = sr_e4m3(y, r16_of(w, 4 * h + q));
-        }
-        out[2 * g + h] = e4m3_exact2(v[0], v[1]) | (e4m3_exact2(v[2], v[3]) << 16);
+      for (int q = 0; q < 8; ++q) {
+        const int i = 8 * g + q;
+        v[q] = (i < 16 ? a.get(i) : b.get(i - 16)) * pw;
       }
+      sr_e4m3_x8(v, w);
+      out[2 * g] = e4m3_exact2(v[0], v[1]) | (e4m3_exact2(v[2], v[3]) << 16);
+      out[2 * g + 1] = e4m3_exact2(v[4], v[5]) | (e4m3_exact2(v[6], v[7]) << 16);
     }
   } else {
 #pragma unroll

@@ -258,13 +258,12 @@ __global__ __launch_bounds__(kThreads) void k_tq(
 #pragma unroll
         for (int g = 0; g < 4; ++g) {
           const U32x4 w = sr_words(seed, stream_id, (uint64_t)(obase >> 3) + g);
+          float v[8];
 #pragma unroll
-          for (int h = 0; h < 2; ++h) {
-            float v[4];
-#pragma unroll
-            for (int q = 0; q < 4; ++q) v[q] = sr_e4m3(z[ch][8 * g + 4 * h + q] * pw, r16_of(w, 4 * h + q));
-            out[2 * g + h] = e4m3_exact2(v[0], v[1]) | (e4m3_exact2(v[2], v[3]) << 16);
-          }
+          for (int q = 0; q < 8; ++q) v[q] = z[ch][8 * g + q] * pw;
+          sr_e4m3_x8(v, w);
+          out[2 * g] = e4m3_exact2(v[0], v[1]) | (e4m3_exact2(v[2], v[3]) << 16);
+          out[2 * g + 1] = e4m3_exact2(v[4], v[5]) | (e4m3_exact2(v[6], v[7]) << 16);
         }
       } else {  // |y| <= 448: the hardware convert is the nearest-even rounding
 #pragma unroll
