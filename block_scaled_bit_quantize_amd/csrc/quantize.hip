@@ -12,8 +12,7 @@
 // HBM-bound kernels: each thread owns whole blocks, loads them with 16-byte
 // vector loads, reduces the block maximum in registers and writes packed codes
 // with one 8- or 16-byte store. Per-row outer scales reduce across the threads
-// of a row; per-tensor outer scales take a separate max pass that runs over
-// chunks small enough for the second read to come from the on-die cache.
+// of a row; per-tensor outer scales take a separate max pass over the tensor.
 #include "bsq_device.h"
 #include "bsq_internal.h"
 
@@ -22,13 +21,9 @@ using namespace bsqd;
 namespace {
 
 constexpr int kThreads = 256;
-#ifndef BSQ_TENSOR_CHUNK_MB
-#define BSQ_TENSOR_CHUNK_MB 64
-#endif
 // per-tensor outer scales need the group maximum before any block can round:
-// the max pass and the quantize pass alternate over chunks of this size so
-// that the second read can come from the 256 MB Infinity Cache
-constexpr int64_t kTensorChunkBytes = (int64_t)BSQ_TENSOR_CHUNK_MB << 20;
+// one max pass over all items, then the quantize pass
+constexpr int kAmaxVecPerThread = 32;  // 16-byte vectors per thread of the max pass
 
 // 16 consecutive elements of type T (bf16 bit patterns or float).
 template <typename T> struct Blk16;
@@ -266,10 +261,13 @@ int launch_quant(const T* x, int64_t row0, int64_t row_end, int64_t R, int64_t C
 #define BSQ_QL(TPR, MAXB)                                                                          \
   hipLaunchKernelGGL((k_quant_nvfp4<T, TPR, MAXB, MODE>), dim3(grid1(n, kThreads / TPR)), dim3(kThreads), 0, s, \
                      x, row0, row_end, R, C, outer_in, amax, codes, scales, outer_out)
+  // one wave per row up to 512 blocks (the row maximum is a wave reduction),
+  // up to 8 blocks (256 bytes of bf16) in flight per thread
   if (nb <= 16) BSQ_QL(16, 1);
   else if (nb <= 64) BSQ_QL(64, 1);
-  else if (nb <= 256) BSQ_QL(256, 1);
-  else if (nb <= 512) BSQ_QL(256, 2);
+  else if (nb <= 128) BSQ_QL(64, 2);
+  else if (nb <= 256) BSQ_QL(64, 4);
+  else if (nb <= 512) BSQ_QL(64, 8);
   else if (nb <= 1024) BSQ_QL(256, 4);
   else BSQ_QL(256, 8);
 #undef BSQ_QL
@@ -283,19 +281,15 @@ int quantize_nvfp4_t(const T* x, int64_t B, int64_t R, int64_t C, int mode, cons
   if (mode == BSQ_OUTER_ROW) return launch_quant<T, BSQ_OUTER_ROW>(x, 0, rows, R, C, nullptr, nullptr, codes, scales, outer_out, s);
   if (mode == BSQ_OUTER_GIVEN) return launch_quant<T, BSQ_OUTER_GIVEN>(x, 0, rows, R, C, outer_in, nullptr, codes, scales, outer_out, s);
   hipLaunchKernelGGL(k_fill_u32, dim3(grid1(B)), dim3(kThreads), 0, s, ws, 0u, B);
-  const int64_t item_bytes = R * C * (int64_t)sizeof(T);
-  const int64_t chunk = item_bytes >= kTensorChunkBytes ? 1 : kTensorChunkBytes / item_bytes;
-  const int64_t vec = item_bytes / 16;
-  const int64_t per_wg = 8 * kThreads * 4;  // 32 vectors (512 bytes) per thread
+  const int64_t vec = R * C * (int64_t)sizeof(T) / 16;  // per item
+  const int64_t per_wg = (int64_t)kThreads * kAmaxVecPerThread;
   const int64_t gx = (vec + per_wg - 1) / per_wg;
-  for (int64_t i0 = 0; i0 < B; i0 += chunk) {
-    const int64_t ni = (B - i0) < chunk ? (B - i0) : chunk;
+  for (int64_t i0 = 0; i0 < B; i0 += 65535) {  // grid y limit
+    const int64_t ni = (B - i0) < 65535 ? (B - i0) : 65535;
     hipLaunchKernelGGL(k_amax_items<T>, dim3((unsigned)gx, (unsigned)ni), dim3(kThreads), 0, s, x, vec, per_wg, ws,
                        i0);
-    const int st = launch_quant<T, BSQ_OUTER_TENSOR>(x, i0 * R, (i0 + ni) * R, R, C, nullptr, ws, codes, scales, outer_out, s);
-    if (st != BSQ_OK) return st;
   }
-  return bsqh::launch_status();
+  return launch_quant<T, BSQ_OUTER_TENSOR>(x, 0, rows, R, C, nullptr, ws, codes, scales, outer_out, s);
 }
 
 }  // namespace
