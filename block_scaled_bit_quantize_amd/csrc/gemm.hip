@@ -64,10 +64,6 @@ constexpr int kXcds = 8;
 constexpr int WN = BSQ_GEMM_WN;
 constexpr int kThreads = 128 * WN;
 constexpr int TJ = 8 / WN;          // 32-wide n tiles per wave
-#ifndef BSQ_GEMM_NGROUP
-#define BSQ_GEMM_NGROUP 0
-#endif
-constexpr int kNGroup = BSQ_GEMM_NGROUP;  // tile order within an expert (segments along M)
 
 typedef _Float16 half8 __attribute__((ext_vector_type(8)));
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
@@ -103,11 +99,10 @@ struct Tile {
 };
 
 // Per-expert unit counts (m-tiles for segments along M, padded tokens for
-// WGRAD) scanned inside the workgroup, then the XCD-aware remap of the
-// workgroup index to a tile. Every thread calls it; false means this
-// workgroup has no tile (uniform across the workgroup).
+// WGRAD), scanned inside the workgroup into s_cum (inclusive). Every thread
+// calls it; returns the number of output tiles.
 template <int WGRAD, int TBM>
-__device__ bool map_tile(const GemmArgs& g, int64_t* s_cum, int64_t* s_part, Tile& tl) {
+__device__ int64_t scan_units(const GemmArgs& g, int64_t* s_cum, int64_t* s_part) {
   const int t = threadIdx.x;
   const int E = g.E;
   auto units = [&](int e) -> int64_t {
@@ -139,26 +134,27 @@ __device__ bool map_tile(const GemmArgs& g, int64_t* s_cum, int64_t* s_part, Til
   }
   __syncthreads();
   const int64_t ntn = g.N / BN;
-  const int64_t ntm_w = g.M / TBM;
-  const int64_t total = WGRAD ? (int64_t)E * ntm_w * ntn : s_cum[E - 1] * ntn;
-  const int64_t per_xcd = (total + kXcds - 1) / kXcds;
-  const int64_t w = blockIdx.x;
-  const int64_t tile = (w % kXcds) * per_xcd + w / kXcds;
-  if (w / kXcds >= per_xcd || tile >= total) return false;
+  return WGRAD ? (int64_t)E * (g.M / TBM) * ntn : s_cum[E - 1] * ntn;
+}
 
+// Coordinates of tile `tile` (tiles run expert by expert, m-tile major);
+// false for malformed segment offsets (the tile is skipped, uniformly).
+template <int WGRAD, int TBM>
+__device__ bool tile_coords(const GemmArgs& g, const int64_t* s_cum, int64_t tile, Tile& tl) {
+  const int64_t ntn = g.N / BN;
   tl.Me = 0;
   tl.seg0 = 0;
   tl.kbase = 0;
   if constexpr (WGRAD) {
-    tl.e = (int)(tile / (ntm_w * ntn));
-    const int64_t r = tile % (ntm_w * ntn);
+    const int64_t ntm = g.M / TBM;
+    tl.e = (int)(tile / (ntm * ntn));
+    const int64_t r = tile % (ntm * ntn);
     tl.m0 = (r / ntn) * TBM;
     tl.n0 = (r % ntn) * BN;
     tl.kbase = tl.e ? s_cum[tl.e - 1] : 0;
     tl.klen = s_cum[tl.e] - tl.kbase;  // Kp_e
   } else {
-    // expert of the tile: tiles run expert by expert, ntn per m-tile
-    int lo = 0, hi = E - 1;
+    int lo = 0, hi = g.E - 1;
     while (lo < hi) {
       const int mid = (lo + hi) >> 1;
       if (s_cum[mid] * ntn > tile) hi = mid; else lo = mid + 1;
@@ -169,68 +165,107 @@ __device__ bool map_tile(const GemmArgs& g, int64_t* s_cum, int64_t* s_part, Til
     if (tl.seg0 < 0 || tl.seg0 + tl.Me > g.M) return false;  // malformed offsets: stay inside the buffers
     const int64_t mt_e = (tl.Me + TBM - 1) / TBM;
     const int64_t li = tile - (s_cum[lo] - mt_e) * ntn;  // tile index within the expert
-    int64_t mt, nt;
-    if constexpr (kNGroup <= 1) {  // m-tile major
-      mt = li / ntn;
-      nt = li % ntn;
-    } else {  // groups of kNGroup n-tiles, each swept over all of the expert's m-tiles
-      const int64_t full = ntn / kNGroup;
-      if (li < full * mt_e * kNGroup) {
-        const int64_t r = li % (mt_e * kNGroup);
-        mt = r / kNGroup;
-        nt = li / (mt_e * kNGroup) * kNGroup + r % kNGroup;
-      } else {
-        const int64_t r = li - full * mt_e * kNGroup, gs = ntn - full * kNGroup;
-        mt = r / gs;
-        nt = full * kNGroup + r % gs;
-      }
-    }
-    tl.m0 = mt * TBM;
-    tl.n0 = nt * BN;
+    tl.m0 = li / ntn * TBM;
+    tl.n0 = li % ntn * BN;
     tl.klen = g.K;
   }
   return true;
 }
 
-// Writes the wave's 128 x 32TJ outputs. acc[i][j] holds rows 32i + (lane & 31)
-// and, in element 4q + u, column 32j + 8q + 4(lane >> 5) + u.
+// Epilogue. The accumulators pass through LDS so that global stores are
+// whole 16-byte pieces of contiguous output rows. acc[i][j] holds tile row
+// 128 wm + 32 i + (lane & 31) and, in element 4q + u, tile column
+// 32 TJ wn + 32 j + 8 q + 4 (lane >> 5) + u. Rows past the segment (FPROP,
+// DGRAD) are not stored; NVFP4 sums take the two FP32 outer scales. `stage`
+// is the workgroup's LDS (at least 256 x 528 bytes); the caller has made sure
+// no wave still reads it.
 template <int NVFP4, int WGRAD, int OUT_F32>
 __device__ __forceinline__ void store_tile(const GemmArgs& g, const Tile& tl, const f32x16 (&acc)[4][TJ], int wm,
-                                           int wn, int lane) {  // wave rows 128 wm .., columns 32 TJ wn ..
+                                           int wn, int lane, uint8_t* stage) {
   const float sw = NVFP4 ? g.b_outer[tl.e] : 1.0f;
+  float rs[4];  // output scale of each of the lane's rows
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
-    const int64_t m = tl.m0 + wm * 128 + i * 32 + (lane & 31);
-    if (!WGRAD && m >= tl.Me) continue;
-    float s = 1.0f;
+    rs[i] = 1.0f;
     if constexpr (NVFP4) {
+      const int64_t m = tl.m0 + wm * 128 + i * 32 + (lane & 31);
       float sx = g.a_outer[0];
       if (g.a_outer_per_row) {
-        int64_t tok = g.a_row_index ? (int64_t)g.a_row_index[tl.seg0 + m] : tl.seg0 + m;
+        const int64_t mm = m < tl.Me ? m : tl.Me - 1;
+        int64_t tok = g.a_row_index ? (int64_t)g.a_row_index[tl.seg0 + mm] : tl.seg0 + mm;
         tok = tok < 0 ? 0 : (tok >= g.a_rows ? g.a_rows - 1 : tok);
         sx = g.a_outer[tok];
       }
-      s = sx * sw;
+      rs[i] = sx * sw;
     }
-    const int64_t obase = (WGRAD ? ((int64_t)tl.e * g.M + m) : (tl.seg0 + m)) * g.N + tl.n0 + wn * 32 * TJ;
+  }
+  const int t = threadIdx.x;
+  const int64_t rows_left = WGRAD ? BM : tl.Me - tl.m0;  // rows of the tile inside the segment
+  if constexpr (!OUT_F32) {
+    // bf16 rows of 512 bytes at a 520-byte pitch (rows 2 banks apart)
+    constexpr int P = BN * 2 + 8;
 #pragma unroll
-    for (int j = 0; j < TJ; ++j)
+    for (int i = 0; i < 4; ++i) {
+      const int r = wm * 128 + i * 32 + (lane & 31);
 #pragma unroll
-      for (int q = 0; q < 4; ++q) {
-        const int n = j * 32 + q * 8 + (lane >> 5) * 4;
-        float v0 = acc[i][j][4 * q], v1 = acc[i][j][4 * q + 1], v2 = acc[i][j][4 * q + 2], v3 = acc[i][j][4 * q + 3];
-        if constexpr (NVFP4) {
-          v0 *= s; v1 *= s; v2 *= s; v3 *= s;
-        }
-        if constexpr (OUT_F32) {
-          *reinterpret_cast<float4*>(static_cast<float*>(g.out) + obase + n) = make_float4(v0, v1, v2, v3);
-        } else {  // round to nearest even
-          const bf2 lo2 = __builtin_convertvector((f2){v0, v1}, bf2);
-          const bf2 hi2 = __builtin_convertvector((f2){v2, v3}, bf2);
-          *reinterpret_cast<uint2*>(static_cast<uint16_t*>(g.out) + obase + n) =
+      for (int j = 0; j < TJ; ++j)
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          const int c = wn * 32 * TJ + j * 32 + q * 8 + (lane >> 5) * 4;
+          const float s = rs[i];
+          const bf2 lo2 = __builtin_convertvector((f2){acc[i][j][4 * q] * s, acc[i][j][4 * q + 1] * s}, bf2);
+          const bf2 hi2 = __builtin_convertvector((f2){acc[i][j][4 * q + 2] * s, acc[i][j][4 * q + 3] * s}, bf2);
+          *reinterpret_cast<uint2*>(stage + r * P + c * 2) =
               make_uint2(__builtin_bit_cast(uint32_t, lo2), __builtin_bit_cast(uint32_t, hi2));
         }
+    }
+    __syncthreads();
+    // 32 pieces of 16 bytes per row; a wave covers two whole rows
+#pragma unroll 4
+    for (int k = 0; k < BM * 32 / kThreads; ++k) {
+      const int id = t + k * kThreads;
+      const int r = id >> 5, c = id & 31;
+      if (r < rows_left) {
+        const uint4 v = *reinterpret_cast<const uint4*>(stage + r * P + c * 16);
+        const int64_t orow = WGRAD ? (int64_t)tl.e * g.M + tl.m0 + r : tl.seg0 + tl.m0 + r;
+        *reinterpret_cast<uint4*>(static_cast<uint16_t*>(g.out) + orow * g.N + tl.n0 + c * 8) = v;
       }
+    }
+  } else {
+    // fp32: two passes of 128 rows (1024 bytes each at a 1040-byte pitch)
+    constexpr int P = BN * 4 + 16;
+#pragma unroll
+    for (int half = 0; half < 2; ++half) {
+      if (half) __syncthreads();  // the first half's reads are done
+      if (wm == half) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const int r = i * 32 + (lane & 31);
+#pragma unroll
+          for (int j = 0; j < TJ; ++j)
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+              const int c = wn * 32 * TJ + j * 32 + q * 8 + (lane >> 5) * 4;
+              const float s = rs[i];
+              *reinterpret_cast<float4*>(stage + r * P + c * 4) =
+                  make_float4(acc[i][j][4 * q] * s, acc[i][j][4 * q + 1] * s, acc[i][j][4 * q + 2] * s,
+                              acc[i][j][4 * q + 3] * s);
+            }
+        }
+      }
+      __syncthreads();
+#pragma unroll 4
+      for (int k = 0; k < 128 * 64 / kThreads; ++k) {  // 64 pieces of 16 bytes per row
+        const int id = t + k * kThreads;
+        const int r = id >> 6, c = id & 63;
+        if (half * 128 + r < rows_left) {
+          const float4 v = *reinterpret_cast<const float4*>(stage + r * P + c * 16);
+          const int64_t m = tl.m0 + half * 128 + r;
+          const int64_t orow = WGRAD ? (int64_t)tl.e * g.M + m : tl.seg0 + m;
+          *reinterpret_cast<float4*>(static_cast<float*>(g.out) + orow * g.N + tl.n0 + c * 4) = v;
+        }
+      }
+    }
   }
 }
 
@@ -272,21 +307,22 @@ template <int FMT> struct Slab {
   uint32_t m;      // MXFP8: all ones, or 0 when the chunk lies past the K extent
 };
 
-__device__ __forceinline__ void load_slab(Slab<FMT_NVFP4>& r, const GemmArgs& g, const int64_t* off, int c,
+__device__ __forceinline__ void load_slab(Slab<FMT_NVFP4>& r, const GemmArgs& g, const uint32_t* off32, int c,
                                           int64_t k0, int64_t) {
   constexpr int R = Slab<FMT_NVFP4>::R;
 #pragma unroll
   for (int i = 0; i < R; ++i) {
     const uint8_t* codes = i < R / 2 ? g.a_codes : g.b_codes;
     const uint8_t* scales = i < R / 2 ? g.a_scales : g.b_scales;
-    r.c[i] = *reinterpret_cast<const uint4*>(codes + off[i] + (k0 >> 1) + 16 * c);
-    r.sc[i] = *reinterpret_cast<const uint16_t*>(scales + (off[i] >> 3) + (k0 >> 4) + 2 * c);
+    const int64_t off = (int64_t)off32[i] << 5;
+    r.c[i] = *reinterpret_cast<const uint4*>(codes + off + (k0 >> 1) + 16 * c);
+    r.sc[i] = *reinterpret_cast<const uint16_t*>(scales + (off >> 3) + (k0 >> 4) + 2 * c);
   }
 }
 // MXFP8 rows of WGRAD end where the expert's padded token count ends, a
 // multiple of 32: a last step can hold one 32-wide half, and the chunks of
 // its second half then read a duplicate of the first that the decode masks.
-__device__ __forceinline__ void load_slab(Slab<FMT_MXFP8>& r, const GemmArgs& g, const int64_t* off, int c,
+__device__ __forceinline__ void load_slab(Slab<FMT_MXFP8>& r, const GemmArgs& g, const uint32_t* off32, int c,
                                           int64_t k0, int64_t klen) {
   constexpr int R = Slab<FMT_MXFP8>::R;
   const bool in = k0 + 16 * c < klen;
@@ -296,8 +332,9 @@ __device__ __forceinline__ void load_slab(Slab<FMT_MXFP8>& r, const GemmArgs& g,
   for (int i = 0; i < R; ++i) {
     const uint8_t* codes = i < R / 2 ? g.a_codes : g.b_codes;
     const uint8_t* scales = i < R / 2 ? g.a_scales : g.b_scales;
-    r.c[i] = *reinterpret_cast<const uint4*>(codes + off[i] + k);
-    r.sc[i] = scales[(off[i] >> 5) + (k >> 5)];
+    const int64_t off = (int64_t)off32[i] << 5;
+    r.c[i] = *reinterpret_cast<const uint4*>(codes + off + k);
+    r.sc[i] = scales[(off >> 5) + (k >> 5)];
   }
 }
 
@@ -357,17 +394,24 @@ __device__ __forceinline__ f32x16 mfma16(bf16x8 b, bf16x8 a, f32x16 acc) {
 
 // ============================================================== kernel
 
+// Persistent kernel: one workgroup per CU walks its XCD's range of tiles
+// (workgroup w runs on XCD w % 8, so each XCD works on a contiguous range of
+// tiles: an expert's weights and token rows stay in that XCD's L2), with one
+// segment scan per workgroup and no launch or scan cost per tile.
 template <int FMT, int WGRAD, int OUT_F32>
 __global__ __launch_bounds__(kThreads) void k_gemm(const GemmArgs g) {
   static_assert(BM == BN, "A and B LDS buffers share one layout");
   static_assert(2 * BM % (kThreads / Slab<FMT>::CPR) == 0, "whole slab rows per thread");
+  static_assert(BM * (BN * 2 + 8) <= 4 * BM * kRow && 128 * (BN * 4 + 16) <= 4 * BM * kRow, "epilogue staging fits");
   __shared__ __attribute__((aligned(16))) uint8_t s_ab[4][BM * kRow];  // A buffers 0, 1; B buffers 0, 1
   uint8_t (*sA)[BM * kRow] = s_ab;
   uint8_t (*sB)[BM * kRow] = s_ab + 2;
   __shared__ int64_t s_cum[kMaxE];
   __shared__ int64_t s_part[256];
-  Tile tl;
-  if (!map_tile<WGRAD, BM>(g, s_cum, s_part, tl)) return;
+  const int64_t total = scan_units<WGRAD, BM>(g, s_cum, s_part);
+  const int64_t per_xcd = (total + kXcds - 1) / kXcds;
+  const int64_t wpx = gridDim.x / kXcds;  // workgroups per XCD (the grid is a multiple of kXcds)
+  const int64_t tile0 = (int64_t)(blockIdx.x % kXcds) * per_xcd;
 
   // ---- the slab this thread loads and decodes each K step
   const int t = threadIdx.x;
@@ -375,14 +419,11 @@ __global__ __launch_bounds__(kThreads) void k_gemm(const GemmArgs g) {
   constexpr int CPR = Slab<FMT>::CPR;
   constexpr int QK = quarters<FMT>() / 4;  // quarters decoded per 16-wide k slice
   const int chunk = t % CPR;
-  int64_t off[SR];
   int ldst[SR];  // LDS offset of each slab row's decoded chunk in buffer 0 (A rows: sA, B rows: sB)
 #pragma unroll
   for (int i = 0; i < SR; ++i) {
     const int row = t / CPR + (kThreads / CPR) * i;  // tile row: A rows below BM, then B rows
-    const bool isA = i < SR / 2;
-    off[i] = row_off<WGRAD, FMT == FMT_NVFP4 ? 2 : 1>(g, tl, isA, row & (BM - 1));
-    ldst[i] = (isA ? 0 : 2 * BM * kRow) + (row & (BM - 1)) * kRow + chunk * (FMT == FMT_NVFP4 ? 64 : 32);
+    ldst[i] = (i < SR / 2 ? 0 : 2 * BM * kRow) + (row & (BM - 1)) * kRow + chunk * (FMT == FMT_NVFP4 ? 64 : 32);
   }
   uint8_t* const lds0 = sA[0];  // sA[0], sA[1], sB[0], sB[1] are contiguous
   // LDS destination of quarter q in buffer b
@@ -394,86 +435,114 @@ __global__ __launch_bounds__(kThreads) void k_gemm(const GemmArgs g) {
   const int lane = t & 63;
   const int wm = wave / WN;  // 128-row half of the tile (m)
   const int wn = wave % WN;  // 32 TJ-column slice of the tile (n)
-
-  f32x16 acc[4][TJ];
-#pragma unroll
-  for (int i = 0; i < 4; ++i)
-#pragma unroll
-    for (int j = 0; j < TJ; ++j)
-#pragma unroll
-      for (int q = 0; q < 16; ++q) acc[i][j][q] = 0.0f;
-
-  const int nk = (int)((tl.klen + BK - 1) / BK);
   typedef typename Frag<FMT>::type V8;
   // fragment: lane -> row (lane & 31), k offset 8 * (lane >> 5) within each 16-wide k slice
   const int frag_off = (lane & 31) * kRow + (lane >> 5) * 16;
   const int a_off = wm * 128 * kRow + frag_off;
   const int b_off = wn * 32 * TJ * kRow + frag_off;
-  V8 fa[2][4], fb[2][TJ];
 #define BSQ_LOAD_FRAGS(slot, buf, ks)                                                              \
   _Pragma("unroll") for (int i_ = 0; i_ < 4; ++i_) fa[slot][i_] =                                  \
       *reinterpret_cast<const V8*>(&sA[buf][a_off + i_ * 32 * kRow + (ks) * 32]);                  \
   _Pragma("unroll") for (int j_ = 0; j_ < TJ; ++j_) fb[slot][j_] =                                 \
       *reinterpret_cast<const V8*>(&sB[buf][b_off + j_ * 32 * kRow + (ks) * 32]);
 
-  // Software pipeline. At the start of step kt, `cur` holds step kt + 1 as
-  // loaded and the loads of step kt + 2 go out into `nxt` (clamped: the last
-  // steps load and decode a duplicate that is never read). Each 16-wide k
-  // slice then reads the next slice's fragments, runs this slice's MFMAs and
-  // decodes one quarter of `cur` into the other LDS buffer; the barrier at the
-  // end of the step publishes that buffer (every read of it from the previous
-  // step finished before the previous barrier). The two register sets swap
-  // roles every step (the loop body is unrolled twice).
-  Slab<FMT> r0, r1;
-  auto step = [&](int kt, Slab<FMT>& cur, Slab<FMT>& nxt) {
-    const int buf = kt & 1;
-    load_slab(nxt, g, off, chunk, (int64_t)(kt + 2 < nk ? kt + 2 : nk - 1) * BK, tl.klen);
-    __builtin_amdgcn_sched_barrier(0);  // keep the loads here: a whole step ahead of their use
+  for (int64_t lt = blockIdx.x / kXcds; lt < per_xcd; lt += wpx) {
+    const int64_t tile = tile0 + lt;
+    if (tile >= total) break;
+    Tile tl;
+    if (!tile_coords<WGRAD, BM>(g, s_cum, tile, tl)) continue;  // uniform across the workgroup
+    uint32_t off[SR];  // row code offsets in units of 32 bytes (every row starts at a multiple of 32)
 #pragma unroll
-    for (int ks = 0; ks < 4; ++ks) {
-      if (ks < 3) {
-        BSQ_LOAD_FRAGS((ks + 1) & 1, buf, ks + 1)
-      }
-#pragma unroll
-      for (int i = 0; i < 4; ++i)
-#pragma unroll
-        for (int j = 0; j < TJ; ++j) acc[i][j] = mfma16(fb[ks & 1][j], fa[ks & 1][i], acc[i][j]);
-#pragma unroll
-      for (int q = ks * QK; q < (ks + 1) * QK; ++q) decode_quarter(cur, qdst(buf ^ 1, q), q);
-      // interleave each MFMA with a few decode VALU ops, the fragment reads and the decode stores
-#pragma unroll
-      for (int m = 0; m < 4 * TJ; ++m) {
-        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);                     // MFMA
-        __builtin_amdgcn_sched_group_barrier(0x002, 12 / TJ, 0);               // VALU
-        if (m < 4 + TJ) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);     // DS read
-        if (m >= 4 * TJ - 2 * QK) __builtin_amdgcn_sched_group_barrier(0x200, 1, 0);  // DS write
-      }
-    }
-    __syncthreads();
-    BSQ_LOAD_FRAGS(0, buf ^ 1, 0)
-  };
-  if (nk > 0) {
-    load_slab(r0, g, off, chunk, 0, tl.klen);
-#pragma unroll
-    for (int q = 0; q < quarters<FMT>(); ++q) decode_quarter(r0, qdst(0, q), q);
-    load_slab(r0, g, off, chunk, nk > 1 ? BK : 0, tl.klen);
-    __syncthreads();
-    BSQ_LOAD_FRAGS(0, 0, 0)
-  }
-  int kt = 0;
-  for (; kt + 1 < nk; kt += 2) {
-    step(kt, r0, r1);
-    step(kt + 1, r1, r0);
-  }
-  if (kt < nk) step(kt, r0, r1);
-#undef BSQ_LOAD_FRAGS
+    for (int i = 0; i < SR; ++i)
+      off[i] = (uint32_t)(row_off<WGRAD, FMT == FMT_NVFP4 ? 2 : 1>(g, tl, i < SR / 2,
+                                                                    (t / CPR + (kThreads / CPR) * i) & (BM - 1)) >> 5);
 
-  store_tile<FMT == FMT_NVFP4, WGRAD, OUT_F32>(g, tl, acc, wm, wn, lane);
+    f32x16 acc[4][TJ];
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+      for (int j = 0; j < TJ; ++j)
+#pragma unroll
+        for (int q = 0; q < 16; ++q) acc[i][j][q] = 0.0f;
+    V8 fa[2][4], fb[2][TJ];
+    const int nk = (int)((tl.klen + BK - 1) / BK);
+
+    // Software pipeline. At the start of step kt, `cur` holds step kt + 1 as
+    // loaded and the loads of step kt + 2 go out into `nxt` (clamped: the last
+    // steps load and decode a duplicate that is never read). Each 16-wide k
+    // slice then reads the next slice's fragments, runs this slice's MFMAs and
+    // decodes one quarter of `cur` into the other LDS buffer; the barrier at the
+    // end of the step publishes that buffer (every read of it from the previous
+    // step finished before the previous barrier). The two register sets swap
+    // roles every step (the loop body is unrolled twice).
+    Slab<FMT> r0, r1;
+    auto step = [&](int kt, Slab<FMT>& cur, Slab<FMT>& nxt) {
+      const int buf = kt & 1;
+      load_slab(nxt, g, off, chunk, (int64_t)(kt + 2 < nk ? kt + 2 : nk - 1) * BK, tl.klen);
+      __builtin_amdgcn_sched_barrier(0);  // keep the loads here: a whole step ahead of their use
+#pragma unroll
+      for (int ks = 0; ks < 4; ++ks) {
+        if (ks < 3) {
+          BSQ_LOAD_FRAGS((ks + 1) & 1, buf, ks + 1)
+        }
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+#pragma unroll
+          for (int j = 0; j < TJ; ++j) acc[i][j] = mfma16(fb[ks & 1][j], fa[ks & 1][i], acc[i][j]);
+#pragma unroll
+        for (int q = ks * QK; q < (ks + 1) * QK; ++q) decode_quarter(cur, qdst(buf ^ 1, q), q);
+        // interleave each MFMA with a few decode VALU ops, the fragment reads and the decode stores
+#pragma unroll
+        for (int m = 0; m < 4 * TJ; ++m) {
+          __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);                     // MFMA
+          __builtin_amdgcn_sched_group_barrier(0x002, 12 / TJ, 0);               // VALU
+          if (m < 4 + TJ) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);     // DS read
+          if (m >= 4 * TJ - 2 * QK) __builtin_amdgcn_sched_group_barrier(0x200, 1, 0);  // DS write
+        }
+      }
+      __syncthreads();
+      BSQ_LOAD_FRAGS(0, buf ^ 1, 0)
+    };
+    if (nk > 0) {
+      load_slab(r0, g, off, chunk, 0, tl.klen);
+#pragma unroll
+      for (int q = 0; q < quarters<FMT>(); ++q) decode_quarter(r0, qdst(0, q), q);
+      load_slab(r0, g, off, chunk, nk > 1 ? BK : 0, tl.klen);
+      __syncthreads();
+      BSQ_LOAD_FRAGS(0, 0, 0)
+    }
+    int kt = 0;
+    for (; kt + 1 < nk; kt += 2) {
+      step(kt, r0, r1);
+      step(kt + 1, r1, r0);
+    }
+    if (kt < nk) step(kt, r0, r1);
+
+    __syncthreads();  // every wave is done with the operand buffers
+    store_tile<FMT == FMT_NVFP4, WGRAD, OUT_F32>(g, tl, acc, wm, wn, lane, lds0);
+    __syncthreads();  // the staging reads are done before the next tile decodes into LDS
+  }
+#undef BSQ_LOAD_FRAGS
+}
+
+// CUs of the current device (one persistent workgroup each).
+int device_cus() {
+  static int cache[64];
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
+  if (cache[dev] <= 0) {
+    int n = 0;
+    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0) n = 256;
+    cache[dev] = n;
+  }
+  return cache[dev];
 }
 
 template <int FMT, int WGRAD>
 int launch(const GemmArgs& a, int64_t slots, int out_dtype, hipStream_t s) {
-  const int64_t grid = (slots + kXcds - 1) / kXcds * kXcds;
+  const int64_t cus = (device_cus() + kXcds - 1) / kXcds * kXcds;
+  int64_t grid = (slots + kXcds - 1) / kXcds * kXcds;
+  if (grid > cus) grid = cus;
   if (out_dtype == BSQ_F32)
     hipLaunchKernelGGL((k_gemm<FMT, WGRAD, 1>), dim3((unsigned)grid), dim3(kThreads), 0, s, a);
   else
