@@ -86,6 +86,17 @@ def algorithmic(seg_host):
     }
 
 
+def stage_sources(stage, native_fp8=False):
+    """HIP sources whose kernels a stage launches (their hash keys the
+    committed HBM traffic figures)."""
+    if stage in ("fprop", "dgrad", "wgrad"):
+        main = "gemm_mxfp8_native.hip" if native_fp8 and stage != "fprop" else "gemm.hip"
+        return (main, "bsq_device.h", "bsq_internal.h")
+    if stage == "route":
+        return ("route.hip", "bsq_internal.h")
+    return ("quantize.hip", "transpose_quant.hip", "bsq_device.h", "bsq_internal.h")
+
+
 def kernel_sha(*files):
     h = hashlib.sha256()
     for f in files:
@@ -282,11 +293,7 @@ def main():
     value = gemm_flops / (ms_per_step * 1e-3) / 1e12
     dom = max(kernels, key=lambda n: kernels[n]["ms"])
     dk = kernels[dom]
-    src = {"fprop": ("gemm.hip",), "dgrad": ("gemm.hip",), "wgrad": ("gemm.hip",)}.get(
-        dom, ("quantize.hip", "transpose_quant.hip"))
-    if args.native_fp8 and dom in ("dgrad", "wgrad"):
-        src = ("gemm_mxfp8_native.hip",)
-    traffic = read_traffic(dom, kernel_sha(*src))
+    traffic = read_traffic(dom, kernel_sha(*stage_sources(dom, args.native_fp8)))
     roofline = {"bound": "hbm" if dk["unit"] == "GB/s" else "mfma", "kernel": dom, "achieved": dk["achieved"],
                 "peak": dk["peak"], "unit": dk["unit"], "frac": dk["frac"], "traffic": traffic}
 
