@@ -144,6 +144,52 @@ __device__ __forceinline__ void sr_e4m3_x8(float (&y)[8], const U32x4& w) {
     for (int i = 0; i < 8; ++i) y[i] = sr_e4m3(y[i], r16_of(w, i));
   }
 }
+// One MX block: 32 values z with E8M0 exponent e (codes of y = z 2^-e, |y| <= 448)
+// rounded stochastically, value i drawing from the Philox call grp0 + i / 8.
+// Scaling by 2^-e keeps the mantissa bits, so when e >= -120 (every z of the
+// fast path is then a normal float) and each z of a group of 8 is 0 or at
+// least 2^(e-6), the one-add rounding of sr_e4m3_x8 applies to z itself and
+// the scaled convert (which divides by its power-of-two scale) makes the
+// codes, two per instruction, packed into the word without shifts. Other
+// groups take y = z 2^-e and sr_e4m3. Codes are the same either way.
+__device__ __forceinline__ void sr_block_e4m3(const float (&z)[32], int e, uint64_t seed, uint64_t stream,
+                                              uint64_t grp0, uint32_t (&out)[8]) {
+  typedef short v2s __attribute__((ext_vector_type(2)));
+  const float scale = __uint_as_float((uint32_t)(e + 127) << 23);  // 2^e, used for e >= -120 only
+  const uint32_t thr = ((uint32_t)(e + 121) << 24) - 2u;           // (bits(2^(e-6)) << 1) - 2
+  const float pw = pow2_neg(e);
+#pragma unroll
+  for (int g = 0; g < 4; ++g) {
+    const U32x4 w = sr_words(seed, stream, grp0 + g);
+    uint32_t mn = 0xFFFFFFFFu;  // zeros map to 0xFFFFFFFE
+#pragma unroll
+    for (int q = 0; q < 8; ++q) mn = min(mn, (__float_as_uint(z[8 * g + q]) << 1) - 2u);
+    if (e >= -120 && mn >= thr) {
+      float v[8];
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const uint32_t nw = ~w.v[q];
+        const uint32_t k0 = ((nw << 4) & 0xFFFF0u) | 7u;
+        const uint32_t k1 = ((nw >> 12) & 0xFFFF0u) | 7u;
+        v[2 * q] = __uint_as_float((__float_as_uint(z[8 * g + 2 * q]) + k0) & 0xFFF00000u);
+        v[2 * q + 1] = __uint_as_float((__float_as_uint(z[8 * g + 2 * q + 1]) + k1) & 0xFFF00000u);
+      }
+#pragma unroll
+      for (int h = 0; h < 2; ++h) {
+        v2s c = {0, 0};
+        c = __builtin_amdgcn_cvt_scalef32_pk_fp8_f32(c, v[4 * h], v[4 * h + 1], scale, false);
+        c = __builtin_amdgcn_cvt_scalef32_pk_fp8_f32(c, v[4 * h + 2], v[4 * h + 3], scale, true);
+        out[2 * g + h] = __builtin_bit_cast(uint32_t, c);
+      }
+    } else {
+      float v[8];
+#pragma unroll
+      for (int q = 0; q < 8; ++q) v[q] = sr_e4m3(z[8 * g + q] * pw, r16_of(w, q));
+      out[2 * g] = e4m3_exact2(v[0], v[1]) | (e4m3_exact2(v[2], v[3]) << 16);
+      out[2 * g + 1] = e4m3_exact2(v[4], v[5]) | (e4m3_exact2(v[6], v[7]) << 16);
+    }
+  }
+}
 // E2M1 target: steps 0.5 below 2, 1 in [2, 4), 2 in [4, 6); 6 and above -> 6.
 __device__ __forceinline__ float sr_e2m1(float y, uint32_t r16) {
   const float m = fabsf(y);

@@ -219,19 +219,10 @@ __global__ __launch_bounds__(kThreads) void k_mxfp8_rows(const T* __restrict__ x
   const float pw = pow2_neg(e);
   uint32_t out[8];
   if constexpr (RND == BSQ_SR) {
+    float z[32];
 #pragma unroll
-    for (int g = 0; g < 4; ++g) {
-      const U32x4 w = sr_words(seed, stream_id, (uint64_t)blk * 4 + g);
-      float v[8];
-#pragma unroll
-      for (int q = 0; q < 8; ++q) {
-        const int i = 8 * g + q;
-        v[q] = (i < 16 ? a.get(i) : b.get(i - 16)) * pw;
-      }
-      sr_e4m3_x8(v, w);
-      out[2 * g] = e4m3_exact2(v[0], v[1]) | (e4m3_exact2(v[2], v[3]) << 16);
-      out[2 * g + 1] = e4m3_exact2(v[4], v[5]) | (e4m3_exact2(v[6], v[7]) << 16);
-    }
+    for (int i = 0; i < 32; ++i) z[i] = i < 16 ? a.get(i) : b.get(i - 16);
+    sr_block_e4m3(z, e, seed, stream_id, (uint64_t)blk * 4, out);
   } else {
 #pragma unroll
     for (int o = 0; o < 8; ++o) {

@@ -128,7 +128,8 @@ __global__ __launch_bounds__(kThreads) void k_tq(
     int in_mode, int64_t C, int64_t R, const int32_t* __restrict__ gather, const int64_t* __restrict__ seg_start_p,
     const int64_t* __restrict__ seg_len_p, const int32_t* __restrict__ slot_seg, const int32_t* __restrict__ slot_mt,
     const int64_t* __restrict__ seg_base, const uint32_t* __restrict__ amax_bits, uint64_t seed, uint64_t stream_id,
-    uint8_t* __restrict__ out_codes, uint8_t* __restrict__ out_scales, float* __restrict__ out_outer) {
+    uint8_t* __restrict__ out_codes, uint8_t* __restrict__ out_scales, float* __restrict__ out_outer,
+    int64_t ntiles) {
   typedef typename TileT<SRC>::type TT;
   constexpr int TCH = tile_channels<SRC>();
   constexpr int CPT = TCH / 64;
@@ -136,26 +137,37 @@ __global__ __launch_bounds__(kThreads) void k_tq(
   __shared__ __attribute__((aligned(16))) uint8_t tile[TM * LROW];
   __shared__ float rowmul[TM];
 
+  // Tiles (token tile x channel tile, channel tiles fastest) are remapped so
+  // that each XCD (workgroup w runs on XCD w % 8) takes a contiguous range:
+  // the channel tiles of one token tile, which share its rows' code and scale
+  // cache lines, then meet in one L2. The grid is 8 * ceil(total / 8).
+  const int64_t nct = (C + TCH - 1) / TCH;
+  const int64_t total = ntiles * nct;
+  const int64_t per_xcd = (total + 7) / 8;
+  const int64_t tid = (int64_t)(blockIdx.x % 8) * per_xcd + blockIdx.x / 8;
+  if (tid >= total) return;
+  const int64_t bx = tid / nct, by = tid % nct;
+
   int64_t e, mt, seg_start, Me, Mp, base;
   if constexpr (SEG) {
-    const int32_t sg = slot_seg[blockIdx.x];
+    const int32_t sg = slot_seg[bx];
     if (sg < 0) return;  // uniform across the workgroup
     e = sg;
-    mt = slot_mt[blockIdx.x];
+    mt = slot_mt[bx];
     seg_start = seg_start_p[e];
     Me = seg_len_p[e];
     Mp = pad32(Me);
     base = seg_base[e];
   } else {
     const int64_t tiles_per = (R + TM - 1) / TM;
-    e = blockIdx.x / tiles_per;
-    mt = blockIdx.x % tiles_per;
+    e = bx / tiles_per;
+    mt = bx % tiles_per;
     seg_start = e * R;
     Me = R;
     Mp = R;
     base = e * C * R;
   }
-  const int64_t c0 = (int64_t)blockIdx.y * TCH;
+  const int64_t c0 = by * TCH;
   const int64_t m0 = mt * TM;
   const int t = threadIdx.x;
 
@@ -252,20 +264,11 @@ __global__ __launch_bounds__(kThreads) void k_tq(
 #pragma unroll
       for (int i = 0; i < 32; ++i) amax = fmaxf(amax, fabsf(z[ch][i]));
       const int ex = e8m0_exponent(amax);
-      const float pw = pow2_neg(ex);
       uint32_t out[8];
       if constexpr (RND == BSQ_SR) {
-#pragma unroll
-        for (int g = 0; g < 4; ++g) {
-          const U32x4 w = sr_words(seed, stream_id, (uint64_t)(obase >> 3) + g);
-          float v[8];
-#pragma unroll
-          for (int q = 0; q < 8; ++q) v[q] = z[ch][8 * g + q] * pw;
-          sr_e4m3_x8(v, w);
-          out[2 * g] = e4m3_exact2(v[0], v[1]) | (e4m3_exact2(v[2], v[3]) << 16);
-          out[2 * g + 1] = e4m3_exact2(v[4], v[5]) | (e4m3_exact2(v[6], v[7]) << 16);
-        }
-      } else {  // |y| <= 448: the hardware convert is the nearest-even rounding
+        sr_block_e4m3(z[ch], ex, seed, stream_id, (uint64_t)(obase >> 3), out);
+      } else {
+        const float pw = pow2_neg(ex);  // |y| <= 448: the hardware convert is the nearest-even rounding
 #pragma unroll
         for (int o = 0; o < 8; ++o)
           out[o] = e4m3_exact2(z[ch][4 * o] * pw, z[ch][4 * o + 1] * pw) |
@@ -279,7 +282,7 @@ __global__ __launch_bounds__(kThreads) void k_tq(
       // NVFP4 target: outer s_t' from the item maximum, round-up block scales.
       const float am = __uint_as_float(amax_bits[e]);
       const float st = am > 0.0f ? am / 2688.0f : 1.0f;
-      if (mt == 0 && blockIdx.y == 0 && t == 0 && ch == 0) out_outer[e] = st;
+      if (mt == 0 && by == 0 && t == 0 && ch == 0) out_outer[e] = st;
       const float d = 6.0f * st;
       uint32_t cw[4];
       uint32_t sc2[2];
@@ -382,6 +385,9 @@ Plan make_plan(void* ws, int64_t rows, int64_t nseg) {
   return p;
 }
 
+// 1-D grid of 8 * ceil(tiles / 8) workgroups for k_tq's XCD-aware remap.
+inline unsigned tq_grid(int64_t ntiles, int64_t nct) { return (unsigned)((ntiles * nct + 7) / 8 * 8); }
+
 // rows: dispatched rows (segments cover [0, rows)); in_rows: rows of the
 // input table that gathered indices point into.
 template <int SRC>
@@ -392,15 +398,15 @@ int launch_tq_seg(const void* src, const uint8_t* in_scales, const float* in_out
   hipLaunchKernelGGL(k_seg_plan, dim3(1), dim3(1024), 0, s, seg, (int)nseg, rows, C, TM, p.nslots, p.slot_seg,
                      p.slot_mt, p.seg_base, p.seg_start, p.seg_len);
   constexpr int TCH = tile_channels<SRC>();
-  const dim3 grid((unsigned)p.nslots, (unsigned)((C + TCH - 1) / TCH));
+  const dim3 grid(tq_grid(p.nslots, (C + TCH - 1) / TCH));
   if (rnd == BSQ_SR)
     hipLaunchKernelGGL((k_tq<SRC, BSQ_MXFP8, BSQ_SR, true>), grid, dim3(kThreads), 0, s, src, in_scales, in_outer,
                        in_mode, C, in_rows, gather, p.seg_start, p.seg_len, p.slot_seg, p.slot_mt, p.seg_base, nullptr,
-                       seed, sid, oc, os, nullptr);
+                       seed, sid, oc, os, nullptr, p.nslots);
   else
     hipLaunchKernelGGL((k_tq<SRC, BSQ_MXFP8, BSQ_RN, true>), grid, dim3(kThreads), 0, s, src, in_scales, in_outer,
                        in_mode, C, in_rows, gather, p.seg_start, p.seg_len, p.slot_seg, p.slot_mt, p.seg_base, nullptr,
-                       seed, sid, oc, os, nullptr);
+                       seed, sid, oc, os, nullptr, p.nslots);
   return bsqh::launch_status();
 }
 
@@ -493,16 +499,17 @@ extern "C" int bsq_requant_transpose_sr(const uint8_t* codes, const uint8_t* sca
   BSQ_REQUIRE(bsqh::aligned16(codes) && bsqh::aligned16(out_codes), BSQ_E_ALIGN);
   const int64_t tiles_per = (rows + TM - 1) / TM;
   constexpr int TCH = tile_channels<SRC_NVFP4>();
-  const dim3 grid((unsigned)(batch * tiles_per), (unsigned)((cols + TCH - 1) / TCH));
+  const int64_t ntiles = batch * tiles_per;
+  const dim3 grid(tq_grid(ntiles, (cols + TCH - 1) / TCH));
   if (out_fmt == BSQ_MXFP8) {
     if (rnd == BSQ_SR)
       hipLaunchKernelGGL((k_tq<SRC_NVFP4, BSQ_MXFP8, BSQ_SR, false>), grid, dim3(kThreads), 0, s, codes, scales, outer,
                          in_mode, cols, rows, nullptr, nullptr, nullptr, nullptr, nullptr, nullptr, nullptr, seed, stream_id,
-                         out_codes, out_scales, nullptr);
+                         out_codes, out_scales, nullptr, ntiles);
     else
       hipLaunchKernelGGL((k_tq<SRC_NVFP4, BSQ_MXFP8, BSQ_RN, false>), grid, dim3(kThreads), 0, s, codes, scales, outer,
                          in_mode, cols, rows, nullptr, nullptr, nullptr, nullptr, nullptr, nullptr, nullptr, seed, stream_id,
-                         out_codes, out_scales, nullptr);
+                         out_codes, out_scales, nullptr, ntiles);
     return bsqh::launch_status();
   }
   BSQ_REQUIRE(out_outer && ws, BSQ_E_NULL);
@@ -516,11 +523,11 @@ extern "C" int bsq_requant_transpose_sr(const uint8_t* codes, const uint8_t* sca
   if (rnd == BSQ_SR)
     hipLaunchKernelGGL((k_tq<SRC_NVFP4, BSQ_NVFP4, BSQ_SR, false>), grid, dim3(kThreads), 0, s, codes, scales, outer,
                        in_mode, cols, rows, nullptr, nullptr, nullptr, nullptr, nullptr, nullptr, amax, seed, stream_id,
-                       out_codes, out_scales, out_outer);
+                       out_codes, out_scales, out_outer, ntiles);
   else
     hipLaunchKernelGGL((k_tq<SRC_NVFP4, BSQ_NVFP4, BSQ_RN, false>), grid, dim3(kThreads), 0, s, codes, scales, outer,
                        in_mode, cols, rows, nullptr, nullptr, nullptr, nullptr, nullptr, nullptr, amax, seed, stream_id,
-                       out_codes, out_scales, out_outer);
+                       out_codes, out_scales, out_outer, ntiles);
   return bsqh::launch_status();
 }
 
