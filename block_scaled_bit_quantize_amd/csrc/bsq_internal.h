@@ -18,6 +18,20 @@ inline int64_t tile_bound(int64_t total_rows, int64_t num_segments, int64_t tile
   return (total_rows + tile - 1) / tile + num_segments;
 }
 
+// Compute units of the current device (persistent kernels launch one
+// workgroup per CU); 256 if the query fails.
+inline int device_cus() {
+  static int cache[64];
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
+  if (cache[dev] <= 0) {
+    int n = 0;
+    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0) n = 256;
+    cache[dev] = n;
+  }
+  return cache[dev];
+}
+
 }  // namespace bsqh
 
 #define BSQ_REQUIRE(cond, err) \

@@ -525,22 +525,9 @@ __global__ __launch_bounds__(kThreads) void k_gemm(const GemmArgs g) {
 #undef BSQ_LOAD_FRAGS
 }
 
-// CUs of the current device (one persistent workgroup each).
-int device_cus() {
-  static int cache[64];
-  int dev = 0;
-  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
-  if (cache[dev] <= 0) {
-    int n = 0;
-    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0) n = 256;
-    cache[dev] = n;
-  }
-  return cache[dev];
-}
-
 template <int FMT, int WGRAD>
 int launch(const GemmArgs& a, int64_t slots, int out_dtype, hipStream_t s) {
-  const int64_t cus = (device_cus() + kXcds - 1) / kXcds * kXcds;
+  const int64_t cus = (bsqh::device_cus() + kXcds - 1) / kXcds * kXcds;
   int64_t grid = (slots + kXcds - 1) / kXcds * kXcds;
   if (grid > cus) grid = cus;
   if (out_dtype == BSQ_F32)

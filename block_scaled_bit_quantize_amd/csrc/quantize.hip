@@ -24,6 +24,9 @@ constexpr int kThreads = 256;
 // per-tensor outer scales need the group maximum before any block can round:
 // one max pass over all items, then the quantize pass
 constexpr int kAmaxVecPerThread = 32;  // 16-byte vectors per thread of the max pass
+// The one-pass per-item kernel serves items of at least 1 MiB of bf16 (a
+// grid-wide wait per item) and at most 4096 items (its slots in the workspace).
+inline bool one_pass_items(int64_t B, int64_t R, int64_t C) { return R * C * 2 >= (1 << 20) && B <= 4096; }
 
 // 16 consecutive elements of type T (bf16 bit patterns or float).
 template <typename T> struct Blk16;
@@ -126,6 +129,29 @@ __global__ __launch_bounds__(kThreads) void k_amax_items(const T* __restrict__ x
   }
 }
 
+// One NVFP4 block of 16 (block maximum am, outer scale st): the E4M3 scale
+// byte and 8 code bytes.
+template <typename T>
+__device__ __forceinline__ void nvfp4_block(const Blk16<T>& b, float am, float st, uint8_t* code_dst,
+                                            uint8_t* scale_dst) {
+  const float d = 6.0f * st;
+  const float r = am / d;
+  const uint32_t sc = e4m3_rne_sat(r);
+  const float D = e4m3_val(sc) * st;
+  const float inv = D >= kFltMinNormal ? 1.0f / D : 0.0f;
+  uint32_t w0 = 0, w1 = 0;
+  w0 = BSQ_CVT_FP4X2(w0, b.get(0) * inv, b.get(1) * inv, 0);
+  w0 = BSQ_CVT_FP4X2(w0, b.get(2) * inv, b.get(3) * inv, 1);
+  w0 = BSQ_CVT_FP4X2(w0, b.get(4) * inv, b.get(5) * inv, 2);
+  w0 = BSQ_CVT_FP4X2(w0, b.get(6) * inv, b.get(7) * inv, 3);
+  w1 = BSQ_CVT_FP4X2(w1, b.get(8) * inv, b.get(9) * inv, 0);
+  w1 = BSQ_CVT_FP4X2(w1, b.get(10) * inv, b.get(11) * inv, 1);
+  w1 = BSQ_CVT_FP4X2(w1, b.get(12) * inv, b.get(13) * inv, 2);
+  w1 = BSQ_CVT_FP4X2(w1, b.get(14) * inv, b.get(15) * inv, 3);
+  *reinterpret_cast<uint2*>(code_dst) = make_uint2(w0, w1);
+  *scale_dst = (uint8_t)sc;
+}
+
 // NVFP4 round-to-nearest quantization of rows [row0, row_end). TPR threads
 // share a row; each owns up to MAXB blocks of 16 (block j = lane + k*TPR).
 template <typename T, int TPR, int MAXB, int MODE>
@@ -180,28 +206,117 @@ __global__ __launch_bounds__(kThreads) void k_quant_nvfp4(
     if (row_ok && tl == 0 && row % rows_per_item == 0) outer_out[item] = st;
   }
 
-  const float d = 6.0f * st;
 #pragma unroll
   for (int k = 0; k < MAXB; ++k) {
     const int64_t j = tl + (int64_t)k * TPR;
-    if (row_ok && j < nb) {
-      const float r = am[k] / d;
-      const uint32_t sc = e4m3_rne_sat(r);
-      const float D = e4m3_val(sc) * st;
-      const float inv = D >= kFltMinNormal ? 1.0f / D : 0.0f;
-      uint32_t w0 = 0, w1 = 0;
-      w0 = BSQ_CVT_FP4X2(w0, blk[k].get(0) * inv, blk[k].get(1) * inv, 0);
-      w0 = BSQ_CVT_FP4X2(w0, blk[k].get(2) * inv, blk[k].get(3) * inv, 1);
-      w0 = BSQ_CVT_FP4X2(w0, blk[k].get(4) * inv, blk[k].get(5) * inv, 2);
-      w0 = BSQ_CVT_FP4X2(w0, blk[k].get(6) * inv, blk[k].get(7) * inv, 3);
-      w1 = BSQ_CVT_FP4X2(w1, blk[k].get(8) * inv, blk[k].get(9) * inv, 0);
-      w1 = BSQ_CVT_FP4X2(w1, blk[k].get(10) * inv, blk[k].get(11) * inv, 1);
-      w1 = BSQ_CVT_FP4X2(w1, blk[k].get(12) * inv, blk[k].get(13) * inv, 2);
-      w1 = BSQ_CVT_FP4X2(w1, blk[k].get(14) * inv, blk[k].get(15) * inv, 3);
-      *reinterpret_cast<uint2*>(codes + row * (C >> 1) + j * 8) = make_uint2(w0, w1);
-      scales[row * nb + j] = (uint8_t)sc;
+    if (row_ok && j < nb) nvfp4_block(blk[k], am[k], st, codes + row * (C >> 1) + j * 8, scales + row * nb + j);
+  }
+}
+
+// Per-item outer scale in one pass over HBM. The grid (one workgroup per CU,
+// all resident, at most kOnePassMaxWg) walks the items in order. Every
+// workgroup loads its share of item e into registers (at most BPT blocks of
+// 16 per thread), publishes its maximum in its own slot slot[e][w] (bit
+// pattern with bit 31 set as the arrival mark: magnitudes have it clear),
+// loads its share of item e + 1, then waits until every slot of item e is
+// marked and quantizes item e from registers with the maximum of the slots.
+// The wait is bounded: after kSpinLimit polls the workgroup reduces the whole
+// item itself (the same maximum, from a second read), so every wave always
+// finishes. The slots start at zero. Slot accesses are relaxed device-scope
+// atomics: no other memory is shared between workgroups (x is only read, each
+// output byte has one writer), so no release/acquire (and no L2 write-back or
+// invalidation on this multi-XCD device) is needed.
+constexpr int kOnePassThreads = 512;
+constexpr int kOnePassMaxWg = 512;
+constexpr uint32_t kSpinLimit = 1u << 22;
+
+template <typename T, int BPT>
+__global__ __launch_bounds__(kOnePassThreads) void k_quant_nvfp4_items(
+    const T* __restrict__ x, int64_t B, int64_t bpi, uint32_t* __restrict__ slot, uint8_t* __restrict__ codes,
+    uint8_t* __restrict__ scales, float* __restrict__ outer_out) {
+  const int nwg = gridDim.x;
+  const int64_t share = (bpi + nwg - 1) / nwg;  // blocks per workgroup and item, <= BPT * threads
+  const int64_t lo = (int64_t)blockIdx.x * share;
+  const int64_t hi = lo + share < bpi ? lo + share : bpi;
+  const int t = threadIdx.x;
+  __shared__ float red[kOnePassThreads / 64];
+  auto wg_max = [&](float m) -> float {  // every thread calls it; result in every thread
+    m = wave_max(m);
+    if ((t & 63) == 0) red[t >> 6] = m;
+    __syncthreads();
+    float r = red[0];
+#pragma unroll
+    for (int w = 1; w < kOnePassThreads / 64; ++w) r = fmaxf(r, red[w]);
+    __syncthreads();
+    return r;
+  };
+  Blk16<T> blk[2][BPT];
+  float am[2][BPT];
+  auto load = [&](int b, int64_t e) -> float {  // share of item e into set b; returns the thread's maximum
+    float m = 0.0f;
+#pragma unroll
+    for (int k = 0; k < BPT; ++k) {
+      const int64_t j = lo + t + (int64_t)k * kOnePassThreads;
+      am[b][k] = 0.0f;
+      if (j < hi) {
+        blk[b][k].load(x + (e * bpi + j) * 16);
+        am[b][k] = blk[b][k].absmax();
+        m = fmaxf(m, am[b][k]);
+      }
+    }
+    return m;
+  };
+  auto publish = [&](int64_t e, float m) {
+    const float r = wg_max(m);
+    if (t == 0) __hip_atomic_store(slot + e * nwg + blockIdx.x, __float_as_uint(r) | 0x80000000u, __ATOMIC_RELAXED,
+                                   __HIP_MEMORY_SCOPE_AGENT);
+  };
+  auto item = [&](int b, int64_t e) {
+    // wait for every workgroup's maximum of item e (thread w polls slot w)
+    float mx = 0.0f;
+    uint32_t spins = 0;
+    for (;;) {
+      uint32_t v = 0x80000000u;
+      if (t < nwg) v = __hip_atomic_load(slot + e * nwg + t, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      if (!__syncthreads_or((v & 0x80000000u) == 0)) {
+        mx = __uint_as_float(v & 0x7FFFFFFFu);
+        break;
+      }
+      if (++spins >= kSpinLimit) {  // uniform: reduce the whole item here
+        for (int64_t j = t; j < bpi; j += kOnePassThreads) {
+          Blk16<T> q;
+          q.load(x + (e * bpi + j) * 16);
+          mx = fmaxf(mx, q.absmax());
+        }
+        break;
+      }
+      __builtin_amdgcn_s_sleep(1);
+    }
+    const float a = wg_max(mx);
+    const float st = a > 0.0f ? a / 2688.0f : 1.0f;
+    if (blockIdx.x == 0 && t == 0) outer_out[e] = st;
+#pragma unroll
+    for (int k = 0; k < BPT; ++k) {
+      const int64_t j = lo + t + (int64_t)k * kOnePassThreads;
+      if (j < hi) nvfp4_block(blk[b][k], am[b][k], st, codes + (e * bpi + j) * 8, scales + e * bpi + j);
+    }
+  };
+  if (B <= 0) return;
+  publish(0, load(0, 0));
+  int64_t e = 0;
+  for (; e + 1 < B; e += 2) {  // register sets alternate: item e in set 0, e + 1 in set 1
+    const float m1 = load(1, e + 1);
+    item(0, e);
+    publish(e + 1, m1);
+    if (e + 2 < B) {
+      const float m2 = load(0, e + 2);
+      item(1, e + 1);
+      publish(e + 2, m2);
+    } else {
+      item(1, e + 1);
     }
   }
+  if (e < B && (B & 1)) item(0, e);
 }
 
 // Row-wise MXFP8: one thread per block of 32 (element index = blk*32 + i).
@@ -271,6 +386,23 @@ int quantize_nvfp4_t(const T* x, int64_t B, int64_t R, int64_t C, int mode, cons
   const int64_t rows = B * R;
   if (mode == BSQ_OUTER_ROW) return launch_quant<T, BSQ_OUTER_ROW>(x, 0, rows, R, C, nullptr, nullptr, codes, scales, outer_out, s);
   if (mode == BSQ_OUTER_GIVEN) return launch_quant<T, BSQ_OUTER_GIVEN>(x, 0, rows, R, C, outer_in, nullptr, codes, scales, outer_out, s);
+  // one pass when the items are large (a grid-wide wait per item) and a
+  // workgroup's share fits in registers
+  const int64_t bpi = R * C / 16;
+  const int64_t nwg = bsqh::device_cus() < kOnePassMaxWg ? bsqh::device_cus() : kOnePassMaxWg;
+  const int64_t per_thread = ((bpi + nwg - 1) / nwg + kOnePassThreads - 1) / kOnePassThreads;
+  if (one_pass_items(B, R, C) && per_thread <= 8) {
+    hipLaunchKernelGGL(k_fill_u32, dim3(grid1(B * nwg)), dim3(kThreads), 0, s, ws, 0u, B * nwg);
+#define BSQ_OP(BPT)                                                                                              \
+  hipLaunchKernelGGL((k_quant_nvfp4_items<T, BPT>), dim3((unsigned)nwg), dim3(kOnePassThreads), 0, s, x, B, bpi, ws, \
+                     codes, scales, outer_out)
+    if (per_thread <= 1) BSQ_OP(1);
+    else if (per_thread <= 2) BSQ_OP(2);
+    else if (per_thread <= 4) BSQ_OP(4);
+    else BSQ_OP(8);
+#undef BSQ_OP
+    return bsqh::launch_status();
+  }
   hipLaunchKernelGGL(k_fill_u32, dim3(grid1(B)), dim3(kThreads), 0, s, ws, 0u, B);
   const int64_t vec = R * C * (int64_t)sizeof(T) / 16;  // per item
   const int64_t per_wg = (int64_t)kThreads * kAmaxVecPerThread;
@@ -289,7 +421,9 @@ extern "C" size_t bsq_quantize_nvfp4_workspace(int64_t batch, int64_t rows, int6
   (void)rows;
   (void)cols;
   if (mode != BSQ_OUTER_TENSOR || batch <= 0) return 0;
-  return (size_t)((batch * 4 + 255) / 256 * 256);
+  // per item: the maximum's bits, or one arrival slot per workgroup of the one-pass kernel
+  const int64_t words = one_pass_items(batch, rows, cols) ? batch * kOnePassMaxWg : batch;
+  return (size_t)((words * 4 + 255) / 256 * 256);
 }
 
 extern "C" int bsq_quantize_nvfp4(const void* x, int dtype, int64_t batch, int64_t rows, int64_t cols, int mode,

@@ -64,6 +64,28 @@ def test_quantize_nvfp4_small(dtype, mode, shape, kind):
     assert np.array_equal(h(go), np.asarray(oo).reshape(-1))
 
 
+@pytest.mark.parametrize("dtype,shape", [("bf16", (3, 300, 4096)), ("f32", (2, 257, 1040)), ("bf16", (1, 4100, 1024))])
+def test_quantize_nvfp4_tensor_one_pass(dtype, shape):
+    """Items of at least 1 MiB take the one-pass grid kernel (shares of blocks
+    per workgroup that do not divide evenly, several items in sequence); the
+    bytes must equal the oracle's."""
+    log(f"quantize_nvfp4 tensor one-pass {dtype} {shape}")
+    rng = np.random.default_rng(7 + shape[1])
+    x = rng.standard_normal(shape).astype(f32)
+    x[0, 1, 5] = 300.0  # an outlier sets item 0's outer scale
+    if dtype == "bf16":
+        bits = synth.bf16_bits(x)
+        x = synth.bf16_to_f32(bits).reshape(shape)
+        xd = bf16_t(bits.reshape(shape))
+    else:
+        xd = t(x)
+    gc, gs, go = bsq.quantize_nvfp4(xd, "tensor")
+    oc, os_, oo = Q.quantize_nvfp4(x, Q.OUTER_TENSOR)
+    assert np.array_equal(h(go), np.asarray(oo).reshape(-1))
+    assert np.array_equal(h(gs), os_)
+    assert np.array_equal(h(gc), oc)
+
+
 def test_quantize_nvfp4_edge_cases():
     # empty tensors, all zeros, largest bf16 values, single block
     log("quantize_nvfp4 edges")
