@@ -13,6 +13,8 @@
 // vector loads, reduces the block maximum in registers and writes packed codes
 // with one 8- or 16-byte store. Per-row outer scales reduce across the threads
 // of a row; per-tensor outer scales take a separate max pass over the tensor.
+#include <cstdlib>
+
 #include "bsq_device.h"
 #include "bsq_internal.h"
 
@@ -220,7 +222,7 @@ __global__ __launch_bounds__(kThreads) void k_quant_nvfp4(
 // pattern with bit 31 set as the arrival mark: magnitudes have it clear),
 // loads its share of item e + 1, then waits until every slot of item e is
 // marked and quantizes item e from registers with the maximum of the slots.
-// The wait is bounded: after kSpinLimit polls the workgroup reduces the whole
+// The wait is bounded: after spin_limit polls the workgroup reduces the whole
 // item itself (the same maximum, from a second read), so every wave always
 // finishes. The slots start at zero. Slot accesses are relaxed device-scope
 // atomics: no other memory is shared between workgroups (x is only read, each
@@ -228,12 +230,19 @@ __global__ __launch_bounds__(kThreads) void k_quant_nvfp4(
 // invalidation on this multi-XCD device) is needed.
 constexpr int kOnePassThreads = 512;
 constexpr int kOnePassMaxWg = 512;
-constexpr uint32_t kSpinLimit = 1u << 22;
+constexpr uint32_t kSpinLimit = 1u << 22;  // polls before a workgroup stops waiting (about 0.1 s)
+
+// The poll limit; the environment variable BSQ_WAIT_POLLS overrides it (tests
+// set 0 to take every workgroup through the fallback).
+inline uint32_t wait_polls() {
+  const char* v = getenv("BSQ_WAIT_POLLS");
+  return v ? (uint32_t)strtoul(v, nullptr, 10) : kSpinLimit;
+}
 
 template <typename T, int BPT>
 __global__ __launch_bounds__(kOnePassThreads) void k_quant_nvfp4_items(
     const T* __restrict__ x, int64_t B, int64_t bpi, uint32_t* __restrict__ slot, uint8_t* __restrict__ codes,
-    uint8_t* __restrict__ scales, float* __restrict__ outer_out) {
+    uint8_t* __restrict__ scales, float* __restrict__ outer_out, uint32_t spin_limit) {
   const int nwg = gridDim.x;
   const int64_t share = (bpi + nwg - 1) / nwg;  // blocks per workgroup and item, <= BPT * threads
   const int64_t lo = (int64_t)blockIdx.x * share;
@@ -282,7 +291,7 @@ __global__ __launch_bounds__(kOnePassThreads) void k_quant_nvfp4_items(
         mx = __uint_as_float(v & 0x7FFFFFFFu);
         break;
       }
-      if (++spins >= kSpinLimit) {  // uniform: reduce the whole item here
+      if (++spins >= spin_limit) {  // uniform: reduce the whole item here
         for (int64_t j = t; j < bpi; j += kOnePassThreads) {
           Blk16<T> q;
           q.load(x + (e * bpi + j) * 16);
@@ -395,7 +404,7 @@ int quantize_nvfp4_t(const T* x, int64_t B, int64_t R, int64_t C, int mode, cons
     hipLaunchKernelGGL(k_fill_u32, dim3(grid1(B * nwg)), dim3(kThreads), 0, s, ws, 0u, B * nwg);
 #define BSQ_OP(BPT)                                                                                              \
   hipLaunchKernelGGL((k_quant_nvfp4_items<T, BPT>), dim3((unsigned)nwg), dim3(kOnePassThreads), 0, s, x, B, bpi, ws, \
-                     codes, scales, outer_out)
+                     codes, scales, outer_out, wait_polls())
     if (per_thread <= 1) BSQ_OP(1);
     else if (per_thread <= 2) BSQ_OP(2);
     else if (per_thread <= 4) BSQ_OP(4);

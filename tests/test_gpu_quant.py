@@ -86,6 +86,28 @@ def test_quantize_nvfp4_tensor_one_pass(dtype, shape):
     assert np.array_equal(h(gc), oc)
 
 
+def test_quantize_nvfp4_tensor_one_pass_wait_fallback():
+    """A poll limit of 0 sends every workgroup of the one-pass kernel that
+    finds a slot unmarked through its fallback (it reduces the item itself);
+    the bytes are unchanged."""
+    import os
+    log("quantize_nvfp4 tensor one-pass, fallback")
+    rng = np.random.default_rng(11)
+    shape = (2, 300, 2048)
+    bits = synth.bf16_bits(rng.standard_normal(shape).astype(f32))
+    x = synth.bf16_to_f32(bits).reshape(shape)
+    os.environ["BSQ_WAIT_POLLS"] = "0"
+    try:
+        gc, gs, go = bsq.quantize_nvfp4(bf16_t(bits.reshape(shape)), "tensor")
+        torch.cuda.synchronize()
+    finally:
+        del os.environ["BSQ_WAIT_POLLS"]
+    oc, os_, oo = Q.quantize_nvfp4(x, Q.OUTER_TENSOR)
+    assert np.array_equal(h(go), np.asarray(oo).reshape(-1))
+    assert np.array_equal(h(gs), os_)
+    assert np.array_equal(h(gc), oc)
+
+
 def test_quantize_nvfp4_edge_cases():
     # empty tensors, all zeros, largest bf16 values, single block
     log("quantize_nvfp4 edges")
