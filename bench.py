@@ -7,7 +7,8 @@ tokens, hidden 4096, 64 experts of 4096 x 1536, top-8 routing -- and of its
 backward (weight requantization and backward GEMMs):
 
   route          top-8 ids -> expert segments
-  quant_x        NVFP4 RTN of x [16384, 4096] bf16, per-token outer scale
+  quant_x        NVFP4 RTN of x [16384, 4096] bf16, per-token outer scale,
+                 Four Over Six block scales (the pages' activation quantizer)
   quant_w        NVFP4 RTN of W [64, 1536, 4096] bf16, per-expert outer scale
   fprop          NVFP4 grouped GEMM y [131072, 1536] (bf16 out)
   requant_w      W_q -> MXFP8 W_q^T [64, 4096, 1536], SR seed 42
@@ -156,7 +157,7 @@ def cpu_baseline(seg_host, row_index_host):
 
     ids = synth.moe_routing(2)
     timed("route", lambda: oroute(ids, E), 1.0)
-    xq = timed("quant_x", lambda: Q.quantize_nvfp4(xs[None], Q.OUTER_ROW), T / R)
+    xq = timed("quant_x", lambda: Q.quantize_nvfp4(xs[None], Q.OUTER_ROW, four_over_six=True), T / R)
     wq = timed("quant_w", lambda: Q.quantize_nvfp4(ws, Q.OUTER_TENSOR), E * F / R)
     seg_g = np.array([0, G_R], dtype=np.int64)
     wsub = (wq[0][:, :G_N], wq[1][:, :G_N], wq[2])
@@ -224,7 +225,7 @@ def main():
             mark("route")
         ri_, seg_ = state.get("ri", ri), state.get("seg", seg)
         if run("quant_x") or "xq" not in state:
-            state["xq"] = bsq.quantize_nvfp4(inp["x"], "row")
+            state["xq"] = bsq.quantize_nvfp4(inp["x"], "row", four_over_six=True)
             mark("quant_x")
         if run("quant_w") or "wq" not in state:
             state["wq"] = bsq.quantize_nvfp4(inp["w"], "tensor")

@@ -19,25 +19,24 @@
 // dense 16-bit MFMA (v_mfma_f32_32x32x16_{f16,bf16}) with fp32 accumulation:
 //   NVFP4: q * s_b (E2M1 x E4M3: at most 6 significant bits, within
 //          [2^-10, 2688]) is exact in fp16; the two FP32 outer scales multiply
-//          the fp32 sum in the epilogue. Decoding costs two VALU ops per two
-//          values, so each element is decoded once per workgroup into LDS.
+//          the fp32 sum in the epilogue.
 //   MXFP8: q * 2^(s-127) (E4M3 x E8M0) is exact in bf16 for scale codes
-//          10..246; the hardware scaled convert (which applies a power-of-two
-//          scale) makes two bf16 values per VALU op, so the raw E4M3 codes
-//          stay in LDS (half the LDS bytes of decoded values) and each wave
-//          converts its own fragments in registers; no epilogue scaling.
+//          10..246 (the hardware scaled convert applies the power-of-two
+//          scale); no epilogue scaling.
+// Each element is decoded once per workgroup into LDS (a per-wave decode in
+// registers repeats it for every wave that reads the row).
 // Every product is exact; the only roundings are the fp32 accumulation and
 // the output conversion (bf16 round-to-nearest-even, or fp32).
 //
-// Tiles: 256 x 256 outputs per workgroup of 8 waves (2 along m x 4 along n,
-// each wave 128 x 64 = 4 x 2 MFMAs of 32 x 32 x 16; two waves per SIMD so one
-// wave's LDS, memory and barrier waits are covered by the other's MFMAs), K
-// steps of 64 double-buffered in LDS (row pitches chosen so 16-byte fragment
-// reads and row writes are bank-conflict free), global loads one step ahead in
-// registers. Tiles map to (expert, m-tile, n-tile) through an in-workgroup
-// scan of the segment offsets; workgroups are remapped so each XCD (workgroup
-// w runs on XCD w % 8) works on a contiguous range of tiles, keeping an
-// expert's weights and its token rows in that XCD's L2.
+// Tiles: 256 x 256 outputs, 8 waves (2 along m x 4 along n, each wave
+// 128 x 64 = 4 x 2 MFMAs of 32 x 32 x 16; two waves per SIMD so one wave's
+// LDS, memory and barrier waits are covered by the other's MFMAs), K steps of
+// 64 double-buffered in LDS (row pitches chosen so 16-byte fragment reads and
+// row writes are bank-conflict free), global loads issued a step ahead into
+// two register sets. Persistent workgroups (one per CU) walk contiguous tile
+// ranges of their XCD (workgroup w runs on XCD w % 8), keeping an expert's
+// weights and token rows in that XCD's L2; tiles map to (expert, m-tile,
+// n-tile) through one in-workgroup scan of the segment offsets.
 //   FPROP/DGRAD (segments along M): row r of expert e reads A row a_row(r)
 //     (gathered token for FPROP) and B[e]; out[r, n].
 //   WGRAD (segments along K): A_e [M, Kp_e], B_e [N, Kp_e] in the padded

@@ -131,17 +131,14 @@ __global__ __launch_bounds__(kThreads) void k_amax_items(const T* __restrict__ x
   }
 }
 
-// One NVFP4 block of 16 (block maximum am, outer scale st): the E4M3 scale
-// byte and 8 code bytes.
+// Element codes of one block with scale code sc (outer st): w0 holds
+// elements 0..7, w1 elements 8..15.
 template <typename T>
-__device__ __forceinline__ void nvfp4_block(const Blk16<T>& b, float am, float st, uint8_t* code_dst,
-                                            uint8_t* scale_dst) {
-  const float d = 6.0f * st;
-  const float r = am / d;
-  const uint32_t sc = e4m3_rne_sat(r);
+__device__ __forceinline__ void nvfp4_codes(const Blk16<T>& b, uint32_t sc, float st, uint32_t& w0, uint32_t& w1) {
   const float D = e4m3_val(sc) * st;
   const float inv = D >= kFltMinNormal ? 1.0f / D : 0.0f;
-  uint32_t w0 = 0, w1 = 0;
+  w0 = 0;
+  w1 = 0;
   w0 = BSQ_CVT_FP4X2(w0, b.get(0) * inv, b.get(1) * inv, 0);
   w0 = BSQ_CVT_FP4X2(w0, b.get(2) * inv, b.get(3) * inv, 1);
   w0 = BSQ_CVT_FP4X2(w0, b.get(4) * inv, b.get(5) * inv, 2);
@@ -150,13 +147,66 @@ __device__ __forceinline__ void nvfp4_block(const Blk16<T>& b, float am, float s
   w1 = BSQ_CVT_FP4X2(w1, b.get(10) * inv, b.get(11) * inv, 1);
   w1 = BSQ_CVT_FP4X2(w1, b.get(12) * inv, b.get(13) * inv, 2);
   w1 = BSQ_CVT_FP4X2(w1, b.get(14) * inv, b.get(15) * inv, 3);
+}
+
+// Squared quantization error of the block in float32, in element order:
+// x^_i = f32(f32(q_i s_b) s_t), e_i = f32(x_i - x^_i), err = sum of f32(e_i^2)
+// with each partial sum rounded (no fused operations).
+template <typename T>
+__device__ __forceinline__ float nvfp4_sq_err(const Blk16<T>& b, uint32_t w0, uint32_t w1, uint32_t sc, float st) {
+  typedef float f2v __attribute__((ext_vector_type(2)));
+  const float sv = e4m3_val(sc);
+  float err = 0.0f;
+#pragma unroll
+  for (int p = 0; p < 8; ++p) {
+    const uint32_t w = p < 4 ? w0 : w1;
+    f2v q;
+    switch (p & 3) {  // decode two codes (byte p & 3 of the word); the selector must be a constant
+      case 0: q = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(w, 1.0f, 0); break;
+      case 1: q = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(w, 1.0f, 1); break;
+      case 2: q = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(w, 1.0f, 2); break;
+      default: q = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(w, 1.0f, 3); break;
+    }
+#pragma unroll
+    for (int u = 0; u < 2; ++u) {
+      const float xh = (q[u] * sv) * st;
+      const float e = b.get(2 * p + u) - xh;
+      err = err + e * e;
+    }
+  }
+  return err;
+}
+
+// One NVFP4 block of 16 (block maximum am, outer scale st): the E4M3 scale
+// byte and 8 code bytes. FS (Four Over Six): the block also tries the scale that maps a_b to 4 and
+// keeps it when its squared error is strictly smaller (ties keep 6).
+template <bool FS, typename T>
+__device__ __forceinline__ void nvfp4_block(const Blk16<T>& b, float am, float st, uint8_t* code_dst,
+                                            uint8_t* scale_dst) {
+  const float d = 6.0f * st;
+  const float r = am / d;
+  uint32_t sc = e4m3_rne_sat(r);
+  uint32_t w0, w1;
+  nvfp4_codes(b, sc, st, w0, w1);
+  if constexpr (FS) {
+    const float d4 = 4.0f * st;
+    const float r4 = am / d4;
+    const uint32_t sc4 = e4m3_rne_sat(r4);
+    uint32_t v0, v1;
+    nvfp4_codes(b, sc4, st, v0, v1);
+    if (nvfp4_sq_err(b, v0, v1, sc4, st) < nvfp4_sq_err(b, w0, w1, sc, st)) {
+      sc = sc4;
+      w0 = v0;
+      w1 = v1;
+    }
+  }
   *reinterpret_cast<uint2*>(code_dst) = make_uint2(w0, w1);
   *scale_dst = (uint8_t)sc;
 }
 
 // NVFP4 round-to-nearest quantization of rows [row0, row_end). TPR threads
 // share a row; each owns up to MAXB blocks of 16 (block j = lane + k*TPR).
-template <typename T, int TPR, int MAXB, int MODE>
+template <typename T, int TPR, int MAXB, int MODE, bool FS>
 __global__ __launch_bounds__(kThreads) void k_quant_nvfp4(
     const T* __restrict__ x, int64_t row0, int64_t row_end, int64_t rows_per_item, int64_t C,
     const float* __restrict__ outer_in, const uint32_t* __restrict__ amax_bits,
@@ -211,7 +261,7 @@ __global__ __launch_bounds__(kThreads) void k_quant_nvfp4(
 #pragma unroll
   for (int k = 0; k < MAXB; ++k) {
     const int64_t j = tl + (int64_t)k * TPR;
-    if (row_ok && j < nb) nvfp4_block(blk[k], am[k], st, codes + row * (C >> 1) + j * 8, scales + row * nb + j);
+    if (row_ok && j < nb) nvfp4_block<FS>(blk[k], am[k], st, codes + row * (C >> 1) + j * 8, scales + row * nb + j);
   }
 }
 
@@ -307,7 +357,7 @@ __global__ __launch_bounds__(kOnePassThreads) void k_quant_nvfp4_items(
 #pragma unroll
     for (int k = 0; k < BPT; ++k) {
       const int64_t j = lo + t + (int64_t)k * kOnePassThreads;
-      if (j < hi) nvfp4_block(blk[b][k], am[b][k], st, codes + (e * bpi + j) * 8, scales + e * bpi + j);
+      if (j < hi) nvfp4_block<false>(blk[b][k], am[b][k], st, codes + (e * bpi + j) * 8, scales + e * bpi + j);
     }
   };
   if (B <= 0) return;
@@ -367,14 +417,14 @@ __global__ __launch_bounds__(kThreads) void k_mxfp8_rows(const T* __restrict__ x
 
 inline unsigned grid1(int64_t n, int t = kThreads) { return (unsigned)((n + t - 1) / t); }
 
-template <typename T, int MODE>
+template <typename T, int MODE, bool FS>
 int launch_quant(const T* x, int64_t row0, int64_t row_end, int64_t R, int64_t C, const float* outer_in,
                  const uint32_t* amax, uint8_t* codes, uint8_t* scales, float* outer_out, hipStream_t s) {
   const int64_t nb = C / 16;
   const int64_t n = row_end - row0;
   if (n <= 0) return BSQ_OK;
 #define BSQ_QL(TPR, MAXB)                                                                          \
-  hipLaunchKernelGGL((k_quant_nvfp4<T, TPR, MAXB, MODE>), dim3(grid1(n, kThreads / TPR)), dim3(kThreads), 0, s, \
+  hipLaunchKernelGGL((k_quant_nvfp4<T, TPR, MAXB, MODE, FS>), dim3(grid1(n, kThreads / TPR)), dim3(kThreads), 0, s, \
                      x, row0, row_end, R, C, outer_in, amax, codes, scales, outer_out)
   // one wave per row up to 512 blocks (the row maximum is a wave reduction),
   // up to 8 blocks (256 bytes of bf16) in flight per thread
@@ -390,17 +440,21 @@ int launch_quant(const T* x, int64_t row0, int64_t row_end, int64_t R, int64_t C
 }
 
 template <typename T>
-int quantize_nvfp4_t(const T* x, int64_t B, int64_t R, int64_t C, int mode, const float* outer_in,
+int quantize_nvfp4_t(const T* x, int64_t B, int64_t R, int64_t C, int mode, bool fs, const float* outer_in,
                      uint8_t* codes, uint8_t* scales, float* outer_out, uint32_t* ws, hipStream_t s) {
   const int64_t rows = B * R;
-  if (mode == BSQ_OUTER_ROW) return launch_quant<T, BSQ_OUTER_ROW>(x, 0, rows, R, C, nullptr, nullptr, codes, scales, outer_out, s);
-  if (mode == BSQ_OUTER_GIVEN) return launch_quant<T, BSQ_OUTER_GIVEN>(x, 0, rows, R, C, outer_in, nullptr, codes, scales, outer_out, s);
+  if (mode == BSQ_OUTER_ROW)
+    return fs ? launch_quant<T, BSQ_OUTER_ROW, true>(x, 0, rows, R, C, nullptr, nullptr, codes, scales, outer_out, s)
+              : launch_quant<T, BSQ_OUTER_ROW, false>(x, 0, rows, R, C, nullptr, nullptr, codes, scales, outer_out, s);
+  if (mode == BSQ_OUTER_GIVEN)
+    return fs ? launch_quant<T, BSQ_OUTER_GIVEN, true>(x, 0, rows, R, C, outer_in, nullptr, codes, scales, outer_out, s)
+              : launch_quant<T, BSQ_OUTER_GIVEN, false>(x, 0, rows, R, C, outer_in, nullptr, codes, scales, outer_out, s);
   // one pass when the items are large (a grid-wide wait per item) and a
   // workgroup's share fits in registers
   const int64_t bpi = R * C / 16;
   const int64_t nwg = bsqh::device_cus() < kOnePassMaxWg ? bsqh::device_cus() : kOnePassMaxWg;
   const int64_t per_thread = ((bpi + nwg - 1) / nwg + kOnePassThreads - 1) / kOnePassThreads;
-  if (one_pass_items(B, R, C) && per_thread <= 8) {
+  if (!fs && one_pass_items(B, R, C) && per_thread <= 8) {
     hipLaunchKernelGGL(k_fill_u32, dim3(grid1(B * nwg)), dim3(kThreads), 0, s, ws, 0u, B * nwg);
 #define BSQ_OP(BPT)                                                                                              \
   hipLaunchKernelGGL((k_quant_nvfp4_items<T, BPT>), dim3((unsigned)nwg), dim3(kOnePassThreads), 0, s, x, B, bpi, ws, \
@@ -421,14 +475,14 @@ int quantize_nvfp4_t(const T* x, int64_t B, int64_t R, int64_t C, int mode, cons
     hipLaunchKernelGGL(k_amax_items<T>, dim3((unsigned)gx, (unsigned)ni), dim3(kThreads), 0, s, x, vec, per_wg, ws,
                        i0);
   }
-  return launch_quant<T, BSQ_OUTER_TENSOR>(x, 0, rows, R, C, nullptr, ws, codes, scales, outer_out, s);
+  return fs ? launch_quant<T, BSQ_OUTER_TENSOR, true>(x, 0, rows, R, C, nullptr, ws, codes, scales, outer_out, s)
+            : launch_quant<T, BSQ_OUTER_TENSOR, false>(x, 0, rows, R, C, nullptr, ws, codes, scales, outer_out, s);
 }
 
 }  // namespace
 
 extern "C" size_t bsq_quantize_nvfp4_workspace(int64_t batch, int64_t rows, int64_t cols, int mode) {
-  (void)rows;
-  (void)cols;
+  mode &= ~BSQ_NVFP4_FOUR_OVER_SIX;
   if (mode != BSQ_OUTER_TENSOR || batch <= 0) return 0;
   // per item: the maximum's bits, or one arrival slot per workgroup of the one-pass kernel
   const int64_t words = one_pass_items(batch, rows, cols) ? batch * kOnePassMaxWg : batch;
@@ -439,6 +493,9 @@ extern "C" int bsq_quantize_nvfp4(const void* x, int dtype, int64_t batch, int64
                                   const float* outer_in, uint8_t* codes, uint8_t* scales, float* outer_out,
                                   void* ws, size_t ws_bytes, bsq_stream_t stream) {
   BSQ_REQUIRE(dtype == BSQ_F32 || dtype == BSQ_BF16, BSQ_E_DTYPE);
+  const bool fs = (mode & BSQ_NVFP4_FOUR_OVER_SIX) != 0;
+  const int flags_in = mode;
+  mode &= ~BSQ_NVFP4_FOUR_OVER_SIX;
   BSQ_REQUIRE(mode == BSQ_OUTER_TENSOR || mode == BSQ_OUTER_ROW || mode == BSQ_OUTER_GIVEN, BSQ_E_ENUM);
   BSQ_REQUIRE(batch >= 0 && rows >= 0 && cols >= 0 && cols % 16 == 0 && cols <= 32768, BSQ_E_SHAPE);
   if (batch == 0) return BSQ_OK;
@@ -447,7 +504,7 @@ extern "C" int bsq_quantize_nvfp4(const void* x, int dtype, int64_t batch, int64
   BSQ_REQUIRE(empty || (x && codes && scales), BSQ_E_NULL);
   BSQ_REQUIRE(bsqh::aligned16(x) && bsqh::aligned16(codes), BSQ_E_ALIGN);
   BSQ_REQUIRE(((uintptr_t)outer_out & 3) == 0 && ((uintptr_t)outer_in & 3) == 0, BSQ_E_ALIGN);
-  const size_t need = empty ? 0 : bsq_quantize_nvfp4_workspace(batch, rows, cols, mode);
+  const size_t need = empty ? 0 : bsq_quantize_nvfp4_workspace(batch, rows, cols, flags_in);
   if (need) {
     BSQ_REQUIRE(ws, BSQ_E_NULL);
     BSQ_REQUIRE(((uintptr_t)ws & 3) == 0, BSQ_E_ALIGN);
@@ -465,9 +522,9 @@ extern "C" int bsq_quantize_nvfp4(const void* x, int dtype, int64_t batch, int64
     return bsqh::launch_status();
   }
   if (dtype == BSQ_BF16)
-    return quantize_nvfp4_t<uint16_t>(static_cast<const uint16_t*>(x), batch, rows, cols, mode, outer_in, codes,
+    return quantize_nvfp4_t<uint16_t>(static_cast<const uint16_t*>(x), batch, rows, cols, mode, fs, outer_in, codes,
                                       scales, outer_out, static_cast<uint32_t*>(ws), s);
-  return quantize_nvfp4_t<float>(static_cast<const float*>(x), batch, rows, cols, mode, outer_in, codes, scales,
+  return quantize_nvfp4_t<float>(static_cast<const float*>(x), batch, rows, cols, mode, fs, outer_in, codes, scales,
                                  outer_out, static_cast<uint32_t*>(ws), s);
 }
 

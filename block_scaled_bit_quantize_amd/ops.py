@@ -6,6 +6,7 @@ from ._lib import BsqError, check, load_library
 
 F32, BF16 = 0, 1
 OUTER_TENSOR, OUTER_ROW, OUTER_GIVEN = 0, 1, 2
+FOUR_OVER_SIX = 16  # flag OR-ed into the NVFP4 quantize mode
 RN, SR = 0, 1
 NVFP4, MXFP8 = 0, 1
 
@@ -36,8 +37,9 @@ def _ws(nbytes, device):
     return torch.empty(max(int(nbytes), 1), dtype=torch.uint8, device=device)
 
 
-def quantize_nvfp4(x, mode="tensor", outer_in=None):
-    """Round-to-nearest NVFP4 of x [B, R, C] or [R, C] (float32 or bfloat16).
+def quantize_nvfp4(x, mode="tensor", outer_in=None, four_over_six=False):
+    """Round-to-nearest NVFP4 of x [B, R, C] or [R, C] (float32 or bfloat16);
+    four_over_six picks each block's scale from the 6- and 4-mapping candidates.
     Returns (codes u8 [..., C/2], scales u8 [..., C/16], outer f32 [B] or [B*R])."""
     lib = load_library()
     _dev(x, outer_in)
@@ -48,12 +50,13 @@ def quantize_nvfp4(x, mode="tensor", outer_in=None):
     if dt is None:
         raise BsqError("x must be float32 or bfloat16")
     m = _enum(mode, _OUTER)
+    flags = m | (FOUR_OVER_SIX if four_over_six else 0)
     codes = torch.empty((B, R, C // 2), dtype=torch.uint8, device=x.device)
     scales = torch.empty((B, R, C // 16), dtype=torch.uint8, device=x.device)
     outer = torch.empty((B * R,) if m == OUTER_ROW else (B,), dtype=torch.float32, device=x.device)
-    wsb = lib.bsq_quantize_nvfp4_workspace(B, R, C, m)
+    wsb = lib.bsq_quantize_nvfp4_workspace(B, R, C, flags)
     ws = _ws(wsb, x.device) if wsb else None
-    check(lib.bsq_quantize_nvfp4(x3.data_ptr(), dt, B, R, C, m, _ptr(outer_in), codes.data_ptr(),
+    check(lib.bsq_quantize_nvfp4(x3.data_ptr(), dt, B, R, C, flags, _ptr(outer_in), codes.data_ptr(),
                                  scales.data_ptr(), outer.data_ptr(), _ptr(ws), wsb, _stream()),
           "bsq_quantize_nvfp4")
     if squeeze:

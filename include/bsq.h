@@ -57,6 +57,8 @@ typedef enum {
   BSQ_OUTER_ROW = 1,    /* one per row (a token) */
   BSQ_OUTER_GIVEN = 2   /* one per batch item, read from outer_in */
 } bsq_outer_mode;
+/* Flag OR'ed into bsq_quantize_nvfp4's mode: Four Over Six block scales. */
+enum { BSQ_NVFP4_FOUR_OVER_SIX = 16 };
 
 typedef enum { BSQ_RN = 0, BSQ_SR = 1 } bsq_round;
 typedef enum { BSQ_NVFP4 = 0, BSQ_MXFP8 = 1 } bsq_format;
@@ -73,7 +75,8 @@ int bsq_version(void);
  * 9; x_i = q_i * s_{i//16} * s_t).
  *
  * x        [batch, rows, cols] of `dtype` (F32 or BF16), cols % 16 == 0.
- * mode     outer-scale granularity (bsq_outer_mode).
+ * mode     outer-scale granularity (bsq_outer_mode), optionally OR'ed with
+ *          BSQ_NVFP4_FOUR_OVER_SIX.
  * outer_in [batch] FP32, required only for BSQ_OUTER_GIVEN (positive, normal).
  * codes    [batch, rows, cols/2] u8 (two E2M1 codes per byte).
  * scales   [batch, rows, cols/16] u8 (E4M3). 1-byte alignment suffices.
@@ -85,6 +88,13 @@ int bsq_version(void);
  * at 448; D = f32(s_b s_t); a block with D below 2^-126 stores magnitude 0;
  * else each element rounds f32(x * f32(1/D)) to the nearest E2M1 value (ties
  * to even, saturating at 6, sign kept).
+ * Four Over Six ("Recipe details": for activations, each block chooses
+ * between two scale factors to reduce quantization error; the quantized
+ * linear layer figure applies it to the per-token activation quantize): the
+ * block also forms s_b4 from r4 = f32(a_b / f32(4 s_t)) with its codes, and
+ * keeps it when its squared error is strictly smaller; the error is
+ * sum_i f32(e_i^2), e_i = f32(x_i - f32(f32(q_i s_b) s_t)), summed in float32
+ * in element order (ties keep the 6 scale).
  * Limits: cols <= 32768. x and codes 16-byte aligned; outer_in, outer_out
  * and ws 4-byte aligned; scales 1-byte.
  * Errors: NULL, SHAPE, ALIGN, DTYPE, ENUM, WORKSPACE, LAUNCH.

@@ -67,7 +67,25 @@ def _nvfp4_block_codes(blocks, d_scale_codes, st_blk):
     return np.where(live[..., None], codes, sign_only).astype(np.uint8)
 
 
-def quantize_nvfp4(x, mode, outer_in=None):
+def _block_sq_error(blocks, codes, s_code, st_blk):
+    """Squared quantization error of each 1x16 block, the measure Four Over
+    Six compares (reading: the pages name the technique, not its error
+    measure). In float32, in a fixed order: x^_i = f32(f32(q_i * s_b) * s_t)
+    (the dequantized value), e_i = f32(x_i - x^_i), and
+    err = f32(...f32(f32(e_0^2 + e_1^2) + e_2^2)... + e_15^2), each square and
+    each partial sum rounded to float32 in element order."""
+    q = e2m1_decode(codes).astype(F32)
+    s = _f32(e4m3_decode(s_code))[..., None]
+    xh = ((q * s).astype(F32) * st_blk[..., None]).astype(F32)
+    e = (blocks - xh).astype(F32)
+    sq = (e * e).astype(F32)
+    err = sq[..., 0]
+    for i in range(1, NVFP4_BLOCK):
+        err = (err + sq[..., i]).astype(F32)
+    return err
+
+
+def quantize_nvfp4(x, mode, outer_in=None, four_over_six=False):
     """Round-to-nearest NVFP4 quantization of x (float32, shape [B, R, C],
     C % 16 == 0); blocks of 16 run along C.
 
@@ -83,6 +101,12 @@ def quantize_nvfp4(x, mode, outer_in=None):
             (reading pinned by the 593.7 example: 98.95 -> 96, error -17.7)
       codes: see _nvfp4_block_codes; two codes per byte, element 2k in the
       low nibble (reading).
+    four_over_six (section "Recipe details": the activation quantizer chooses
+    between two scale factors per block to reduce quantization error;
+    Figure 4 applies it to the per-token activation quantize): each block
+    also tries r4 = f32(a_b / f32(4 * s_t)), the scale that maps a_b to 4, and
+    keeps it when its squared error (_block_sq_error) is strictly smaller
+    than that of the 6 scale (reading: ties keep 6).
     Returns (packed [B,R,C/2] u8, scales [B,R,C/16] u8, outer f32 [B] or [B,R]).
     """
     x = _f32(x)
@@ -106,6 +130,16 @@ def quantize_nvfp4(x, mode, outer_in=None):
         r = (a_b / d).astype(F32)
     s_code = e4m3_encode_rne_sat(r)
     codes = _nvfp4_block_codes(blocks, s_code, st_b)
+    if four_over_six:
+        d4 = (F32(4.0) * st_b).astype(F32)
+        with np.errstate(divide="ignore", invalid="ignore"):
+            r4 = (a_b / d4).astype(F32)
+        s4 = e4m3_encode_rne_sat(r4)
+        codes4 = _nvfp4_block_codes(blocks, s4, st_b)
+        st_full = np.broadcast_to(st_b, a_b.shape)
+        use4 = _block_sq_error(blocks, codes4, s4, st_full) < _block_sq_error(blocks, codes, s_code, st_full)
+        s_code = np.where(use4, s4, s_code).astype(np.uint8)
+        codes = np.where(use4[..., None], codes4, codes).astype(np.uint8)
     return pack_fp4(codes.reshape(B, R, C)), s_code, st
 
 

@@ -108,6 +108,28 @@ def test_quantize_nvfp4_tensor_one_pass_wait_fallback():
     assert np.array_equal(h(gc), oc)
 
 
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+@pytest.mark.parametrize("mode", ["tensor", "row", "given"])
+@pytest.mark.parametrize("shape,kind", [((2, 5, 256), "wide"), ((3, 7, 1040), "zeros_mix"), ((1, 33, 64), "normal")])
+def test_quantize_nvfp4_four_over_six_small(dtype, mode, shape, kind):
+    log(f"quantize_nvfp4 4/6 {dtype} {mode} {shape} {kind}")
+    rng = np.random.default_rng(hash(("46", dtype, mode, shape, kind)) % 2**32)
+    x = _data(rng, shape, kind)
+    if dtype == "bf16":
+        bits = synth.bf16_bits(x)
+        x = synth.bf16_to_f32(bits).reshape(shape)
+        xd = bf16_t(bits.reshape(shape))
+    else:
+        xd = t(x)
+    outer = (np.abs(rng.standard_normal(shape[0])) * 0.01 + 1e-3).astype(f32) if mode == "given" else None
+    m = {"tensor": Q.OUTER_TENSOR, "row": Q.OUTER_ROW, "given": Q.OUTER_GIVEN}[mode]
+    gc, gs, go = bsq.quantize_nvfp4(xd, mode, t(outer) if outer is not None else None, four_over_six=True)
+    oc, os_, oo = Q.quantize_nvfp4(x, m, outer, four_over_six=True)
+    assert np.array_equal(h(gs), os_)
+    assert np.array_equal(h(gc), oc)
+    assert np.array_equal(h(go), np.asarray(oo).reshape(-1))
+
+
 def test_quantize_nvfp4_edge_cases():
     # empty tensors, all zeros, largest bf16 values, single block
     log("quantize_nvfp4 edges")
@@ -286,6 +308,20 @@ def test_quantize_nvfp4_workload2_full(wl2):
         rows = np.r_[0, 5, 1535]
         oc, os_, _ = Q.quantize_nvfp4(we[rows][None], Q.OUTER_GIVEN, np.array([st], f32))
         assert np.array_equal(h(gc[e][rows]), oc[0]) and np.array_equal(h(gs[e][rows]), os_[0])
+
+
+def test_quantize_nvfp4_four_over_six_workload2_full(wl2):
+    """The activation quantizer of the quantized linear layer figure: per
+    token, Four Over Six, at full size; sampled rows against the oracle."""
+    log("quantize workload2 activations, four over six")
+    x = wl2["x"]
+    gc, gs, go = bsq.quantize_nvfp4(bf16_t(x), "row", four_over_six=True)
+    rows = np.r_[0, 3, 4097, 12000, 16383]
+    xf = synth.bf16_to_f32(x[rows])
+    oc, os_, oo = Q.quantize_nvfp4(xf[None], Q.OUTER_ROW, four_over_six=True)
+    assert np.array_equal(h(gs[rows]), os_[0])
+    assert np.array_equal(h(gc[rows]), oc[0])
+    assert np.array_equal(h(go)[rows], oo[0])
 
 
 def test_requant_workload3_full(wl2):

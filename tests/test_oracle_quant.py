@@ -325,3 +325,71 @@ def test_segmented_transposed_layout_and_padding():
     idx = (np.uint64(base[2]) + np.arange(64 * 64, dtype=np.uint64)).reshape(64, 64)
     c2, s2 = Q.mxfp8_quantize(Z, idx, Q.SR, 4, 2)
     assert np.array_equal(blk, c2)
+
+
+# ---------------------------------------------------------------- Four Over Six
+def _given(x):
+    return Q.quantize_nvfp4(np.asarray(x, np.float32).reshape(1, 1, -1), Q.OUTER_GIVEN,
+                            np.ones(1, np.float32), four_over_six=True)
+
+
+def test_four_over_six_worked_blocks():
+    """A block of 5.0 (outer scale 1): the 6 scale 5/6 rounds to E4M3 0.8125,
+    so 5 -> 6.15 -> 6 -> 4.875; the 4 scale 5/4 = 1.25 is exact and gives 5
+    exactly, so 4/6 keeps it. A block [6, 1, ..., 1]: the 6 scale (1.0) is
+    exact; the 4 scale 1.5 sends 1 to 1/1.5 -> 0.5 -> 0.75, so 6 is kept."""
+    plain = Q.quantize_nvfp4(np.full((1, 1, 16), 5.0, np.float32), Q.OUTER_GIVEN, np.ones(1, np.float32))
+    assert int(plain[1][0, 0, 0]) == 0x35  # 0.8125
+    assert np.all(Q.dequantize_nvfp4(*plain, Q.OUTER_GIVEN) == np.float32(4.875))
+    fs = _given(np.full(16, 5.0))
+    assert int(fs[1][0, 0, 0]) == 0x3A     # 1.25
+    assert np.all(Q.dequantize_nvfp4(*fs, Q.OUTER_GIVEN) == np.float32(5.0))
+    blk = np.ones(16, np.float32)
+    blk[0] = 6.0
+    fs = _given(blk)
+    assert int(fs[1][0, 0, 0]) == 0x38     # 1.0: the 6 scale
+    assert np.array_equal(Q.dequantize_nvfp4(*fs, Q.OUTER_GIVEN).reshape(-1), blk)
+
+
+def _f64_block_errors(x, packed, scales, outer):
+    xh = Q.dequantize_nvfp4_f64(packed, scales, outer, Q.OUTER_GIVEN)
+    d = x.astype(np.float64) - xh
+    return (d * d).reshape(x.shape[0], x.shape[1], -1, 16).sum(-1)
+
+
+@pytest.mark.parametrize("seed", [0, 1, 2])
+def test_four_over_six_choice_matches_exact_errors(seed):
+    """Independent of the float32 error sum: compute both candidates' block
+    errors in float64 from their dequantized values; wherever they differ by
+    more than float32 rounding could explain, 4/6 must have taken the smaller."""
+    rng = np.random.default_rng(seed)
+    x = (rng.standard_normal((1, 64, 512)) * np.exp(rng.standard_normal((1, 64, 1)))).astype(np.float32)
+    outer = np.ones(1, np.float32)
+    six = Q.quantize_nvfp4(x, Q.OUTER_GIVEN, outer)
+    fs = Q.quantize_nvfp4(x, Q.OUTER_GIVEN, outer, four_over_six=True)
+    # the 4 candidate alone: scales from r4, codes as RTN
+    a_b = np.abs(x.reshape(1, 64, 32, 16)).max(-1)
+    s4 = F.e4m3_encode_rne_sat((a_b / np.float32(4.0)).astype(np.float32))
+    e6 = _f64_block_errors(x, *six[:2], outer)
+    took4 = fs[1] != six[1]
+    assert np.all(fs[1][took4] == s4[took4])
+    # float64 errors of what 4/6 produced vs of the plain 6 choice
+    efs = _f64_block_errors(x, *fs[:2], outer)
+    clear = np.abs(efs - e6) > 1e-5 * np.maximum(e6, 1e-30)
+    assert np.all(efs[clear & took4] < e6[clear & took4])
+    assert took4.mean() > 0.1 and (~took4).mean() > 0.1
+
+
+def test_four_over_six_never_worse_and_off_by_default():
+    rng = np.random.default_rng(5)
+    x = rng.standard_t(3, (2, 32, 256)).astype(np.float32)
+    for mode in (Q.OUTER_TENSOR, Q.OUTER_ROW):
+        plain = Q.quantize_nvfp4(x, mode)
+        fs = Q.quantize_nvfp4(x, mode, four_over_six=True)
+        assert np.array_equal(plain[2], fs[2])            # outer scales unchanged
+        d_plain = x.astype(np.float64) - Q.dequantize_nvfp4_f64(*plain, mode)
+        d_fs = x.astype(np.float64) - Q.dequantize_nvfp4_f64(*fs, mode)
+        e_plain = (d_plain ** 2).reshape(2, 32, 16, 16).sum(-1)
+        e_fs = (d_fs ** 2).reshape(2, 32, 16, 16).sum(-1)
+        assert np.all(e_fs <= e_plain * (1 + 1e-5) + 1e-30)
+        assert e_fs.sum() < 0.95 * e_plain.sum()
