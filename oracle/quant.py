@@ -143,22 +143,49 @@ def quantize_nvfp4(x, mode, outer_in=None, four_over_six=False):
     return pack_fp4(codes.reshape(B, R, C)), s_code, st
 
 
-def quantize_nvfp4_tile16(x, outer):
-    """The square-tile variant the pages compare against (section "Block-scaled
-    backward passes", outlier figure): one scale per 16x16 tile, from the
-    tile's largest magnitude, shared by the 16 row blocks of the tile.
-    x float32 [R, C], R and C multiples of 16, one given outer scale.
-    Returns unpacked codes [R, C] and tile scale codes [R/16, C/16]."""
+def quantize_nvfp4_square(x, mode, outer_in=None):
+    """The square-tile NVFP4 variant the pages compare against (section
+    "Block-scaled backward passes", the row-vs-column and outlier figures):
+    one E4M3 scale per 16x16 tile instead of per 1x16 block, so that the
+    quantization of the transpose is the transpose of the quantization.
+
+    x float32 [B, R, C], R % 16 == 0 and C % 16 == 0. mode OUTER_TENSOR (one
+    outer scale per item from its amax, as in quantize_nvfp4) or OUTER_GIVEN
+    (``outer_in`` [B]). Per 16x16 tile:
+      a_t = max |x| over the tile
+      s_b = E4M3 round-to-nearest-even of f32(a_t / f32(6 * s_t)), saturating
+      every element then rounds exactly as in a 1x16 block with scale s_b
+      (_nvfp4_block_codes).
+    Returns (packed [B,R,C/2] u8, scales [B,R,C/16] u8, outer f32 [B]); the
+    scales use the layout of the 1x16 quantizer (one byte per row block), each
+    tile's byte repeated in its 16 rows, so any consumer of 1x16 blocks reads
+    the result unchanged (reading: the pages do not fix a storage layout)."""
     x = _f32(x)
-    R, C = x.shape
-    st = F32(outer)
-    tiles = x.reshape(R // 16, 16, C // 16, 16)
-    a_t = np.max(np.abs(tiles), axis=(1, 3))
-    r = (a_t / (F32(6.0) * st).astype(F32)).astype(F32)
-    s_code = e4m3_encode_rne_sat(r)
-    per_block = np.repeat(s_code, 16, axis=0)                    # [R, C/16]
-    codes = _nvfp4_block_codes(x.reshape(R, C // 16, 16), per_block, st)
-    return codes.reshape(R, C), s_code
+    B, R, C = x.shape
+    assert R % 16 == 0 and C % 16 == 0
+    if mode == OUTER_TENSOR:
+        st = outer_scale_from_amax(np.max(np.abs(x), axis=(1, 2)) if R * C else np.zeros(B, F32))
+    elif mode == OUTER_GIVEN:
+        st = _f32(outer_in).reshape(B)
+    else:
+        raise ValueError("mode")
+    st_b = st[:, None, None]
+    tiles = x.reshape(B, R // 16, 16, C // 16, 16)
+    a_t = np.max(np.abs(tiles), axis=(2, 4))                      # [B, R/16, C/16]
+    d = (F32(6.0) * st_b).astype(F32)
+    with np.errstate(divide="ignore", invalid="ignore"):
+        r = (a_t / d).astype(F32)
+    s_tile = e4m3_encode_rne_sat(r)
+    s_code = np.repeat(s_tile, 16, axis=1)                         # [B, R, C/16]
+    codes = _nvfp4_block_codes(x.reshape(B, R, C // 16, 16), s_code, st_b)
+    return pack_fp4(codes.reshape(B, R, C)), s_code.astype(np.uint8), st
+
+
+def quantize_nvfp4_tile16(x, outer):
+    """One item of quantize_nvfp4_square with a given outer scale: x float32
+    [R, C]; returns unpacked codes [R, C] and the tile scales [R/16, C/16]."""
+    packed, s_code, _ = quantize_nvfp4_square(_f32(x)[None], OUTER_GIVEN, np.array([outer], F32))
+    return unpack_fp4(packed)[0], s_code[0, ::16, :]
 
 
 def _outer_broadcast(outer, mode, B, R):

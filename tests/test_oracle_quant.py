@@ -393,3 +393,83 @@ def test_four_over_six_never_worse_and_off_by_default():
         e_fs = (d_fs ** 2).reshape(2, 32, 16, 16).sum(-1)
         assert np.all(e_fs <= e_plain * (1 + 1e-5) + 1e-30)
         assert e_fs.sum() < 0.95 * e_plain.sum()
+
+
+def _square_inputs(dist, shape, seed):
+    rng = np.random.default_rng(seed)
+    if dist == "normal":
+        x = rng.standard_normal(shape)
+    elif dist == "outlier":
+        x = rng.uniform(1, 2, shape)
+        x[..., rng.integers(0, shape[-2]), rng.integers(0, shape[-1])] = 1000.0
+    elif dist == "zeros":
+        x = rng.standard_normal(shape)
+        x[..., :16, :16] = 0.0
+        x[..., 16:32, 16:32] = -0.0
+    else:
+        x = rng.standard_normal(shape) * np.exp(rng.uniform(-20, 20, shape))
+    return x.astype(f32)
+
+
+@pytest.mark.parametrize("dist,seed", [("normal", 0), ("outlier", 1), ("zeros", 2), ("wide", 3)])
+def test_square_tile_brute_force(dist, seed):
+    """Every 16x16 tile against a float64 nearest-value search: the tile scale is
+    the E4M3 value nearest to (tile max)/(6 s_t), each element the E2M1 value
+    nearest to x/(s_b s_t); near-ties are skipped."""
+    x = _square_inputs(dist, (2, 48, 64), seed)
+    for mode, outer in ((Q.OUTER_TENSOR, None), (Q.OUTER_GIVEN, np.array([0.37, 2.5], f32))):
+        p, s, st = Q.quantize_nvfp4_square(x, mode, outer)
+        codes = F.unpack_fp4(p)
+        for b in range(2):
+            stb = float(st[b])
+            if mode == Q.OUTER_TENSOR:
+                amax = float(np.abs(x[b]).max())
+                assert stb == (f32(amax) / f32(2688.0) if amax > 0 else 1.0)
+            for ti in range(3):
+                for tj in range(4):
+                    blk = x[b, ti * 16:(ti + 1) * 16, tj * 16:(tj + 1) * 16].astype(np.float64)
+                    ratio = np.abs(blk).max() / (6 * stb)
+                    got = s[b, ti * 16:(ti + 1) * 16, tj]
+                    assert (got == got[0]).all()                  # one scale for the 16 rows
+                    want = int(np.argmin(np.abs(F.E4M3_VAL - ratio)))
+                    if not _near_tie(np.array([ratio]), F.E4M3_VAL)[0]:
+                        assert got[0] == want, (b, ti, tj)
+                    D = F.e4m3_decode(got[0]) * stb
+                    yv = blk / D if D >= 2.0 ** -126 else np.zeros_like(blk)
+                    want_c = np.argmin(np.abs(F.E2M1_MAG[None, :] - np.abs(yv).reshape(-1)[:, None]), axis=1)
+                    got_c = codes[b, ti * 16:(ti + 1) * 16, tj * 16:(tj + 1) * 16]
+                    nt = _near_tie(np.abs(yv).reshape(-1), F.E2M1_MAG).reshape(16, 16)
+                    assert not (((got_c & 7) != want_c.reshape(16, 16)) & ~nt).any(), (b, ti, tj)
+                    assert np.array_equal(got_c >> 3, np.signbit(blk.astype(f32)).astype(np.uint8))
+
+
+@pytest.mark.parametrize("dist,seed", [("normal", 4), ("outlier", 5), ("wide", 6)])
+def test_square_tile_transpose_is_bitwise(dist, seed):
+    """The property the pages give the square tile: quantizing the transpose
+    yields the transpose of the codes and of the tile scales, bit for bit."""
+    x = _square_inputs(dist, (3, 32, 80), seed)
+    p, s, st = Q.quantize_nvfp4_square(x, Q.OUTER_TENSOR)
+    pt, s_t, st_t = Q.quantize_nvfp4_square(np.ascontiguousarray(x.transpose(0, 2, 1)), Q.OUTER_TENSOR)
+    assert np.array_equal(st, st_t)
+    assert np.array_equal(F.unpack_fp4(pt), F.unpack_fp4(p).transpose(0, 2, 1))
+    assert np.array_equal(s_t[:, ::16, :], s[:, ::16, :].transpose(0, 2, 1))
+
+
+def test_square_tile_equals_row_blocks_when_row_maxima_agree():
+    """When every 1x16 block of a tile has the tile's largest magnitude, the
+    square variant reduces to the pinned 1x16 quantizer bit for bit; otherwise
+    its scale is never below the row block's (E4M3 codes order like values)."""
+    rng = np.random.default_rng(7)
+    x = rng.uniform(-1, 1, (2, 32, 48)).astype(f32)
+    tiles = x.reshape(2, 2, 16, 3, 16)
+    m = rng.uniform(0.5, 40, (2, 2, 1, 3, 1)).astype(f32)
+    tiles *= m
+    tiles[..., 5] = np.where(rng.integers(0, 2, (2, 2, 16, 3)) == 1, m[..., 0], -m[..., 0])
+    outer = np.array([0.25, 1.5], f32)
+    p, s, _ = Q.quantize_nvfp4_square(x, Q.OUTER_GIVEN, outer)
+    p1, s1, _ = Q.quantize_nvfp4(x, Q.OUTER_GIVEN, outer)
+    assert np.array_equal(p, p1) and np.array_equal(s, s1)
+    y = rng.standard_t(3, (2, 32, 48)).astype(f32)
+    _, s, _ = Q.quantize_nvfp4_square(y, Q.OUTER_TENSOR)
+    _, s1, _ = Q.quantize_nvfp4(y, Q.OUTER_TENSOR)
+    assert (s >= s1).all() and (s > s1).any()
