@@ -84,6 +84,8 @@ def algorithmic(seg_host):
         "requant_x": ("GB/s", nv(T, H) + T * 4 + M * 4 + mx(H * smp)),
         "dgrad": ("TFLOP/s", gemm),
         "wgrad": ("TFLOP/s", gemm),
+        # not a step stage: the square-tile weight quantizer, both layouts from one read
+        "quant_w_square": ("GB/s", E * F * H * 2 + 2 * nv(E * F, H) + E * 4),
     }
 
 
@@ -298,6 +300,28 @@ def main():
     roofline = {"bound": "hbm" if dk["unit"] == "GB/s" else "mfma", "kernel": dom, "achieved": dk["achieved"],
                 "peak": dk["peak"], "unit": dk["unit"], "frac": dk["frac"], "traffic": traffic}
 
+    # Alternatives to a step stage, timed on their own after the step (not in
+    # ms_per_step): the 16x16 square-tile weight quantizer writing W and W^T.
+    alternatives = {}
+    if stages is None:
+        reps = 10
+        for _ in range(2):
+            bsq.quantize_nvfp4_square(inp["w"], "tensor")
+        torch.cuda.synchronize()
+        a0, a1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a0.record()
+        for _ in range(reps):
+            bsq.quantize_nvfp4_square(inp["w"], "tensor")
+        a1.record()
+        torch.cuda.synchronize()
+        ms = a0.elapsed_time(a1) / reps
+        ach = algo["quant_w_square"][1] / (ms * 1e-3) / 1e9
+        alternatives["quant_w_square"] = {
+            "ms": round(ms, 4), "achieved": round(ach, 2), "unit": "GB/s", "peak": HBM_PEAK_GBS,
+            "frac": round(ach / HBM_PEAK_GBS, 4),
+            "traffic": read_traffic("quant_w_square", kernel_sha(*stage_sources("quant_w_square"))),
+            "alternative_to": "quant_w + requant_w where the backward reads W^T in NVFP4 (square tiles) instead of SR MXFP8"}
+
     if args.copy_calibration:
         src_buf = torch.empty(512 << 20, dtype=torch.uint8, device=dev).fill_(1)
         dst_buf = torch.empty_like(src_buf)
@@ -320,6 +344,7 @@ def main():
                    "backward_gemm": "native-fp8" if args.native_fp8 else "exact-bf16"},
         "kernels": kernels,
         "roofline": roofline,
+        "alternatives": alternatives,
         "cpu_baseline": cpu,
     }
     print(json.dumps(line))

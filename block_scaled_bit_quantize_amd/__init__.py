@@ -10,7 +10,8 @@ GPU, but calling an operation without the built library or a GPU raises.
 from ._lib import BsqError, library_path, load_library
 from .ops import (BF16, F32, MXFP8, NVFP4, OUTER_GIVEN, OUTER_ROW, OUTER_TENSOR, RN, SR,
                   dequantize_mxfp8, dequantize_nvfp4, grouped_gemm_mxfp8, grouped_gemm_nvfp4,
-                  padded_segment_layout, quantize_mxfp8, quantize_nvfp4, requant_transpose_sr,
+                  padded_segment_layout, quantize_mxfp8, quantize_nvfp4, quantize_nvfp4_square,
+                  requant_transpose_sr,
                   rng_bits16, route)
 
 __all__ = [
@@ -18,5 +19,5 @@ __all__ = [
     "F32", "BF16", "OUTER_TENSOR", "OUTER_ROW", "OUTER_GIVEN", "RN", "SR", "NVFP4", "MXFP8",
     "quantize_nvfp4", "quantize_mxfp8", "requant_transpose_sr", "grouped_gemm_nvfp4",
     "grouped_gemm_mxfp8", "route", "dequantize_nvfp4", "dequantize_mxfp8", "rng_bits16",
-    "padded_segment_layout",
+    "padded_segment_layout", "quantize_nvfp4_square",
 ]

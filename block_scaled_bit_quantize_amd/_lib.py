@@ -18,6 +18,9 @@ SIGNATURES = {
     "bsq_quantize_nvfp4_workspace": (c_size, [c_i64, c_i64, c_i64, c_int]),
     "bsq_quantize_nvfp4": (c_int, [c_vp, c_int, c_i64, c_i64, c_i64, c_int, c_vp, c_vp, c_vp, c_vp, c_vp,
                                    c_size, c_vp]),
+    "bsq_quantize_nvfp4_square_workspace": (c_size, [c_i64, c_i64, c_i64, c_int]),
+    "bsq_quantize_nvfp4_square": (c_int, [c_vp, c_int, c_i64, c_i64, c_i64, c_int, c_vp, c_vp, c_vp, c_vp, c_vp,
+                                          c_vp, c_vp, c_size, c_vp]),
     "bsq_quantize_mxfp8_workspace": (c_size, [c_i64, c_int, c_i64]),
     "bsq_quantize_mxfp8": (c_int, [c_vp, c_int, c_i64, c_i64, c_int, c_vp, c_i64, c_int, c_u64, c_u64, c_vp, c_vp,
                                    c_vp, c_size, c_vp]),

@@ -265,8 +265,10 @@ __global__ __launch_bounds__(kThreads) void k_quant_nvfp4(
   }
 }
 
-// Per-item outer scale in one pass over HBM. The grid (one workgroup per CU,
-// all resident, at most kOnePassMaxWg) walks the items in order. Every
+// Per-item outer scale in one pass over HBM. Each group of the grid (one
+// workgroup per CU, at most kOnePassMaxWg; with two groups two workgroups
+// share a CU, so one group's loads overlap the other's wait and stores) walks
+// its items (every groups-th item) in order. Every
 // workgroup loads its share of item e into registers (at most BPT blocks of
 // 16 per thread), publishes its maximum in its own slot slot[e][w] (bit
 // pattern with bit 31 set as the arrival mark: magnitudes have it clear),
@@ -281,6 +283,10 @@ __global__ __launch_bounds__(kThreads) void k_quant_nvfp4(
 constexpr int kOnePassThreads = 512;
 constexpr int kOnePassMaxWg = 512;
 constexpr uint32_t kSpinLimit = 1u << 22;  // polls before a workgroup stops waiting (about 0.1 s)
+#ifndef BSQ_ONEPASS_GROUPS
+#define BSQ_ONEPASS_GROUPS 2
+#endif
+constexpr int kOnePassGroups = BSQ_ONEPASS_GROUPS;
 
 // The poll limit; the environment variable BSQ_WAIT_POLLS overrides it (tests
 // set 0 to take every workgroup through the fallback).
@@ -291,11 +297,14 @@ inline uint32_t wait_polls() {
 
 template <typename T, int BPT>
 __global__ __launch_bounds__(kOnePassThreads) void k_quant_nvfp4_items(
-    const T* __restrict__ x, int64_t B, int64_t bpi, uint32_t* __restrict__ slot, uint8_t* __restrict__ codes,
-    uint8_t* __restrict__ scales, float* __restrict__ outer_out, uint32_t spin_limit) {
-  const int nwg = gridDim.x;
+    const T* __restrict__ x, int64_t B, int64_t bpi, int groups, uint32_t* __restrict__ slot,
+    uint8_t* __restrict__ codes, uint8_t* __restrict__ scales, float* __restrict__ outer_out, uint32_t spin_limit) {
+  // `groups` independent grids of nwg workgroups each: group g takes items
+  // g, g + groups, ..., so that one group's loads overlap another's wait
+  const int nwg = gridDim.x / groups;
+  const int grp = blockIdx.x / nwg, wid = blockIdx.x % nwg;
   const int64_t share = (bpi + nwg - 1) / nwg;  // blocks per workgroup and item, <= BPT * threads
-  const int64_t lo = (int64_t)blockIdx.x * share;
+  const int64_t lo = (int64_t)wid * share;
   const int64_t hi = lo + share < bpi ? lo + share : bpi;
   const int t = threadIdx.x;
   __shared__ float red[kOnePassThreads / 64];
@@ -327,7 +336,7 @@ __global__ __launch_bounds__(kOnePassThreads) void k_quant_nvfp4_items(
   };
   auto publish = [&](int64_t e, float m) {
     const float r = wg_max(m);
-    if (t == 0) __hip_atomic_store(slot + e * nwg + blockIdx.x, __float_as_uint(r) | 0x80000000u, __ATOMIC_RELAXED,
+    if (t == 0) __hip_atomic_store(slot + e * nwg + wid, __float_as_uint(r) | 0x80000000u, __ATOMIC_RELAXED,
                                    __HIP_MEMORY_SCOPE_AGENT);
   };
   auto item = [&](int b, int64_t e) {
@@ -353,29 +362,31 @@ __global__ __launch_bounds__(kOnePassThreads) void k_quant_nvfp4_items(
     }
     const float a = wg_max(mx);
     const float st = a > 0.0f ? a / 2688.0f : 1.0f;
-    if (blockIdx.x == 0 && t == 0) outer_out[e] = st;
+    if (wid == 0 && t == 0) outer_out[e] = st;
 #pragma unroll
     for (int k = 0; k < BPT; ++k) {
       const int64_t j = lo + t + (int64_t)k * kOnePassThreads;
       if (j < hi) nvfp4_block<false>(blk[b][k], am[b][k], st, codes + (e * bpi + j) * 8, scales + e * bpi + j);
     }
   };
-  if (B <= 0) return;
-  publish(0, load(0, 0));
-  int64_t e = 0;
-  for (; e + 1 < B; e += 2) {  // register sets alternate: item e in set 0, e + 1 in set 1
-    const float m1 = load(1, e + 1);
-    item(0, e);
-    publish(e + 1, m1);
-    if (e + 2 < B) {
-      const float m2 = load(0, e + 2);
-      item(1, e + 1);
-      publish(e + 2, m2);
+  const int64_t n = grp < B ? (B - grp + groups - 1) / groups : 0;  // this group's items
+  if (n <= 0) return;
+  auto it = [&](int64_t i) -> int64_t { return grp + i * groups; };
+  publish(it(0), load(0, it(0)));
+  int64_t i = 0;
+  for (; i + 1 < n; i += 2) {  // register sets alternate: item i in set 0, i + 1 in set 1
+    const float m1 = load(1, it(i + 1));
+    item(0, it(i));
+    publish(it(i + 1), m1);
+    if (i + 2 < n) {
+      const float m2 = load(0, it(i + 2));
+      item(1, it(i + 1));
+      publish(it(i + 2), m2);
     } else {
-      item(1, e + 1);
+      item(1, it(i + 1));
     }
   }
-  if (e < B && (B & 1)) item(0, e);
+  if (i < n && (n & 1)) item(0, it(i));
 }
 
 // Row-wise MXFP8: one thread per block of 32 (element index = blk*32 + i).
@@ -454,15 +465,20 @@ int quantize_nvfp4_t(const T* x, int64_t B, int64_t R, int64_t C, int mode, bool
   const int64_t bpi = R * C / 16;
   const int64_t nwg = bsqh::device_cus() < kOnePassMaxWg ? bsqh::device_cus() : kOnePassMaxWg;
   const int64_t per_thread = ((bpi + nwg - 1) / nwg + kOnePassThreads - 1) / kOnePassThreads;
-  if (!fs && one_pass_items(B, R, C) && per_thread <= 8) {
+  // (a float share of 8 blocks per thread would not fit in registers)
+  if (!fs && one_pass_items(B, R, C) && per_thread <= (sizeof(T) == 2 ? 8 : 4)) {
     hipLaunchKernelGGL(k_fill_u32, dim3(grid1(B * nwg)), dim3(kThreads), 0, s, ws, 0u, B * nwg);
-#define BSQ_OP(BPT)                                                                                              \
-  hipLaunchKernelGGL((k_quant_nvfp4_items<T, BPT>), dim3((unsigned)nwg), dim3(kOnePassThreads), 0, s, x, B, bpi, ws, \
-                     codes, scales, outer_out, wait_polls())
+    // two groups when two workgroups fit on a CU (at most 128 VGPRs: bf16 BPT <= 4, float BPT <= 2)
+#define BSQ_OP(BPT)                                                                                               \
+  do {                                                                                                            \
+    const int grp = BPT * sizeof(T) <= 8 ? kOnePassGroups : 1;                                                    \
+    hipLaunchKernelGGL((k_quant_nvfp4_items<T, BPT>), dim3((unsigned)(nwg * grp)), dim3(kOnePassThreads), 0, s, x, B, \
+                       bpi, grp, ws, codes, scales, outer_out, wait_polls());                                     \
+  } while (0)
     if (per_thread <= 1) BSQ_OP(1);
     else if (per_thread <= 2) BSQ_OP(2);
     else if (per_thread <= 4) BSQ_OP(4);
-    else BSQ_OP(8);
+    else if constexpr (sizeof(T) == 2) BSQ_OP(8);
 #undef BSQ_OP
     return bsqh::launch_status();
   }
@@ -477,6 +493,288 @@ int quantize_nvfp4_t(const T* x, int64_t B, int64_t R, int64_t C, int mode, bool
   }
   return fs ? launch_quant<T, BSQ_OUTER_TENSOR, true>(x, 0, rows, R, C, nullptr, ws, codes, scales, outer_out, s)
             : launch_quant<T, BSQ_OUTER_TENSOR, false>(x, 0, rows, R, C, nullptr, ws, codes, scales, outer_out, s);
+}
+
+// ------------------------------------------------------------ square tiles
+// The 16x16-tile variant ("Block-scaled backward passes", row-vs-column and
+// outlier figures): one E4M3 scale per 16x16 tile from the tile's largest
+// magnitude, every element then rounding as in a 1x16 block with that scale.
+// Because the tile is square, the quantization of the transpose is the
+// transpose of the codes, so one read of x yields both layouts.
+//
+// A workgroup unit is 128 rows x 64 columns (8 x 4 tiles, 512 threads): wave
+// w owns tile row w, lane (tc = lane / 16, j = lane % 16) owns row j of tile
+// tc (16 elements), and the tile maximum reduces over the 16 lanes of a tile.
+// Row-major codes and scales are stored straight from registers. For the
+// transposed layout the codes go through LDS (128 rows of 32 bytes, 8 bytes of
+// skew per 16 rows so that the reads below hit 8 different banks); thread
+// (c, q) then gathers column c of rows 16q .. 16q + 15 (one byte per row) and
+// writes them as one 8-byte run, so a wave's store covers 8 columns x 64
+// contiguous bytes.
+constexpr int kSqThreads = 512;
+constexpr int kSqRows = 128, kSqCols = 64;
+constexpr int kSqLdsBytes = kSqRows * 32 + 8 * (kSqRows / 16);
+
+__device__ __forceinline__ int sq_lds(int r, int byte) { return r * 32 + 8 * (r >> 4) + byte; }
+
+struct SqGeom {
+  int64_t R, C, nrt, nct;  // units: nrt = ceil(R / 128) down, nct = ceil(C / 64) across
+};
+
+// First row and column of unit u of an item. RF: units ordered down the rows
+// first (the one-shot kernel: the XCD-local neighbours continue each other's
+// transposed runs); else across the columns first (the one-pass kernel: a
+// workgroup's units and its XCD neighbours read long runs of each row).
+template <bool RF>
+__device__ __forceinline__ void sq_origin(const SqGeom& g, int64_t u, int64_t& r0, int64_t& c0) {
+  if constexpr (RF) {
+    r0 = (u % g.nrt) * kSqRows;
+    c0 = (u / g.nrt) * kSqCols;
+  } else {
+    r0 = (u / g.nct) * kSqRows;
+    c0 = (u % g.nct) * kSqCols;
+  }
+}
+
+// Loads this thread's 16 elements of unit u (column-major unit order) of item
+// b; returns their largest magnitude (0 for a thread outside the matrix).
+template <bool RF, typename T>
+__device__ __forceinline__ float sq_load(const T* __restrict__ x, const SqGeom& g, int64_t b, int64_t u, Blk16<T>& e) {
+  const int w = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  int64_t r0, c0;
+  sq_origin<RF>(g, u, r0, c0);
+  const int64_t r = r0 + 16 * w, col = c0 + 16 * (lane >> 4);
+  if (r >= g.R || col >= g.C) return 0.0f;  // R and C are multiples of 16: whole 16x16 tiles
+  e.load(x + (b * g.R + r + (lane & 15)) * g.C + col);
+  return e.absmax();
+}
+
+// Quantizes unit u of item b from registers with outer scale st. Every thread
+// of the workgroup calls it (it holds barriers when TR).
+template <bool RF, bool TR, typename T>
+__device__ __forceinline__ void sq_unit(const Blk16<T>& e, float m, float st, const SqGeom& g, int64_t b, int64_t u,
+                                        uint8_t* __restrict__ codes, uint8_t* __restrict__ scales,
+                                        uint8_t* __restrict__ codes_t, uint8_t* __restrict__ scales_t, uint8_t* lds,
+                                        uint8_t* lds_sc) {
+  const int w = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int tc = lane >> 4, j = lane & 15;
+  int64_t r0, c0;
+  sq_origin<RF>(g, u, r0, c0);
+  const int64_t row = r0 + 16 * w + j, col = c0 + 16 * tc;
+  const bool ok = r0 + 16 * w < g.R && col < g.C;
+  m = group_max<16>(m);
+  const uint32_t sc = e4m3_rne_sat(m / (6.0f * st));
+  uint32_t a0 = 0, a1 = 0;
+  if (ok) {
+    nvfp4_codes(e, sc, st, a0, a1);
+    *reinterpret_cast<uint2*>(codes + ((b * g.R + row) * g.C + col) / 2) = make_uint2(a0, a1);
+    scales[(b * g.R + row) * (g.C / 16) + col / 16] = (uint8_t)sc;
+  }
+  if constexpr (TR) {
+    *reinterpret_cast<uint2*>(lds + sq_lds(16 * w + j, tc * 8)) = make_uint2(a0, a1);
+    if (j == 0) lds_sc[w * 4 + tc] = (uint8_t)sc;
+    __syncthreads();
+    const int c = threadIdx.x >> 3, q = threadIdx.x & 7;  // column c, rows 16q .. 16q + 15
+    const int64_t rr = r0 + 16 * q, cc = c0 + c;
+    if (rr < g.R && cc < g.C) {
+      const int sh = (c & 1) * 4;
+      uint32_t o[2] = {0u, 0u};
+#pragma unroll
+      for (int p = 0; p < 8; ++p) {  // rows 2p, 2p + 1 of the tile -> output byte p
+        const uint32_t lo = (lds[sq_lds(16 * q + 2 * p, c >> 1)] >> sh) & 0xFu;
+        const uint32_t hi = (lds[sq_lds(16 * q + 2 * p + 1, c >> 1)] >> sh) & 0xFu;
+        o[p >> 2] |= (lo | (hi << 4)) << (8 * (p & 3));
+      }
+      *reinterpret_cast<uint2*>(codes_t + ((b * g.C + cc) * g.R + rr) / 2) = make_uint2(o[0], o[1]);
+      scales_t[(b * g.C + cc) * (g.R / 16) + rr / 16] = lds_sc[q * 4 + (c >> 4)];
+    }
+    __syncthreads();  // the LDS unit is reused by the next unit of a persistent workgroup
+  }
+}
+
+// One unit per workgroup; the outer scale comes from amax_bits (TENSOR,
+// filled by k_amax_items) or outer_in (GIVEN).
+template <typename T, int MODE, bool TR>
+__global__ __launch_bounds__(kSqThreads) void k_quant_nvfp4_square(
+    const T* __restrict__ x, SqGeom g, int64_t nunits, const float* __restrict__ outer_in,
+    const uint32_t* __restrict__ amax_bits, uint8_t* __restrict__ codes, uint8_t* __restrict__ scales,
+    uint8_t* __restrict__ codes_t, uint8_t* __restrict__ scales_t, float* __restrict__ outer_out) {
+  __shared__ __align__(16) uint8_t lds[kSqLdsBytes];
+  __shared__ uint8_t lds_sc[32];
+  // consecutive units run on one XCD (blockIdx.x % 8 picks it)
+  const int64_t per_xcd = (nunits + 7) / 8;
+  const int64_t unit = (int64_t)(blockIdx.x % 8) * per_xcd + blockIdx.x / 8;
+  if (unit >= nunits) return;  // uniform over the workgroup
+  const int64_t per_item = g.nrt * g.nct;
+  const int64_t b = unit / per_item, u = unit % per_item;
+  float st;
+  if constexpr (MODE == BSQ_OUTER_TENSOR) {
+    const float a = __uint_as_float(amax_bits[b]);
+    st = a > 0.0f ? a / 2688.0f : 1.0f;
+  } else {
+    st = outer_in[b];
+  }
+  if (threadIdx.x == 0 && u == 0) outer_out[b] = st;
+  Blk16<T> e;
+  const float m = sq_load<true>(x, g, b, u, e);
+  sq_unit<true, TR>(e, m, st, g, b, u, codes, scales, codes_t, scales_t, lds, lds_sc);
+}
+
+// Per-item outer scale in one HBM pass, as k_quant_nvfp4_items (groups of
+// resident workgroups, each group walking every groups-th item): logical
+// workgroup v of a group (consecutive v on one XCD) owns the contiguous units
+// [v*U/n, (v+1)*U/n) of each of its items (U units per item, at most UPW),
+// publishes the maximum of its share in slot[item][v], prefetches its share of
+// its next item, waits (bounded, with the same re-read fallback) for all slots
+// of the item and quantizes its units from registers.
+template <typename T, int UPW, bool TR>
+__global__ __launch_bounds__(kSqThreads) void k_quant_nvfp4_square_items(
+    const T* __restrict__ x, SqGeom g, int64_t B, int groups, uint32_t* __restrict__ slot,
+    uint8_t* __restrict__ codes, uint8_t* __restrict__ scales, uint8_t* __restrict__ codes_t,
+    uint8_t* __restrict__ scales_t, float* __restrict__ outer_out, uint32_t spin_limit) {
+  __shared__ __align__(16) uint8_t lds[kSqLdsBytes];
+  __shared__ uint8_t lds_sc[32];
+  __shared__ float red[kSqThreads / 64];
+  const int nwg = gridDim.x / groups;  // workgroups per group, a multiple of 8
+  const int grp = blockIdx.x / nwg, wid = blockIdx.x % nwg;
+  const int v = (wid % 8) * (nwg / 8) + wid / 8;
+  const int64_t upi = g.nrt * g.nct;
+  const int64_t lo = v * upi / nwg, hi = (v + 1) * upi / nwg;
+  const int t = threadIdx.x;
+  auto wg_max = [&](float m) -> float {
+    m = wave_max(m);
+    if ((t & 63) == 0) red[t >> 6] = m;
+    __syncthreads();
+    float r = red[0];
+#pragma unroll
+    for (int w = 1; w < kSqThreads / 64; ++w) r = fmaxf(r, red[w]);
+    __syncthreads();
+    return r;
+  };
+  Blk16<T> blk[2][UPW];
+  float am[2][UPW];
+  auto load = [&](int s, int64_t e) -> float {
+    float m = 0.0f;
+#pragma unroll
+    for (int k = 0; k < UPW; ++k) {
+      am[s][k] = 0.0f;
+      if (lo + k < hi) {
+        am[s][k] = sq_load<false>(x, g, e, lo + k, blk[s][k]);
+        m = fmaxf(m, am[s][k]);
+      }
+    }
+    return m;
+  };
+  auto publish = [&](int64_t e, float m) {
+    const float r = wg_max(m);
+    if (t == 0)
+      __hip_atomic_store(slot + e * nwg + v, __float_as_uint(r) | 0x80000000u, __ATOMIC_RELAXED,
+                         __HIP_MEMORY_SCOPE_AGENT);
+  };
+  auto item = [&](int s, int64_t e) {
+    float mx = 0.0f;
+    uint32_t spins = 0;
+    for (;;) {
+      uint32_t val = 0x80000000u;
+      if (t < nwg) val = __hip_atomic_load(slot + e * nwg + t, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      if (!__syncthreads_or((val & 0x80000000u) == 0)) {
+        mx = __uint_as_float(val & 0x7FFFFFFFu);
+        break;
+      }
+      if (++spins >= spin_limit) {  // uniform: reduce the whole item here
+        const uint4* p = reinterpret_cast<const uint4*>(x + e * g.R * g.C);
+        const int64_t nvec = g.R * g.C * (int64_t)sizeof(T) / 16;
+        for (int64_t i = t; i < nvec; i += kSqThreads) mx = fmaxf(mx, absmax16B<T>(p[i]));
+        break;
+      }
+      __builtin_amdgcn_s_sleep(1);
+    }
+    const float a = wg_max(mx);
+    const float st = a > 0.0f ? a / 2688.0f : 1.0f;
+    if (v == 0 && t == 0) outer_out[e] = st;
+#pragma unroll
+    for (int k = 0; k < UPW; ++k)
+      if (lo + k < hi)  // uniform over the workgroup
+        sq_unit<false, TR>(blk[s][k], am[s][k], st, g, e, lo + k, codes, scales, codes_t, scales_t, lds, lds_sc);
+  };
+  const int64_t n = grp < B ? (B - grp + groups - 1) / groups : 0;  // this group's items
+  if (n <= 0) return;
+  auto it = [&](int64_t i) -> int64_t { return grp + i * groups; };
+  publish(it(0), load(0, it(0)));
+  int64_t i = 0;
+  for (; i + 1 < n; i += 2) {  // register sets alternate: item i in set 0, i + 1 in set 1
+    const float m1 = load(1, it(i + 1));
+    item(0, it(i));
+    publish(it(i + 1), m1);
+    if (i + 2 < n) {
+      const float m2 = load(0, it(i + 2));
+      item(1, it(i + 1));
+      publish(it(i + 2), m2);
+    } else {
+      item(1, it(i + 1));
+    }
+  }
+  if (i < n && (n & 1)) item(0, it(i));
+}
+
+// Workgroups per group of the one-pass square kernel (a multiple of 8, one per
+// CU), or 0 when the items are small (see one_pass_items) or need more than
+// max_upw units per workgroup.
+inline int64_t square_one_pass_wgs(int64_t B, int64_t R, int64_t C, int64_t max_upw) {
+  if (!one_pass_items(B, R, C)) return 0;
+  const int64_t cus = bsqh::device_cus() < kOnePassMaxWg ? bsqh::device_cus() : kOnePassMaxWg;
+  const int64_t nwg = cus / 8 * 8;
+  const int64_t upi = ((R + kSqRows - 1) / kSqRows) * ((C + kSqCols - 1) / kSqCols);
+  return nwg >= 8 && upi <= max_upw * nwg ? nwg : 0;
+}
+
+template <typename T>
+int quantize_nvfp4_square_t(const T* x, int64_t B, int64_t R, int64_t C, int mode, const float* outer_in,
+                            uint8_t* codes, uint8_t* scales, uint8_t* codes_t, uint8_t* scales_t,
+                            float* outer_out, uint32_t* ws, hipStream_t s) {
+  const SqGeom g{R, C, (R + kSqRows - 1) / kSqRows, (C + kSqCols - 1) / kSqCols};
+  const bool tr = codes_t != nullptr;
+  if (mode == BSQ_OUTER_TENSOR) {
+    // at most 3 (bf16) or 2 (float) units per workgroup; two groups where a
+    // workgroup stays within 128 VGPRs (two per CU)
+    const int64_t nwg = square_one_pass_wgs(B, R, C, sizeof(T) == 2 ? 3 : 2);
+    if (nwg) {
+      const int64_t upw = (g.nrt * g.nct + nwg - 1) / nwg;
+      const int grp = sizeof(T) == 2 || upw <= 1 ? kOnePassGroups : 1;
+      hipLaunchKernelGGL(k_fill_u32, dim3(grid1(B * nwg)), dim3(kThreads), 0, s, ws, 0u, B * nwg);
+#define BSQ_SQI(UPW, TR)                                                                                          \
+  hipLaunchKernelGGL((k_quant_nvfp4_square_items<T, UPW, TR>), dim3((unsigned)(nwg * grp)), dim3(kSqThreads), 0, s, \
+                     x, g, B, grp, ws, codes, scales, codes_t, scales_t, outer_out, wait_polls())
+      if (upw <= 1) { if (tr) BSQ_SQI(1, true); else BSQ_SQI(1, false); }
+      else if (upw <= 2) { if (tr) BSQ_SQI(2, true); else BSQ_SQI(2, false); }
+      else if constexpr (sizeof(T) == 2) { if (tr) BSQ_SQI(3, true); else BSQ_SQI(3, false); }
+#undef BSQ_SQI
+      return bsqh::launch_status();
+    }
+    hipLaunchKernelGGL(k_fill_u32, dim3(grid1(B)), dim3(kThreads), 0, s, ws, 0u, B);
+    const int64_t vec = R * C * (int64_t)sizeof(T) / 16;
+    const int64_t per_wg = (int64_t)kThreads * kAmaxVecPerThread;
+    const int64_t gx = (vec + per_wg - 1) / per_wg;
+    for (int64_t i0 = 0; i0 < B; i0 += 65535) {
+      const int64_t ni = (B - i0) < 65535 ? (B - i0) : 65535;
+      hipLaunchKernelGGL(k_amax_items<T>, dim3((unsigned)gx, (unsigned)ni), dim3(kThreads), 0, s, x, vec, per_wg,
+                         ws, i0);
+    }
+  }
+  const int64_t nunits = B * g.nrt * g.nct;
+  const dim3 grid((unsigned)((nunits + 7) / 8 * 8));
+#define BSQ_SQ(MODE, TR)                                                                                      \
+  hipLaunchKernelGGL((k_quant_nvfp4_square<T, MODE, TR>), grid, dim3(kSqThreads), 0, s, x, g, nunits, outer_in, \
+                     ws, codes, scales, codes_t, scales_t, outer_out)
+  if (mode == BSQ_OUTER_TENSOR) {
+    if (tr) BSQ_SQ(BSQ_OUTER_TENSOR, true);
+    else BSQ_SQ(BSQ_OUTER_TENSOR, false);
+  } else {
+    if (tr) BSQ_SQ(BSQ_OUTER_GIVEN, true);
+    else BSQ_SQ(BSQ_OUTER_GIVEN, false);
+  }
+#undef BSQ_SQ
+  return bsqh::launch_status();
 }
 
 }  // namespace
@@ -550,4 +848,53 @@ int bsq_quantize_mxfp8_rows(const void* x, int dtype, int64_t rows, int64_t cols
                          static_cast<const float*>(x), nblk, seed, stream_id, codes, scales);
   }
   return bsqh::launch_status();
+}
+
+extern "C" size_t bsq_quantize_nvfp4_square_workspace(int64_t batch, int64_t rows, int64_t cols, int mode) {
+  if (mode != BSQ_OUTER_TENSOR || batch <= 0) return 0;
+  // per item: the maximum's bits, or one arrival slot per workgroup of the one-pass kernel
+  const int64_t words = one_pass_items(batch, rows, cols) ? batch * kOnePassMaxWg : batch;
+  return (size_t)((words * 4 + 255) / 256 * 256);
+}
+
+extern "C" int bsq_quantize_nvfp4_square(const void* x, int dtype, int64_t batch, int64_t rows, int64_t cols,
+                                         int mode, const float* outer_in, uint8_t* codes, uint8_t* scales,
+                                         uint8_t* codes_t, uint8_t* scales_t, float* outer_out, void* ws,
+                                         size_t ws_bytes, bsq_stream_t stream) {
+  BSQ_REQUIRE(dtype == BSQ_F32 || dtype == BSQ_BF16, BSQ_E_DTYPE);
+  BSQ_REQUIRE(mode == BSQ_OUTER_TENSOR || mode == BSQ_OUTER_GIVEN, BSQ_E_ENUM);
+  BSQ_REQUIRE(batch >= 0 && rows >= 0 && cols >= 0 && rows % 16 == 0 && cols % 16 == 0, BSQ_E_SHAPE);
+  if (batch == 0) return BSQ_OK;
+  // element offsets stay far inside int64, the grid inside 2^31 workgroups
+  BSQ_REQUIRE(rows <= ((int64_t)1 << 31) && cols <= ((int64_t)1 << 31), BSQ_E_SHAPE);
+  BSQ_REQUIRE(batch <= ((int64_t)1 << 46) / (rows * cols > 0 ? rows * cols : 1), BSQ_E_SHAPE);
+  const int64_t nunits = batch * ((rows + 127) / 128) * ((cols + 63) / 64);
+  BSQ_REQUIRE(nunits <= ((int64_t)1 << 31) - 8, BSQ_E_SHAPE);
+  const bool empty = rows == 0 || cols == 0;
+  BSQ_REQUIRE(outer_out && (mode != BSQ_OUTER_GIVEN || outer_in), BSQ_E_NULL);
+  BSQ_REQUIRE(empty || (x && codes && scales), BSQ_E_NULL);
+  BSQ_REQUIRE((codes_t == nullptr) == (scales_t == nullptr), BSQ_E_NULL);
+  BSQ_REQUIRE(bsqh::aligned16(x) && bsqh::aligned16(codes) && bsqh::aligned16(codes_t), BSQ_E_ALIGN);
+  BSQ_REQUIRE(((uintptr_t)outer_out & 3) == 0 && ((uintptr_t)outer_in & 3) == 0, BSQ_E_ALIGN);
+  const size_t need = empty ? 0 : bsq_quantize_nvfp4_square_workspace(batch, rows, cols, mode);
+  if (need) {
+    BSQ_REQUIRE(ws, BSQ_E_NULL);
+    BSQ_REQUIRE(((uintptr_t)ws & 3) == 0, BSQ_E_ALIGN);
+    BSQ_REQUIRE(ws_bytes >= need, BSQ_E_WORKSPACE);
+  }
+  hipStream_t s = bsqh::as_stream(stream);
+  if (empty) {
+    if (mode == BSQ_OUTER_GIVEN)
+      hipLaunchKernelGGL(k_copy_f32, dim3(grid1(batch)), dim3(kThreads), 0, s, outer_in, outer_out, batch);
+    else
+      hipLaunchKernelGGL(k_fill_u32, dim3(grid1(batch)), dim3(kThreads), 0, s,
+                         reinterpret_cast<uint32_t*>(outer_out), 0x3F800000u, batch);
+    return bsqh::launch_status();
+  }
+  if (dtype == BSQ_BF16)
+    return quantize_nvfp4_square_t<uint16_t>(static_cast<const uint16_t*>(x), batch, rows, cols, mode, outer_in,
+                                             codes, scales, codes_t, scales_t, outer_out,
+                                             static_cast<uint32_t*>(ws), s);
+  return quantize_nvfp4_square_t<float>(static_cast<const float*>(x), batch, rows, cols, mode, outer_in, codes,
+                                        scales, codes_t, scales_t, outer_out, static_cast<uint32_t*>(ws), s);
 }

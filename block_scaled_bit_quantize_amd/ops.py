@@ -64,6 +64,38 @@ def quantize_nvfp4(x, mode="tensor", outer_in=None, four_over_six=False):
     return codes, scales, outer
 
 
+def quantize_nvfp4_square(x, mode="tensor", outer_in=None, transpose=True):
+    """Square-tile NVFP4 (one scale per 16x16 tile) of x [B, R, C] or [R, C]
+    (float32 or bfloat16; R and C multiples of 16); mode "tensor" or "given".
+    Returns (codes [..., R, C/2], scales [..., R, C/16], outer f32 [B],
+    codes_t [..., C, R/2], scales_t [..., C, R/16]); the transposed pair is
+    None when transpose is False."""
+    lib = load_library()
+    _dev(x, outer_in)
+    squeeze = x.dim() == 2
+    x3 = x.unsqueeze(0) if squeeze else x
+    B, R, C = x3.shape
+    dt = {torch.float32: F32, torch.bfloat16: BF16}.get(x.dtype)
+    if dt is None:
+        raise BsqError("x must be float32 or bfloat16")
+    m = _enum(mode, _OUTER)
+    dev = x.device
+    codes = torch.empty((B, R, C // 2), dtype=torch.uint8, device=dev)
+    scales = torch.empty((B, R, C // 16), dtype=torch.uint8, device=dev)
+    codes_t = torch.empty((B, C, R // 2), dtype=torch.uint8, device=dev) if transpose else None
+    scales_t = torch.empty((B, C, R // 16), dtype=torch.uint8, device=dev) if transpose else None
+    outer = torch.empty((B,), dtype=torch.float32, device=dev)
+    wsb = lib.bsq_quantize_nvfp4_square_workspace(B, R, C, m)
+    ws = _ws(wsb, dev) if wsb else None
+    check(lib.bsq_quantize_nvfp4_square(x3.data_ptr(), dt, B, R, C, m, _ptr(outer_in), codes.data_ptr(),
+                                        scales.data_ptr(), _ptr(codes_t), _ptr(scales_t), outer.data_ptr(),
+                                        _ptr(ws), wsb, _stream()), "bsq_quantize_nvfp4_square")
+    if squeeze:
+        return (codes[0], scales[0], outer, codes_t[0] if transpose else None,
+                scales_t[0] if transpose else None)
+    return codes, scales, outer, codes_t, scales_t
+
+
 def padded_segment_layout(seg_offsets_host, cols):
     """Host helper: (padded length of each segment, total elements) of the padded
     per-segment transposed layout for a host list/array of segment offsets."""

@@ -105,6 +105,40 @@ int bsq_quantize_nvfp4(const void* x, int dtype, int64_t batch, int64_t rows, in
                        float* outer_out, void* ws, size_t ws_bytes, bsq_stream_t stream);
 
 /* ------------------------------------------------------------------------
+ * Square-tile NVFP4 quantization ("Block-scaled backward passes": the
+ * alternative the pages compare against, one scale per 16x16 tile, shown in
+ * the row-vs-column and outlier figures). Because the tile is square, the
+ * quantization of the transpose is bitwise the transpose of the quantization;
+ * the call can write both layouts from one read of x.
+ *
+ * x         [batch, rows, cols] of `dtype` (F32 or BF16); rows % 16 == 0 and
+ *           cols % 16 == 0.
+ * mode      BSQ_OUTER_TENSOR (s_t = f32(amax/2688) per batch item, 1 for an
+ *           all-zero item) or BSQ_OUTER_GIVEN (outer_in [batch], positive).
+ * codes     [batch, rows, cols/2] u8, two E2M1 codes per byte (element 2k in
+ *           the low nibble), as bsq_quantize_nvfp4.
+ * scales    [batch, rows, cols/16] u8 (E4M3): the 1x16 layout, each tile's
+ *           scale repeated in its 16 rows, so the 1x16 consumers (the grouped
+ *           GEMM, dequantize, requantize) read it unchanged.
+ * codes_t   [batch, cols, rows/2] u8 and scales_t [batch, cols, rows/16] u8:
+ *           the same quantization of x transposed (per item); both NULL to
+ *           skip, else both non-NULL.
+ * outer_out [batch] FP32, receives s_t.
+ * ws        bsq_quantize_nvfp4_square_workspace() bytes (0 for GIVEN).
+ * Per tile: a_t = max |x|; s_b = E4M3 round-to-nearest-even of
+ * f32(a_t / f32(6 s_t)), saturating at 448; each element rounds as in
+ * bsq_quantize_nvfp4 with that s_b.
+ * Alignment: x, codes, codes_t 16 bytes; outer_in, outer_out, ws 4 bytes.
+ * Errors: NULL, SHAPE, ALIGN, DTYPE, ENUM (BSQ_OUTER_ROW or a flag),
+ * WORKSPACE, LAUNCH.
+ * ---------------------------------------------------------------------- */
+size_t bsq_quantize_nvfp4_square_workspace(int64_t batch, int64_t rows, int64_t cols, int mode);
+int bsq_quantize_nvfp4_square(const void* x, int dtype, int64_t batch, int64_t rows, int64_t cols,
+                              int mode, const float* outer_in, uint8_t* codes, uint8_t* scales,
+                              uint8_t* codes_t, uint8_t* scales_t, float* outer_out, void* ws,
+                              size_t ws_bytes, bsq_stream_t stream);
+
+/* ------------------------------------------------------------------------
  * MXFP8 quantization of a gradient (quantized linear layer figure: the BF16
  * output gradient is quantized to MXFP8 with stochastic rounding, row-wise
  * for DGRAD and transposed for WGRAD).

@@ -65,6 +65,26 @@ def test_quantize_nvfp4_validation(lib):
     assert lib.bsq_quantize_nvfp4_workspace(3, 4, 16, 1) == 0
 
 
+def test_quantize_nvfp4_square_validation(lib):
+    q = lib.bsq_quantize_nvfp4_square
+    # x, dtype, B, R, C, mode, outer_in, codes, scales, codes_t, scales_t, outer_out, ws, ws_bytes, stream
+    assert q(FAKE, 7, 1, 16, 16, 2, FAKE, FAKE, FAKE, None, None, FAKE, None, 0, None) == E_DTYPE
+    assert q(FAKE, 1, 1, 16, 16, 1, None, FAKE, FAKE, None, None, FAKE, None, 0, None) == E_ENUM   # per-row
+    assert q(FAKE, 1, 1, 16, 16, 16, FAKE, FAKE, FAKE, None, None, FAKE, None, 0, None) == E_ENUM  # a flag
+    assert q(FAKE, 1, 1, 24, 16, 2, FAKE, FAKE, FAKE, None, None, FAKE, None, 0, None) == E_SHAPE
+    assert q(FAKE, 1, 1, 16, 8, 2, FAKE, FAKE, FAKE, None, None, FAKE, None, 0, None) == E_SHAPE
+    assert q(FAKE, 1, 1, 2 ** 32, 16, 2, FAKE, FAKE, FAKE, None, None, FAKE, None, 0, None) == E_SHAPE
+    assert q(FAKE, 1, 1, 16, 16, 2, None, FAKE, FAKE, None, None, FAKE, None, 0, None) == E_NULL   # GIVEN needs outer_in
+    assert q(FAKE, 1, 1, 16, 16, 2, FAKE, FAKE, FAKE, FAKE, None, FAKE, None, 0, None) == E_NULL   # codes_t alone
+    assert q(FAKE, 1, 1, 16, 16, 2, FAKE, FAKE, FAKE, FAKE + 8, FAKE, FAKE, None, 0, None) == E_ALIGN
+    assert q(FAKE, 1, 1, 16, 16, 0, None, FAKE, FAKE, None, None, FAKE, None, 0, None) == E_NULL   # TENSOR needs ws
+    assert q(FAKE, 1, 1, 16, 16, 0, None, FAKE, FAKE, None, None, FAKE, FAKE, 4, None) == E_WORKSPACE
+    assert q(None, 1, 0, 16, 16, 0, None, None, None, None, None, None, None, 0, None) == OK      # empty batch
+    assert lib.bsq_quantize_nvfp4_square_workspace(3, 16, 16, 0) >= 12
+    assert lib.bsq_quantize_nvfp4_square_workspace(3, 1024, 1024, 0) >= 3 * 4 * 256
+    assert lib.bsq_quantize_nvfp4_square_workspace(3, 1024, 1024, 2) == 0
+
+
 def test_quantize_mxfp8_validation(lib):
     q = lib.bsq_quantize_mxfp8
     assert q(FAKE, 1, 4, 48, 0, None, 0, 1, 0, 0, FAKE, FAKE, None, 0, None) == E_SHAPE

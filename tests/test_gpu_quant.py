@@ -1,6 +1,9 @@
 """GPU parity of the quantizers, requantization, RNG and routing against the
 CPU oracle (bit-exact bytes), at small sizes spanning several tiles with
 ragged tails and at the workloads' full sizes on sampled outputs."""
+import json
+import os
+
 import numpy as np
 import pytest
 import torch
@@ -206,13 +209,14 @@ def test_quantize_mxfp8_transposed_small(dtype, rnd):
     assert np.array_equal(h(gc), oc) and np.array_equal(h(gs), os_)
 
 
-@pytest.mark.parametrize("fmt", ["mxfp8", "nvfp4"])
+_REQ_SHAPES = [(2, 64, 128), (1, 160, 64), (3, 256, 192), (1, 48, 128)]
+
+
 @pytest.mark.parametrize("rnd", ["rn", "sr"])
 @pytest.mark.parametrize("in_mode", ["tensor", "row"])
-@pytest.mark.parametrize("B,R,C", [(2, 64, 128), (1, 160, 64), (3, 256, 192), (1, 48, 128)])
+@pytest.mark.parametrize("fmt,B,R,C", [(f, *shp) for f in ("mxfp8", "nvfp4") for shp in _REQ_SHAPES
+                                       if f == "nvfp4" or shp[1] % 32 == 0])  # MXFP8 output: rows % 32 == 0
 def test_requant_batch_small(fmt, rnd, in_mode, B, R, C):
-    if fmt == "mxfp8" and R % 32:
-        pytest.skip("MXFP8 output needs rows % 32 == 0")
     log(f"requant batch {fmt} {rnd} {in_mode} {(B, R, C)}")
     rng = np.random.default_rng(B * 1000 + R + C)
     x = _data(rng, (B, R, C), "t3")
@@ -276,6 +280,103 @@ def test_route_small_and_full():
         assert np.array_equal(h(seg), oseg)
         assert np.array_equal(h(ri), ori)
         assert np.array_equal(h(pr), opr)
+
+
+def _square_oracle(x, mode, outer):
+    m = {"tensor": Q.OUTER_TENSOR, "given": Q.OUTER_GIVEN}[mode]
+    oc, os_, oo = Q.quantize_nvfp4_square(x, m, outer)
+    oct_, ost, _ = Q.quantize_nvfp4_square(np.ascontiguousarray(x.transpose(0, 2, 1)), m, outer)
+    return oc, os_, oo, oct_, ost
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+@pytest.mark.parametrize("mode", ["tensor", "given"])
+@pytest.mark.parametrize("shape,kind", [((1, 16, 16), "normal"), ((2, 48, 80), "wide"), ((3, 144, 272), "zeros_mix"),
+                                        ((1, 256, 384), "t3"), ((2, 400, 16), "normal"), ((1, 16, 400), "wide")])
+def test_quantize_nvfp4_square_small(dtype, mode, shape, kind):
+    """Square-tile NVFP4, both layouts, against the oracle (the transposed
+    layout against the oracle run on x transposed), bit for bit; shapes span
+    several 128 x 128 workgroup tiles with ragged 16-multiples."""
+    log(f"quantize_nvfp4_square {dtype} {mode} {shape} {kind}")
+    rng = np.random.default_rng(hash(("sq", dtype, mode, shape, kind)) % 2**32)
+    x = _data(rng, shape, kind)
+    if dtype == "bf16":
+        bits = synth.bf16_bits(x)
+        x = synth.bf16_to_f32(bits).reshape(shape)
+        xd = bf16_t(bits.reshape(shape))
+    else:
+        xd = t(x)
+    outer = (np.abs(rng.standard_normal(shape[0])) * 0.01 + 1e-3).astype(f32) if mode == "given" else None
+    gc, gs, go, gct, gst = bsq.quantize_nvfp4_square(xd, mode, t(outer) if outer is not None else None)
+    oc, os_, oo, oct_, ost = _square_oracle(x, mode, outer)
+    assert np.array_equal(h(go), oo)
+    assert np.array_equal(h(gs), os_) and np.array_equal(h(gc), oc)
+    assert np.array_equal(h(gst), ost) and np.array_equal(h(gct), oct_)
+    gc2, gs2, go2, n1, n2 = bsq.quantize_nvfp4_square(xd, mode, t(outer) if outer is not None else None,
+                                                      transpose=False)
+    assert n1 is None and n2 is None
+    assert np.array_equal(h(gc2), oc) and np.array_equal(h(gs2), os_)
+
+
+@pytest.mark.parametrize("dtype,shape", [("bf16", (3, 512, 1024)), ("bf16", (2, 1280, 2048)),
+                                         ("bf16", (3, 1536, 3072)), ("bf16", (1, 4096, 2560)),
+                                         ("f32", (2, 512, 1040)), ("f32", (1, 1024, 2560)),
+                                         ("f32", (1, 4096, 2560)), ("bf16", (2, 1040, 528))])
+def test_quantize_nvfp4_square_one_pass(dtype, shape):
+    """Items of at least 1 MiB take the one-pass square kernel (1, 2 or 3
+    units per workgroup, one or two interleaved groups, an odd item count,
+    workgroups without a unit, ragged units); items needing more units per
+    workgroup take the two-pass path. Both layouts must equal the oracle's
+    bytes."""
+    log(f"quantize_nvfp4_square tensor one-pass {dtype} {shape}")
+    rng = np.random.default_rng(17 + shape[1])
+    x = rng.standard_normal(shape).astype(f32)
+    x[-1, 3, 7] = -250.0  # an outlier sets the last item's outer scale
+    if dtype == "bf16":
+        bits = synth.bf16_bits(x)
+        x = synth.bf16_to_f32(bits).reshape(shape)
+        xd = bf16_t(bits.reshape(shape))
+    else:
+        xd = t(x)
+    gc, gs, go, gct, gst = bsq.quantize_nvfp4_square(xd, "tensor")
+    oc, os_, oo, oct_, ost = _square_oracle(x, "tensor", None)
+    assert np.array_equal(h(go), oo)
+    assert np.array_equal(h(gs), os_) and np.array_equal(h(gc), oc)
+    assert np.array_equal(h(gst), ost) and np.array_equal(h(gct), oct_)
+
+
+def test_quantize_nvfp4_square_one_pass_wait_fallback():
+    """A poll limit of 0 sends every workgroup of the one-pass square kernel that
+    finds a slot unmarked through its fallback (it reduces the item itself);
+    the bytes are unchanged."""
+    log("quantize_nvfp4_square tensor one-pass, fallback")
+    rng = np.random.default_rng(23)
+    shape = (2, 512, 2048)
+    bits = synth.bf16_bits(rng.standard_normal(shape).astype(f32))
+    x = synth.bf16_to_f32(bits).reshape(shape)
+    os.environ["BSQ_WAIT_POLLS"] = "0"
+    try:
+        gc, gs, go, gct, gst = bsq.quantize_nvfp4_square(bf16_t(bits.reshape(shape)), "tensor")
+        torch.cuda.synchronize()
+    finally:
+        del os.environ["BSQ_WAIT_POLLS"]
+    oc, os_, oo, oct_, ost = _square_oracle(x, "tensor", None)
+    assert np.array_equal(h(go), oo)
+    assert np.array_equal(h(gs), os_) and np.array_equal(h(gc), oc)
+    assert np.array_equal(h(gst), ost) and np.array_equal(h(gct), oct_)
+
+
+def test_quantize_nvfp4_square_outlier_figure():
+    """The outlier figure's tile (one large value among values in [1, 2], outer
+    scale 1): with one 16x16 scale only the outlier survives, on the GPU too."""
+    log("quantize_nvfp4_square outlier figure")
+    rng = np.random.default_rng(11)
+    x = rng.uniform(1.0, 2.0, (16, 16)).astype(f32)
+    x[15, 7] = 100.0
+    gc, gs, _, gct, _ = bsq.quantize_nvfp4_square(t(x), "given", t(np.array([1.0], f32)))
+    gold = json.load(open(os.path.join(os.path.dirname(__file__), "golden", "worked_examples.json")))
+    assert int(np.count_nonzero(F.unpack_fp4(h(gc)) & 7)) == gold["figure3_outlier_tile"]["survive_16x16"]
+    assert int(np.count_nonzero(F.unpack_fp4(h(gct)) & 7)) == gold["figure3_outlier_tile"]["survive_16x16"]
 
 
 # ---------------------------------------------------------------- full sizes, sampled outputs
@@ -444,3 +545,29 @@ def test_determinism():
     r1 = [h(v) for v in bsq.requant_transpose_sr(p, s, o, "row", "mxfp8", seed=9, stream_id=1)]
     r2 = [h(v) for v in bsq.requant_transpose_sr(p, s, o, "row", "mxfp8", seed=9, stream_id=1)]
     assert all(np.array_equal(u, v) for u, v in zip(r1, r2))
+
+
+def test_quantize_nvfp4_square_workload2_weights_full(wl2):
+    """The square-tile variant on the full expert weights [64, 1536, 4096]
+    (bf16, per-expert outer scale): sampled experts against the oracle in
+    both layouts, and on every expert the transposed codes and scales are the
+    transpose of the row-major ones (the property the square tile exists for)."""
+    log("quantize_nvfp4_square workload2 weights")
+    w = wl2["w"]
+    gc, gs, go, gct, gst = bsq.quantize_nvfp4_square(bf16_t(w), "tensor")
+    for e in (0, 29, 63):
+        we = synth.bf16_to_f32(w[e])[None]
+        oc, os_, oo, oct_, ost = _square_oracle(we, "tensor", None)
+        assert np.array_equal(h(go)[e:e + 1], oo)
+        assert np.array_equal(h(gs[e]), os_[0]) and np.array_equal(h(gc[e]), oc[0])
+        assert np.array_equal(h(gst[e]), ost[0]) and np.array_equal(h(gct[e]), oct_[0])
+    for e0 in range(0, 64, 16):
+        c = gc[e0:e0 + 16]
+        ct = gct[e0:e0 + 16]
+        lo = torch.stack([c & 15, c >> 4], dim=-1).flatten(-2)       # [16, 1536, 4096] nibbles
+        lot = torch.stack([ct & 15, ct >> 4], dim=-1).flatten(-2)    # [16, 4096, 1536]
+        assert torch.equal(lot, lo.transpose(1, 2))
+        del lo, lot
+    gs_tiles = gs[:, ::16, :]                                          # [64, 96, 256]
+    assert torch.equal(gs, gs_tiles.repeat_interleave(16, dim=1))
+    assert torch.equal(gst, gs_tiles.transpose(1, 2).repeat_interleave(16, dim=1))   # [64, 4096, 96]
