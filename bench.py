@@ -84,8 +84,11 @@ def algorithmic(seg_host):
         "requant_x": ("GB/s", nv(T, H) + T * 4 + M * 4 + mx(H * smp)),
         "dgrad": ("TFLOP/s", gemm),
         "wgrad": ("TFLOP/s", gemm),
-        # not a step stage: the square-tile weight quantizer, both layouts from one read
+        # not step stages: the square-tile weight quantizer (both layouts from one
+        # read) and the combine codec on the dispatched expert output rows [M, H]
         "quant_w_square": ("GB/s", E * F * H * 2 + 2 * nv(E * F, H) + E * 4),
+        "combine_encode": ("GB/s", M * H * 2 + M * H + M * H // 32),
+        "combine_decode": ("GB/s", M * H + M * H // 32 + M * 4 + T * H * 2),
     }
 
 
@@ -97,6 +100,8 @@ def stage_sources(stage, native_fp8=False):
         return (main, "bsq_device.h", "bsq_internal.h")
     if stage == "route":
         return ("route.hip", "bsq_internal.h")
+    if stage.startswith("combine_"):
+        return ("codec.hip", "bsq_device.h", "bsq_internal.h")
     return ("quantize.hip", "transpose_quant.hip", "bsq_device.h", "bsq_internal.h")
 
 
@@ -321,6 +326,34 @@ def main():
             "frac": round(ach / HBM_PEAK_GBS, 4),
             "traffic": read_traffic("quant_w_square", kernel_sha(*stage_sources("quant_w_square"))),
             "alternative_to": "quant_w + requant_w where the backward reads W^T in NVFP4 (square tiles) instead of SR MXFP8"}
+        # the combine codec (RHT-32 + block-scaled S2F6) on the expert output
+        # rows of the layer's combine: [tokens * topk, hidden] bf16, seeded
+        gen = torch.Generator(device=dev)
+        gen.manual_seed(2)
+        payload = torch.randn((M, H), generator=gen, device=dev, dtype=torch.float32)
+        payload = torch.where(torch.rand((M, H), generator=gen, device=dev) < 1e-3, payload * 20.0, payload)
+        payload = payload.to(torch.bfloat16)
+        _, _, pair_row = bsq.route(inp["ids"], E)
+        signs = 0x9E3779B9
+        enc = bsq.rht_s2f6_encode(payload, signs)
+        for name, fn in (("combine_encode", lambda: bsq.rht_s2f6_encode(payload, signs)),
+                         ("combine_decode", lambda: bsq.rht_s2f6_combine(enc[0], enc[1], pair_row, K_TOP, signs))):
+            for _ in range(2):
+                fn()
+            torch.cuda.synchronize()
+            a0.record()
+            for _ in range(reps):
+                fn()
+            a1.record()
+            torch.cuda.synchronize()
+            ms = a0.elapsed_time(a1) / reps
+            ach = algo[name][1] / (ms * 1e-3) / 1e9
+            alternatives[name] = {
+                "ms": round(ms, 4), "achieved": round(ach, 2), "unit": "GB/s", "peak": HBM_PEAK_GBS,
+                "frac": round(ach / HBM_PEAK_GBS, 4),
+                "traffic": read_traffic(name, kernel_sha(*stage_sources(name))),
+                "alternative_to": "bf16 combine payload (16 bits per value; the codec carries 8.25)"}
+        del payload, enc
 
     if args.copy_calibration:
         src_buf = torch.empty(512 << 20, dtype=torch.uint8, device=dev).fill_(1)

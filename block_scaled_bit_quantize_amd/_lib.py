@@ -35,6 +35,9 @@ SIGNATURES = {
                                               c_int, c_vp]),
     "bsq_route_workspace": (c_size, [c_i64, c_i64]),
     "bsq_route": (c_int, [c_vp, c_i64, c_i64, c_i64, c_vp, c_vp, c_vp, c_vp, c_size, c_vp]),
+    "bsq_rht_s2f6_encode": (c_int, [c_vp, c_int, c_i64, c_i64, ctypes.c_uint32, c_vp, c_vp, c_vp]),
+    "bsq_rht_s2f6_combine": (c_int, [c_vp, c_vp, c_i64, c_i64, c_vp, c_i64, c_i64, ctypes.c_uint32, c_vp, c_int,
+                                     c_vp]),
     "bsq_dequantize_nvfp4": (c_int, [c_vp, c_vp, c_vp, c_int, c_i64, c_i64, c_i64, c_vp, c_vp]),
     "bsq_dequantize_mxfp8": (c_int, [c_vp, c_vp, c_i64, c_i64, c_vp, c_vp]),
     "bsq_rng_bits16": (c_int, [c_u64, c_u64, c_u64, c_i64, c_vp, c_vp]),

@@ -248,6 +248,39 @@ def route(topk_ids, num_experts):
     return row_index, seg, pair_row
 
 
+def rht_s2f6_encode(x, signs):
+    """Combine-codec sender: x [R, C] (float32 or bfloat16, C % 32 == 0) ->
+    (codes u8 [R, C] two's-complement S2F6, scales u8 [R, C/32] UE8M0) of the
+    rows rotated by the 32-point Hadamard transform with sign mask `signs`."""
+    lib = load_library()
+    _dev(x)
+    R, C = x.shape
+    dt = {torch.float32: F32, torch.bfloat16: BF16}.get(x.dtype)
+    if dt is None:
+        raise BsqError("x must be float32 or bfloat16")
+    codes = torch.empty((R, C), dtype=torch.uint8, device=x.device)
+    scales = torch.empty((R, C // 32), dtype=torch.uint8, device=x.device)
+    check(lib.bsq_rht_s2f6_encode(x.data_ptr(), dt, R, C, signs & 0xFFFFFFFF, codes.data_ptr(), scales.data_ptr(),
+                                  _stream()), "bsq_rht_s2f6_encode")
+    return codes, scales
+
+
+def rht_s2f6_combine(codes, scales, pair_row, k, signs, out_dtype=torch.bfloat16):
+    """Combine-codec receiver: token t sums the dequantized rows
+    pair_row[t*k + j] (int32 [T*k]) and inverts the transform -> [T, C]."""
+    lib = load_library()
+    _dev(codes, scales, pair_row)
+    R, C = codes.shape
+    T = pair_row.numel() // k
+    od = {torch.float32: F32, torch.bfloat16: BF16}.get(out_dtype)
+    if od is None:
+        raise BsqError("out_dtype must be float32 or bfloat16")
+    out = torch.empty((T, C), dtype=out_dtype, device=codes.device)
+    check(lib.bsq_rht_s2f6_combine(codes.data_ptr(), scales.data_ptr(), R, C, pair_row.data_ptr(), T, k,
+                                   signs & 0xFFFFFFFF, out.data_ptr(), od, _stream()), "bsq_rht_s2f6_combine")
+    return out
+
+
 def dequantize_nvfp4(codes, scales, outer, mode="tensor"):
     lib = load_library()
     _dev(codes, scales, outer)

@@ -295,6 +295,42 @@ int bsq_route(const int32_t* topk_ids, int64_t tokens, int64_t k, int64_t E, int
               bsq_stream_t stream);
 
 /* ------------------------------------------------------------------------
+ * Combine codec ("Quantized communications": before the combine exchange an
+ * expert output row is rotated by a 32-dimensional random Hadamard transform
+ * and quantized to block-scaled S2F6, one UE8M0 scale per 32 values, 8.25
+ * bits per value; the receiver dequantizes and aggregates a token's copies
+ * and inverts the transform).
+ *
+ * Transform: z = H D x / sqrt(32) per block of 32 along a row; D = diag of
+ * signs (bit i of `signs` set: element i negated), H the Sylvester Hadamard
+ * matrix (H_2n = [[H, H], [H, -H]]); float32 butterfly of spans 1, 2, 4, 8, 16
+ * ((a, b) -> (a + b, a - b)) and one multiply by f32(1/sqrt(32)).
+ * S2F6: values k/64, k in [-128, 127] (two's-complement byte). Scale: the
+ * smallest 2^e with max|z| <= (127/64) 2^e, e in [-127, 127] (-127 for a zero
+ * block), byte e + 127; k = round-half-even(z 2^(6-e)) saturated.
+ *
+ * bsq_rht_s2f6_encode
+ *   x       [rows, cols] of `dtype` (F32 or BF16), cols % 32 == 0.
+ *   codes   [rows, cols] u8; scales [rows, cols/32] u8.
+ *   Alignment: x and codes 16 bytes. Errors: NULL, SHAPE, ALIGN, DTYPE, LAUNCH.
+ * bsq_rht_s2f6_combine
+ *   codes, scales  as written by the encoder for `rows` rows of `cols`.
+ *   pair_row int32 [tokens*k]: row of copy j of token t at t*k + j (as
+ *            bsq_route writes it); indices outside [0, rows) are clamped.
+ *   out      [tokens, cols] of out_dtype (F32, or BF16 rounded to nearest
+ *            even): D H / sqrt(32) applied to the float32 sum, in slot order j,
+ *            of the dequantized blocks k/64 * 2^e (exact) of the token's rows.
+ *   1 <= k <= 64. Alignment: codes and out 16 bytes, pair_row 4 bytes.
+ *   Errors: NULL, SHAPE, ALIGN, DTYPE, LAUNCH.
+ * NaN and infinite inputs give unspecified codes (memory-safe).
+ * ---------------------------------------------------------------------- */
+int bsq_rht_s2f6_encode(const void* x, int dtype, int64_t rows, int64_t cols, uint32_t signs,
+                        uint8_t* codes, uint8_t* scales, bsq_stream_t stream);
+int bsq_rht_s2f6_combine(const uint8_t* codes, const uint8_t* scales, int64_t rows, int64_t cols,
+                         const int32_t* pair_row, int64_t tokens, int64_t k, uint32_t signs, void* out,
+                         int out_dtype, bsq_stream_t stream);
+
+/* ------------------------------------------------------------------------
  * Test support: dequantization and the raw random bits.
  * bsq_dequantize_nvfp4: out[b, r, c] = f32(f32(q * s_b) * s_t) (FP32),
  *   outer per mode as in bsq_requant_transpose_sr's batch mode.

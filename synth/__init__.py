@@ -14,6 +14,9 @@ Workloads (data seed 1000 + workload number, one PCG64 sub-stream per tensor):
   5 large skewed forward: x bf16 [65536, 7168] ~ Student-t(3);
     W bf16 [128, 2048, 7168] ~ N(0, 0.02); top-8 of 128 experts with Zipf(1.1)
     popularity.
+Combine payload (the expert output rows that the combine codec carries):
+    workload 2's dispatched rows, bf16 [131072, 4096] ~ N(0, 1), 0.1% of
+    entries scaled by 20 (outliers).
 """
 import numpy as np
 
@@ -132,5 +135,20 @@ def output_grad(rows, cols, workload=4):
         v = rng.standard_normal(m, dtype=np.float32) * np.float32(p["g_std"])
         spike = rng.random(m) < p["spike_frac"]
         v[spike] *= np.float32(p["spike_scale"])
+        out[s:s + m] = bf16_bits(v)
+    return out.reshape(rows, cols)
+
+
+def combine_rows(rows, cols, workload=2):
+    """Expert output rows bf16 [rows, cols] ~ N(0, 1) with 0.1% of entries
+    scaled by 20."""
+    rng = rng_for(workload, 4)
+    n = rows * cols
+    out = np.empty(n, dtype=np.uint16)
+    for s in range(0, n, _CHUNK):
+        m = min(_CHUNK, n - s)
+        v = rng.standard_normal(m, dtype=np.float32)
+        spike = rng.random(m) < 1e-3
+        v[spike] *= np.float32(20.0)
         out[s:s + m] = bf16_bits(v)
     return out.reshape(rows, cols)

@@ -85,6 +85,27 @@ def test_quantize_nvfp4_square_validation(lib):
     assert lib.bsq_quantize_nvfp4_square_workspace(3, 1024, 1024, 2) == 0
 
 
+def test_codec_validation(lib):
+    e = lib.bsq_rht_s2f6_encode
+    assert e(FAKE, 7, 1, 32, 0, FAKE, FAKE, None) == E_DTYPE
+    assert e(FAKE, 1, 1, 48, 0, FAKE, FAKE, None) == E_SHAPE
+    assert e(FAKE, 1, -1, 32, 0, FAKE, FAKE, None) == E_SHAPE
+    assert e(FAKE, 1, 2 ** 40, 2 ** 20, 0, FAKE, FAKE, None) == E_SHAPE
+    assert e(None, 1, 1, 32, 0, FAKE, FAKE, None) == E_NULL
+    assert e(FAKE + 8, 1, 1, 32, 0, FAKE, FAKE, None) == E_ALIGN
+    assert e(None, 1, 0, 32, 0, None, None, None) == OK                       # empty: no work
+    c = lib.bsq_rht_s2f6_combine
+    # codes, scales, rows, cols, pair_row, tokens, k, signs, out, out_dtype, stream
+    assert c(FAKE, FAKE, 4, 32, FAKE, 2, 2, 0, FAKE, 9, None) == E_DTYPE
+    assert c(FAKE, FAKE, 4, 40, FAKE, 2, 2, 0, FAKE, 1, None) == E_SHAPE
+    assert c(FAKE, FAKE, 4, 32, FAKE, 2, 0, 0, FAKE, 1, None) == E_SHAPE       # k >= 1
+    assert c(FAKE, FAKE, 4, 32, FAKE, 2, 65, 0, FAKE, 1, None) == E_SHAPE      # k <= 64
+    assert c(FAKE, FAKE, 0, 32, FAKE, 2, 2, 0, FAKE, 1, None) == E_SHAPE       # tokens need rows
+    assert c(FAKE, FAKE, 4, 32, None, 2, 2, 0, FAKE, 1, None) == E_NULL
+    assert c(FAKE, FAKE, 4, 32, FAKE + 2, 2, 2, 0, FAKE, 1, None) == E_ALIGN
+    assert c(None, None, 4, 32, None, 0, 2, 0, None, 1, None) == OK            # no tokens: no work
+
+
 def test_quantize_mxfp8_validation(lib):
     q = lib.bsq_quantize_mxfp8
     assert q(FAKE, 1, 4, 48, 0, None, 0, 1, 0, 0, FAKE, FAKE, None, 0, None) == E_SHAPE
