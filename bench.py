@@ -34,7 +34,7 @@ sys.path.insert(0, ROOT)
 
 METRIC = "quantize/requant GB/s (% HBM peak); NVFP4 expert grouped-GEMM TFLOPS (% MFMA)"
 HBM_PEAK_GBS = 8000.0            # MI355X HBM3E, published
-MFMA_PEAK_TFLOPS = {"f16": 2500.0, "bf16": 2500.0, "fp8": 5000.0}  # dense, published
+MFMA_PEAK_TFLOPS = {"f16": 2500.0, "bf16": 2500.0, "fp8": 5000.0, "fp4": 10100.0}  # dense, published
 
 T, H, E, K_TOP, F = 16384, 4096, 64, 8, 1536
 M = T * K_TOP
@@ -286,7 +286,7 @@ def main():
     algo = algorithmic(seg_host)
     kernels = {}
     for name, ts in per_stage.items():
-        ms = float(np.mean(ts))
+        ms = float(np.median(ts))
         unit, work = algo[name]
         if unit == "GB/s":
             ach = work / (ms * 1e-3) / 1e9
@@ -296,6 +296,9 @@ def main():
             peak = MFMA_PEAK_TFLOPS["f16" if name == "fprop" else ("fp8" if args.native_fp8 else "bf16")]
         kernels[name] = {"ms": round(ms, 4), "achieved": round(ach, 2), "unit": unit, "peak": peak,
                          "frac": round(ach / peak, 4)}
+        if unit != "GB/s":  # the contraction also against the block-scaled FP8 and FP4 MFMA peaks
+            kernels[name]["frac_of_fp8_peak"] = round(ach / MFMA_PEAK_TFLOPS["fp8"], 4)
+            kernels[name]["frac_of_fp4_peak"] = round(ach / MFMA_PEAK_TFLOPS["fp4"], 4)
 
     gemm_flops = sum(algo[n][1] for n in ("fprop", "dgrad", "wgrad") if n in kernels)
     value = gemm_flops / (ms_per_step * 1e-3) / 1e12
