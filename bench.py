@@ -89,6 +89,13 @@ def algorithmic(seg_host):
         "quant_w_square": ("GB/s", E * F * H * 2 + 2 * nv(E * F, H) + E * 4),
         "combine_encode": ("GB/s", M * H * 2 + M * H + M * H // 32),
         "combine_decode": ("GB/s", M * H + M * H // 32 + M * 4 + T * H * 2),
+        # the expert forward chain (w13 GEMM, SwiGLU + quantize, w2 GEMM + codec)
+        "chain_quant_w13": ("GB/s", E * 2 * F * H * 2 + nv(E * 2 * F, H) + E * 4),
+        "chain_w13": ("TFLOP/s", 2.0 * M * 2 * F * H),
+        "chain_swiglu_quant": ("GB/s", M * 2 * F * 2 + nv(M, F) + M * 4),
+        "chain_quant_w2": ("GB/s", E * H * F * 2 + nv(E * H, F) + E * 4),
+        "chain_w2_codec": ("TFLOP/s", 2.0 * M * H * F),
+        "chain_combine": ("GB/s", M * H + M * H // 32 + M * 4 + T * H * 2),
     }
 
 
@@ -190,6 +197,55 @@ def cpu_baseline(seg_host, row_index_host):
                        "GEMM references are float64 BLAS"),
             "step_seconds_equiv": round(step_s, 3),
             "stage_seconds_equiv": {k: round(v, 3) for k, v in times.items()}}
+
+
+def chain_forward(torch, bsq, inp, algo, dev, pair_row, reps=5):
+    """The expert forward chain (w13 GEMM, SwiGLU + per-row NVFP4, w2 GEMM with
+    the RHT + S2F6 combine codec in its epilogue, combine) on the step's
+    tokens and routing with seeded w13 [E, 2F, H] and w2 [E, H, F]; each
+    stage timed with HIP events, median over `reps` passes."""
+    gen = torch.Generator(device=dev)
+    gen.manual_seed(3)
+    w13 = (torch.randn((E, 2 * F, H), generator=gen, device=dev) * 0.02).to(torch.bfloat16)
+    w2 = (torch.randn((E, H, F), generator=gen, device=dev) * 0.02).to(torch.bfloat16)
+    ri, seg, _ = bsq.route(inp["ids"], E)
+    xc, xs, xo = bsq.quantize_nvfp4(inp["x"], "row", four_over_six=True)
+    signs = 0x13579BDF
+    names = ["chain_quant_w13", "chain_w13", "chain_swiglu_quant", "chain_quant_w2", "chain_w2_codec",
+             "chain_combine"]
+    times = {n: [] for n in names}
+    for it in range(reps + 1):
+        ev = [torch.cuda.Event(enable_timing=True) for _ in range(len(names) + 1)]
+        ev[0].record()
+        w13q = bsq.quantize_nvfp4(w13, "tensor")
+        ev[1].record()
+        h13 = bsq.grouped_gemm_nvfp4(xc, xs, xo, *w13q, seg, M, row_index=ri)
+        ev[2].record()
+        hq = bsq.swiglu_quantize_nvfp4(h13)
+        ev[3].record()
+        w2q = bsq.quantize_nvfp4(w2, "tensor")
+        ev[4].record()
+        codes, scales = bsq.grouped_gemm_nvfp4_s2f6(*hq, *w2q, seg, M, signs)
+        ev[5].record()
+        bsq.rht_s2f6_combine(codes, scales, pair_row, K_TOP, signs)
+        ev[6].record()
+        torch.cuda.synchronize()
+        if it:  # the first pass is warm-up
+            for i, n in enumerate(names):
+                times[n].append(ev[i].elapsed_time(ev[i + 1]))
+    import numpy as np
+    out = {}
+    for n in names:
+        ms = float(np.median(times[n]))
+        unit, work = algo[n]
+        ach = work / (ms * 1e-3) / (1e9 if unit == "GB/s" else 1e12)
+        peak = HBM_PEAK_GBS if unit == "GB/s" else MFMA_PEAK_TFLOPS["f16"]
+        out[n] = {"ms": round(ms, 4), "achieved": round(ach, 2), "unit": unit, "peak": peak,
+                  "frac": round(ach / peak, 4)}
+    out["ms_total"] = round(sum(out[n]["ms"] for n in names), 4)
+    out["what"] = ("MoE expert forward (w13 GEMM -> SwiGLU + NVFP4 -> w2 GEMM with RHT-32 + S2F6 epilogue -> "
+                   "combine), outside the step")
+    return out
 
 
 def main():
@@ -357,6 +413,7 @@ def main():
                 "traffic": read_traffic(name, kernel_sha(*stage_sources(name))),
                 "alternative_to": "bf16 combine payload (16 bits per value; the codec carries 8.25)"}
         del payload, enc
+        alternatives["expert_chain_fwd"] = chain_forward(torch, bsq, inp, algo, dev, pair_row)
 
     if args.copy_calibration:
         src_buf = torch.empty(512 << 20, dtype=torch.uint8, device=dev).fill_(1)

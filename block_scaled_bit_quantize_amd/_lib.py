@@ -18,6 +18,7 @@ SIGNATURES = {
     "bsq_quantize_nvfp4_workspace": (c_size, [c_i64, c_i64, c_i64, c_int]),
     "bsq_quantize_nvfp4": (c_int, [c_vp, c_int, c_i64, c_i64, c_i64, c_int, c_vp, c_vp, c_vp, c_vp, c_vp,
                                    c_size, c_vp]),
+    "bsq_swiglu_quantize_nvfp4": (c_int, [c_vp, c_int, c_i64, c_i64, c_int, c_vp, c_vp, c_vp, c_vp]),
     "bsq_quantize_nvfp4_square_workspace": (c_size, [c_i64, c_i64, c_i64, c_int]),
     "bsq_quantize_nvfp4_square": (c_int, [c_vp, c_int, c_i64, c_i64, c_i64, c_int, c_vp, c_vp, c_vp, c_vp, c_vp,
                                           c_vp, c_vp, c_size, c_vp]),
@@ -29,6 +30,8 @@ SIGNATURES = {
                                          c_int, c_int, c_u64, c_u64, c_vp, c_vp, c_vp, c_vp, c_size, c_vp]),
     "bsq_grouped_gemm_nvfp4": (c_int, [c_vp, c_vp, c_vp, c_int, c_i64, c_vp, c_vp, c_vp, c_vp, c_vp, c_i64, c_i64,
                                        c_i64, c_i64, c_vp, c_int, c_vp]),
+    "bsq_grouped_gemm_nvfp4_s2f6": (c_int, [c_vp, c_vp, c_vp, c_int, c_i64, c_vp, c_vp, c_vp, c_vp, c_vp, c_i64, c_i64,
+                                            c_i64, c_i64, ctypes.c_uint32, c_vp, c_vp, c_vp]),
     "bsq_grouped_gemm_mxfp8": (c_int, [c_int, c_vp, c_vp, c_vp, c_vp, c_vp, c_i64, c_i64, c_i64, c_i64, c_vp,
                                        c_int, c_vp]),
     "bsq_grouped_gemm_mxfp8_native": (c_int, [c_int, c_vp, c_vp, c_vp, c_vp, c_vp, c_i64, c_i64, c_i64, c_i64, c_vp,

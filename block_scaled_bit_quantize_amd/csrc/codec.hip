@@ -29,37 +29,6 @@ using namespace bsqd;
 namespace {
 
 constexpr int kThreads = 256;
-constexpr uint32_t kInvSqrt32 = 0x3E3504F3u;  // float32 nearest to 1/sqrt(32)
-
-// Unnormalized Walsh-Hadamard transform of v (v H, Sylvester order).
-__device__ __forceinline__ void fwht32(float (&v)[32]) {
-#pragma unroll
-  for (int h = 1; h < 32; h <<= 1)
-#pragma unroll
-    for (int i = 0; i < 32; ++i)
-      if ((i & h) == 0) {
-        const float a = v[i], b = v[i + h];
-        v[i] = a + b;
-        v[i + h] = a - b;
-      }
-}
-
-// Smallest e with a <= (127/64) 2^e for a >= 0, clamped to [-127, 127]; -127
-// for a == 0. From the bits: a = f 2^p with f in [1, 2) rounds up to p + 1 when
-// f > 127/64, i.e. when the 23-bit fraction exceeds 63 * 2^17.
-__device__ __forceinline__ int s2f6_exponent(float a) {
-  const uint32_t bits = __float_as_uint(a);
-  const uint32_t E = bits >> 23;
-  if (E == 0) return bits > 0x7F0000u ? -126 : -127;  // subnormal: below 2^-126
-  const int e = (int)E - 127 + ((bits & 0x7FFFFFu) > 0x7E0000u ? 1 : 0);
-  return e > 127 ? 127 : e;
-}
-
-__device__ __forceinline__ uint32_t s2f6_code(float z, int sh) {
-  float y = rintf(ldexpf(z, sh));  // exact scaling, then round half to even
-  y = fminf(fmaxf(y, -128.0f), 127.0f);
-  return (uint32_t)(int)y & 0xFFu;
-}
 
 template <typename T>
 __global__ __launch_bounds__(kThreads) void k_rht_s2f6_encode(const T* __restrict__ x, int64_t nblk, uint32_t signs,
@@ -90,28 +59,12 @@ __global__ __launch_bounds__(kThreads) void k_rht_s2f6_encode(const T* __restric
       v[4 * q + 3] = __uint_as_float(w.w);
     }
   }
-#pragma unroll
-  for (int i = 0; i < 32; ++i) v[i] = __uint_as_float(__float_as_uint(v[i]) ^ (((signs >> i) & 1u) << 31));
-  fwht32(v);
-  const float c = __uint_as_float(kInvSqrt32);
-  float amax = 0.0f;
-#pragma unroll
-  for (int i = 0; i < 32; ++i) {
-    v[i] = v[i] * c;
-    amax = fmaxf(amax, fabsf(v[i]));
-  }
-  const int e = s2f6_exponent(amax);
   uint32_t w[8];
-#pragma unroll
-  for (int o = 0; o < 8; ++o) {
-    w[o] = 0;
-#pragma unroll
-    for (int i = 0; i < 4; ++i) w[o] |= s2f6_code(v[4 * o + i], 6 - e) << (8 * i);
-  }
+  const uint32_t sc = rht_s2f6_block(v, signs, w);
   uint4* dst = reinterpret_cast<uint4*>(codes + blk * 32);
   dst[0] = make_uint4(w[0], w[1], w[2], w[3]);
   dst[1] = make_uint4(w[4], w[5], w[6], w[7]);
-  scales[blk] = (uint8_t)(e + 127);
+  scales[blk] = (uint8_t)sc;
 }
 
 // Token t, block b of cols/32: sum of the dequantized blocks of rows

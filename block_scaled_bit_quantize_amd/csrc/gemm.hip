@@ -86,8 +86,12 @@ struct GemmArgs {
   int64_t M;                // M_total (segments along M) or rows per expert (WGRAD)
   int64_t N;
   int64_t K;                // shared K (segments along M)
-  void* out;
+  void* out;                // bf16 / fp32 output, or the S2F6 codes [M_total, N]
+  uint8_t* out_scales;      // S2F6 output: UE8M0 scales [M_total, N/32]
+  uint32_t signs;           // S2F6 output: the RHT's sign mask
 };
+
+enum { OUT_BF16 = 0, OUT_F32 = 1, OUT_S2F6 = 2 };
 
 struct Tile {
   int e;
@@ -172,13 +176,17 @@ __device__ bool tile_coords(const GemmArgs& g, const int64_t* s_cum, int64_t til
 }
 
 // Epilogue. The accumulators pass through LDS so that global stores are
-// whole 16-byte pieces of contiguous output rows. acc[i][j] holds tile row
+// whole 16-byte pieces of contiguous output rows. OUT_S2F6 (the w2 GEMM of
+// the expert chain, "Quantized communications": RHT and S2F6 quantization in
+// the epilogue): the fp32 rows are staged as for OUT_F32 and each thread
+// turns one 32-wide block of a row into 32 S2F6 codes and a UE8M0 scale (one
+// row per lane, so the 16-byte LDS reads of a wave hit every bank once). acc[i][j] holds tile row
 // 128 wm + 32 i + (lane & 31) and, in element 4q + u, tile column
 // 32 TJ wn + 32 j + 8 q + 4 (lane >> 5) + u. Rows past the segment (FPROP,
 // DGRAD) are not stored; NVFP4 sums take the two FP32 outer scales. `stage`
 // is the workgroup's LDS (at least 256 x 528 bytes); the caller has made sure
 // no wave still reads it.
-template <int NVFP4, int WGRAD, int OUT_F32>
+template <int NVFP4, int WGRAD, int OUT>
 __device__ __forceinline__ void store_tile(const GemmArgs& g, const Tile& tl, const f32x16 (&acc)[4][TJ], int wm,
                                            int wn, int lane, uint8_t* stage) {
   const float sw = NVFP4 ? g.b_outer[tl.e] : 1.0f;
@@ -200,7 +208,7 @@ __device__ __forceinline__ void store_tile(const GemmArgs& g, const Tile& tl, co
   }
   const int t = threadIdx.x;
   const int64_t rows_left = WGRAD ? BM : tl.Me - tl.m0;  // rows of the tile inside the segment
-  if constexpr (!OUT_F32) {
+  if constexpr (OUT == OUT_BF16) {
     // bf16 rows of 512 bytes at a 520-byte pitch (rows 2 banks apart)
     constexpr int P = BN * 2 + 8;
 #pragma unroll
@@ -253,15 +261,41 @@ __device__ __forceinline__ void store_tile(const GemmArgs& g, const Tile& tl, co
         }
       }
       __syncthreads();
+      if constexpr (OUT == OUT_F32) {
 #pragma unroll 4
-      for (int k = 0; k < 128 * 64 / kThreads; ++k) {  // 64 pieces of 16 bytes per row
-        const int id = t + k * kThreads;
-        const int r = id >> 6, c = id & 63;
-        if (half * 128 + r < rows_left) {
-          const float4 v = *reinterpret_cast<const float4*>(stage + r * P + c * 16);
-          const int64_t m = tl.m0 + half * 128 + r;
-          const int64_t orow = WGRAD ? (int64_t)tl.e * g.M + m : tl.seg0 + m;
-          *reinterpret_cast<float4*>(static_cast<float*>(g.out) + orow * g.N + tl.n0 + c * 4) = v;
+        for (int k = 0; k < 128 * 64 / kThreads; ++k) {  // 64 pieces of 16 bytes per row
+          const int id = t + k * kThreads;
+          const int r = id >> 6, c = id & 63;
+          if (half * 128 + r < rows_left) {
+            const float4 v = *reinterpret_cast<const float4*>(stage + r * P + c * 16);
+            const int64_t m = tl.m0 + half * 128 + r;
+            const int64_t orow = WGRAD ? (int64_t)tl.e * g.M + m : tl.seg0 + m;
+            *reinterpret_cast<float4*>(static_cast<float*>(g.out) + orow * g.N + tl.n0 + c * 4) = v;
+          }
+        }
+      } else {
+        for (int k = 0; k < 128 * (BN / 32) / kThreads; ++k) {  // 8 blocks of 32 per row
+          const int id = t + k * kThreads;
+          const int r = id & 127, b = id >> 7;
+          if (half * 128 + r < rows_left) {
+            float v[32];
+            const float4* src = reinterpret_cast<const float4*>(stage + r * P + b * 128);
+#pragma unroll
+            for (int q = 0; q < 8; ++q) {
+              const float4 f = src[q];
+              v[4 * q] = f.x;
+              v[4 * q + 1] = f.y;
+              v[4 * q + 2] = f.z;
+              v[4 * q + 3] = f.w;
+            }
+            uint32_t w[8];
+            const uint32_t sc = rht_s2f6_block(v, g.signs, w);
+            const int64_t orow = tl.seg0 + tl.m0 + half * 128 + r;
+            uint4* dst = reinterpret_cast<uint4*>(static_cast<uint8_t*>(g.out) + orow * g.N + tl.n0 + b * 32);
+            dst[0] = make_uint4(w[0], w[1], w[2], w[3]);
+            dst[1] = make_uint4(w[4], w[5], w[6], w[7]);
+            g.out_scales[orow * (g.N / 32) + tl.n0 / 32 + b] = (uint8_t)sc;
+          }
         }
       }
     }
@@ -397,7 +431,7 @@ __device__ __forceinline__ f32x16 mfma16(bf16x8 b, bf16x8 a, f32x16 acc) {
 // (workgroup w runs on XCD w % 8, so each XCD works on a contiguous range of
 // tiles: an expert's weights and token rows stay in that XCD's L2), with one
 // segment scan per workgroup and no launch or scan cost per tile.
-template <int FMT, int WGRAD, int OUT_F32>
+template <int FMT, int WGRAD, int OUT>
 __global__ __launch_bounds__(kThreads) void k_gemm(const GemmArgs g) {
   static_assert(BM == BN, "A and B LDS buffers share one layout");
   static_assert(2 * BM % (kThreads / Slab<FMT>::CPR) == 0, "whole slab rows per thread");
@@ -518,7 +552,7 @@ __global__ __launch_bounds__(kThreads) void k_gemm(const GemmArgs g) {
     if (kt < nk) step(kt, r0, r1);
 
     __syncthreads();  // every wave is done with the operand buffers
-    store_tile<FMT == FMT_NVFP4, WGRAD, OUT_F32>(g, tl, acc, wm, wn, lane, lds0);
+    store_tile<FMT == FMT_NVFP4, WGRAD, OUT>(g, tl, acc, wm, wn, lane, lds0);
     __syncthreads();  // the staging reads are done before the next tile decodes into LDS
   }
 #undef BSQ_LOAD_FRAGS
@@ -529,10 +563,16 @@ int launch(const GemmArgs& a, int64_t slots, int out_dtype, hipStream_t s) {
   const int64_t cus = (bsqh::device_cus() + kXcds - 1) / kXcds * kXcds;
   int64_t grid = (slots + kXcds - 1) / kXcds * kXcds;
   if (grid > cus) grid = cus;
+  if constexpr (FMT == FMT_NVFP4 && !WGRAD) {
+    if (out_dtype == OUT_S2F6) {
+      hipLaunchKernelGGL((k_gemm<FMT, WGRAD, OUT_S2F6>), dim3((unsigned)grid), dim3(kThreads), 0, s, a);
+      return bsqh::launch_status();
+    }
+  }
   if (out_dtype == BSQ_F32)
-    hipLaunchKernelGGL((k_gemm<FMT, WGRAD, 1>), dim3((unsigned)grid), dim3(kThreads), 0, s, a);
+    hipLaunchKernelGGL((k_gemm<FMT, WGRAD, OUT_F32>), dim3((unsigned)grid), dim3(kThreads), 0, s, a);
   else
-    hipLaunchKernelGGL((k_gemm<FMT, WGRAD, 0>), dim3((unsigned)grid), dim3(kThreads), 0, s, a);
+    hipLaunchKernelGGL((k_gemm<FMT, WGRAD, OUT_BF16>), dim3((unsigned)grid), dim3(kThreads), 0, s, a);
   return bsqh::launch_status();
 }
 
@@ -552,8 +592,28 @@ extern "C" int bsq_grouped_gemm_nvfp4(const uint8_t* a_codes, const uint8_t* a_s
   BSQ_REQUIRE(bsqh::aligned16(a_codes) && bsqh::aligned16(b_codes) && bsqh::aligned16(out), BSQ_E_ALIGN);
   BSQ_REQUIRE(((uintptr_t)a_scales & 3) == 0 && ((uintptr_t)b_scales & 3) == 0, BSQ_E_ALIGN);
   const GemmArgs a{a_codes, a_scales, a_outer, a_outer_per_row, a_rows, a_row_index, b_codes, b_scales, b_outer,
-                   seg_offsets, (int)E, M_total, N, K, out};
+                   seg_offsets, (int)E, M_total, N, K, out, nullptr, 0u};
   return launch<FMT_NVFP4, 0>(a, bsqh::tile_bound(M_total, E, BM) * (N / BN), out_dtype, bsqh::as_stream(stream));
+}
+
+extern "C" int bsq_grouped_gemm_nvfp4_s2f6(const uint8_t* a_codes, const uint8_t* a_scales, const float* a_outer,
+                                           int a_outer_per_row, int64_t a_rows, const int32_t* a_row_index,
+                                           const uint8_t* b_codes, const uint8_t* b_scales, const float* b_outer,
+                                           const int64_t* seg_offsets, int64_t E, int64_t M_total, int64_t N,
+                                           int64_t K, uint32_t signs, uint8_t* out_codes, uint8_t* out_scales,
+                                           bsq_stream_t stream) {
+  BSQ_REQUIRE(E >= 1 && E <= kMaxE && M_total >= 0 && N >= 0 && K >= 0 && a_rows >= 0, BSQ_E_SHAPE);
+  BSQ_REQUIRE(N % BN == 0 && K % BK == 0, BSQ_E_SHAPE);
+  if (M_total == 0 || N == 0) return BSQ_OK;
+  BSQ_REQUIRE(K > 0 && a_rows > 0, BSQ_E_SHAPE);
+  BSQ_REQUIRE(a_codes && a_scales && a_outer && b_codes && b_scales && b_outer && seg_offsets && out_codes &&
+                  out_scales,
+              BSQ_E_NULL);
+  BSQ_REQUIRE(bsqh::aligned16(a_codes) && bsqh::aligned16(b_codes) && bsqh::aligned16(out_codes), BSQ_E_ALIGN);
+  BSQ_REQUIRE(((uintptr_t)a_scales & 3) == 0 && ((uintptr_t)b_scales & 3) == 0, BSQ_E_ALIGN);
+  const GemmArgs a{a_codes, a_scales, a_outer, a_outer_per_row, a_rows, a_row_index, b_codes, b_scales, b_outer,
+                   seg_offsets, (int)E, M_total, N, K, out_codes, out_scales, signs};
+  return launch<FMT_NVFP4, 0>(a, bsqh::tile_bound(M_total, E, BM) * (N / BN), OUT_S2F6, bsqh::as_stream(stream));
 }
 
 extern "C" int bsq_grouped_gemm_mxfp8(int wgrad, const uint8_t* a_codes, const uint8_t* a_scales,
@@ -571,7 +631,7 @@ extern "C" int bsq_grouped_gemm_mxfp8(int wgrad, const uint8_t* a_codes, const u
   BSQ_REQUIRE(a_codes && a_scales && b_codes && b_scales && seg_offsets && out, BSQ_E_NULL);
   BSQ_REQUIRE(bsqh::aligned16(a_codes) && bsqh::aligned16(b_codes) && bsqh::aligned16(out), BSQ_E_ALIGN);
   const GemmArgs a{a_codes, a_scales, nullptr, 0, M_total, nullptr, b_codes, b_scales, nullptr,
-                   seg_offsets, (int)E, M_total, N, K, out};
+                   seg_offsets, (int)E, M_total, N, K, out, nullptr, 0u};
   hipStream_t s = bsqh::as_stream(stream);
   if (wgrad) return launch<FMT_MXFP8, 1>(a, E * (M_total / BM) * (N / BN), out_dtype, s);
   return launch<FMT_MXFP8, 0>(a, bsqh::tile_bound(M_total, E, BM) * (N / BN), out_dtype, s);

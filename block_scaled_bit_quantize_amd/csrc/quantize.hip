@@ -14,6 +14,7 @@
 // with one 8- or 16-byte store. Per-row outer scales reduce across the threads
 // of a row; per-tensor outer scales take a separate max pass over the tensor.
 #include <cstdlib>
+#include <type_traits>
 
 #include "bsq_device.h"
 #include "bsq_internal.h"
@@ -204,9 +205,50 @@ __device__ __forceinline__ void nvfp4_block(const Blk16<T>& b, float am, float s
   *scale_dst = (uint8_t)sc;
 }
 
+// e^x in float32 (Cody and Waite's reduction, degree-7 Taylor polynomial):
+// n = round-half-even(f32(x * f32(1/ln 2))) clamped to [-300, 300],
+// r = f32(f32(x - n ln2_hi) - f32(n ln2_lo)) with ln2_hi = 0.693145751953125
+// (n ln2_hi exact), p(r) = sum r^k / k! in Horner form, each product and sum
+// rounded separately (no fused operations), e^x = p 2^n; within 1.2 ulp.
+__device__ __forceinline__ float exp_cw(float x) {
+  constexpr double kLn2 = 0.69314718055994530942;
+  constexpr double c2 = 1.0 / 2, c3 = c2 / 3, c4 = c3 / 4, c5 = c4 / 5, c6 = c5 / 6, c7 = c6 / 7;
+  float n = rintf(__fmul_rn(x, (float)(1.0 / kLn2)));
+  n = fminf(fmaxf(n, -300.0f), 300.0f);
+  float r = __fsub_rn(x, __fmul_rn(n, 0.693145751953125f));
+  r = __fsub_rn(r, __fmul_rn(n, (float)(kLn2 - 0.693145751953125)));
+  float p = (float)c7;
+  p = __fadd_rn(__fmul_rn(p, r), (float)c6);
+  p = __fadd_rn(__fmul_rn(p, r), (float)c5);
+  p = __fadd_rn(__fmul_rn(p, r), (float)c4);
+  p = __fadd_rn(__fmul_rn(p, r), (float)c3);
+  p = __fadd_rn(__fmul_rn(p, r), (float)c2);
+  p = __fadd_rn(__fmul_rn(p, r), 1.0f);
+  p = __fadd_rn(__fmul_rn(p, r), 1.0f);
+  return ldexpf(p, (int)n);
+}
+
+// SwiGLU of 16 gate and 16 up values: silu(g) * u, silu(g) = g / (1 + e^-g),
+// every step rounded to float32.
+template <typename T>
+__device__ __forceinline__ void swiglu16(const T* gate, const T* up, Blk16<float>& out) {
+  Blk16<T> g, u;
+  g.load(gate);
+  u.load(up);
+#pragma unroll
+  for (int i = 0; i < 16; ++i) {
+    const float gi = g.get(i);
+    const float s = gi / __fadd_rn(1.0f, exp_cw(-gi));
+    out.w[i] = __fmul_rn(s, u.get(i));
+  }
+}
+
 // NVFP4 round-to-nearest quantization of rows [row0, row_end). TPR threads
 // share a row; each owns up to MAXB blocks of 16 (block j = lane + k*TPR).
-template <typename T, int TPR, int MAXB, int MODE, bool FS>
+// GLU: a row of x holds 2C values, gate [0, C) and up [C, 2C); the quantized
+// values are their SwiGLU (the quantization step between the w13 and w2 GEMMs
+// of the expert chain).
+template <typename T, int TPR, int MAXB, int MODE, bool FS, bool GLU = false>
 __global__ __launch_bounds__(kThreads) void k_quant_nvfp4(
     const T* __restrict__ x, int64_t row0, int64_t row_end, int64_t rows_per_item, int64_t C,
     const float* __restrict__ outer_in, const uint32_t* __restrict__ amax_bits,
@@ -218,7 +260,8 @@ __global__ __launch_bounds__(kThreads) void k_quant_nvfp4(
   const bool row_ok = row < row_end;
   const int64_t nb = C >> 4;
 
-  Blk16<T> blk[MAXB];
+  typedef typename std::conditional<GLU, Blk16<float>, Blk16<T>>::type Blk;
+  Blk blk[MAXB];
   float am[MAXB];
   float rmax = 0.0f;
 #pragma unroll
@@ -226,7 +269,10 @@ __global__ __launch_bounds__(kThreads) void k_quant_nvfp4(
     const int64_t j = tl + (int64_t)k * TPR;
     am[k] = 0.0f;
     if (row_ok && j < nb) {
-      blk[k].load(x + row * C + j * 16);
+      if constexpr (GLU)
+        swiglu16(x + row * 2 * C + j * 16, x + row * 2 * C + C + j * 16, blk[k]);
+      else
+        blk[k].load(x + row * C + j * 16);
       am[k] = blk[k].absmax();
       rmax = fmaxf(rmax, am[k]);
     }
@@ -428,15 +474,15 @@ __global__ __launch_bounds__(kThreads) void k_mxfp8_rows(const T* __restrict__ x
 
 inline unsigned grid1(int64_t n, int t = kThreads) { return (unsigned)((n + t - 1) / t); }
 
-template <typename T, int MODE, bool FS>
+template <typename T, int MODE, bool FS, bool GLU = false>
 int launch_quant(const T* x, int64_t row0, int64_t row_end, int64_t R, int64_t C, const float* outer_in,
                  const uint32_t* amax, uint8_t* codes, uint8_t* scales, float* outer_out, hipStream_t s) {
   const int64_t nb = C / 16;
   const int64_t n = row_end - row0;
   if (n <= 0) return BSQ_OK;
-#define BSQ_QL(TPR, MAXB)                                                                          \
-  hipLaunchKernelGGL((k_quant_nvfp4<T, TPR, MAXB, MODE, FS>), dim3(grid1(n, kThreads / TPR)), dim3(kThreads), 0, s, \
-                     x, row0, row_end, R, C, outer_in, amax, codes, scales, outer_out)
+#define BSQ_QL(TPR, MAXB)                                                                                      \
+  hipLaunchKernelGGL((k_quant_nvfp4<T, TPR, MAXB, MODE, FS, GLU>), dim3(grid1(n, kThreads / TPR)), dim3(kThreads), 0, \
+                     s, x, row0, row_end, R, C, outer_in, amax, codes, scales, outer_out)
   // one wave per row up to 512 blocks (the row maximum is a wave reduction),
   // up to 8 blocks (256 bytes of bf16) in flight per thread
   if (nb <= 16) BSQ_QL(16, 1);
@@ -897,4 +943,36 @@ extern "C" int bsq_quantize_nvfp4_square(const void* x, int dtype, int64_t batch
                                              static_cast<uint32_t*>(ws), s);
   return quantize_nvfp4_square_t<float>(static_cast<const float*>(x), batch, rows, cols, mode, outer_in, codes,
                                         scales, codes_t, scales_t, outer_out, static_cast<uint32_t*>(ws), s);
+}
+
+extern "C" int bsq_swiglu_quantize_nvfp4(const void* h13, int dtype, int64_t rows, int64_t ffn, int flags,
+                                         uint8_t* codes, uint8_t* scales, float* outer_out, bsq_stream_t stream) {
+  BSQ_REQUIRE(dtype == BSQ_F32 || dtype == BSQ_BF16, BSQ_E_DTYPE);
+  BSQ_REQUIRE((flags & ~BSQ_NVFP4_FOUR_OVER_SIX) == 0, BSQ_E_ENUM);
+  BSQ_REQUIRE(rows >= 0 && ffn >= 0 && ffn % 16 == 0 && ffn <= 32768, BSQ_E_SHAPE);
+  if (rows == 0 || ffn == 0) {
+    if (rows > 0) {  // empty rows: outer scale 1
+      BSQ_REQUIRE(outer_out, BSQ_E_NULL);
+      hipLaunchKernelGGL(k_fill_u32, dim3(grid1(rows)), dim3(kThreads), 0, bsqh::as_stream(stream),
+                         reinterpret_cast<uint32_t*>(outer_out), 0x3F800000u, rows);
+      return bsqh::launch_status();
+    }
+    return BSQ_OK;
+  }
+  BSQ_REQUIRE(h13 && codes && scales && outer_out, BSQ_E_NULL);
+  BSQ_REQUIRE(bsqh::aligned16(h13) && bsqh::aligned16(codes) && ((uintptr_t)outer_out & 3) == 0, BSQ_E_ALIGN);
+  hipStream_t s = bsqh::as_stream(stream);
+  const bool fs = (flags & BSQ_NVFP4_FOUR_OVER_SIX) != 0;
+  if (dtype == BSQ_BF16) {
+    const uint16_t* p = static_cast<const uint16_t*>(h13);
+    return fs ? launch_quant<uint16_t, BSQ_OUTER_ROW, true, true>(p, 0, rows, rows, ffn, nullptr, nullptr, codes,
+                                                                  scales, outer_out, s)
+              : launch_quant<uint16_t, BSQ_OUTER_ROW, false, true>(p, 0, rows, rows, ffn, nullptr, nullptr, codes,
+                                                                   scales, outer_out, s);
+  }
+  const float* p = static_cast<const float*>(h13);
+  return fs ? launch_quant<float, BSQ_OUTER_ROW, true, true>(p, 0, rows, rows, ffn, nullptr, nullptr, codes, scales,
+                                                             outer_out, s)
+            : launch_quant<float, BSQ_OUTER_ROW, false, true>(p, 0, rows, rows, ffn, nullptr, nullptr, codes, scales,
+                                                              outer_out, s);
 }

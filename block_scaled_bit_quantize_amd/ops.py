@@ -64,6 +64,26 @@ def quantize_nvfp4(x, mode="tensor", outer_in=None, four_over_six=False):
     return codes, scales, outer
 
 
+def swiglu_quantize_nvfp4(h13, four_over_six=True):
+    """The expert chain's quantization step: h13 [M, 2F] (float32 or bfloat16,
+    gate columns first) -> NVFP4 of silu(gate) * up with per-row outer scales:
+    (codes u8 [M, F/2], scales u8 [M, F/16], outer f32 [M])."""
+    lib = load_library()
+    _dev(h13)
+    M, F2 = h13.shape
+    F = F2 // 2
+    dt = {torch.float32: F32, torch.bfloat16: BF16}.get(h13.dtype)
+    if dt is None:
+        raise BsqError("h13 must be float32 or bfloat16")
+    codes = torch.empty((M, F // 2), dtype=torch.uint8, device=h13.device)
+    scales = torch.empty((M, F // 16), dtype=torch.uint8, device=h13.device)
+    outer = torch.empty((M,), dtype=torch.float32, device=h13.device)
+    check(lib.bsq_swiglu_quantize_nvfp4(h13.data_ptr(), dt, M, F, FOUR_OVER_SIX if four_over_six else 0,
+                                        codes.data_ptr(), scales.data_ptr(), outer.data_ptr(), _stream()),
+          "bsq_swiglu_quantize_nvfp4")
+    return codes, scales, outer
+
+
 def quantize_nvfp4_square(x, mode="tensor", outer_in=None, transpose=True):
     """Square-tile NVFP4 (one scale per 16x16 tile) of x [B, R, C] or [R, C]
     (float32 or bfloat16; R and C multiples of 16); mode "tensor" or "given".
@@ -210,6 +230,26 @@ def grouped_gemm_nvfp4(a_codes, a_scales, a_outer, b_codes, b_scales, b_outer, s
                                      seg_offsets.data_ptr(), E, M_total, N, 2 * K2, out.data_ptr(), _OUT[out.dtype],
                                      _stream()), "bsq_grouped_gemm_nvfp4")
     return out
+
+
+def grouped_gemm_nvfp4_s2f6(a_codes, a_scales, a_outer, b_codes, b_scales, b_outer, seg_offsets, M_total, signs,
+                            row_index=None):
+    """The w2 GEMM with the combine codec in its epilogue: the product of
+    grouped_gemm_nvfp4, RHT-rotated and S2F6-quantized per 32 columns ->
+    (codes u8 [M_total, N], scales u8 [M_total, N/32])."""
+    lib = load_library()
+    _dev(a_codes, a_scales, a_outer, b_codes, b_scales, b_outer, seg_offsets, row_index)
+    T, K2 = a_codes.shape
+    E, N, _ = b_codes.shape
+    per_row = 1 if a_outer.numel() == T and T > 1 else 0
+    codes = torch.empty((M_total, N), dtype=torch.uint8, device=a_codes.device)
+    scales = torch.empty((M_total, N // 32), dtype=torch.uint8, device=a_codes.device)
+    check(lib.bsq_grouped_gemm_nvfp4_s2f6(a_codes.data_ptr(), a_scales.data_ptr(), a_outer.data_ptr(), per_row, T,
+                                          _ptr(row_index), b_codes.data_ptr(), b_scales.data_ptr(),
+                                          b_outer.data_ptr(), seg_offsets.data_ptr(), E, M_total, N, 2 * K2,
+                                          signs & 0xFFFFFFFF, codes.data_ptr(), scales.data_ptr(), _stream()),
+          "bsq_grouped_gemm_nvfp4_s2f6")
+    return codes, scales
 
 
 def grouped_gemm_mxfp8(wgrad, a_codes, a_scales, b_codes, b_scales, seg_offsets, M, N, K=0, out=None,

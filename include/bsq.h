@@ -105,6 +105,28 @@ int bsq_quantize_nvfp4(const void* x, int dtype, int64_t batch, int64_t rows, in
                        float* outer_out, void* ws, size_t ws_bytes, bsq_stream_t stream);
 
 /* ------------------------------------------------------------------------
+ * The quantization step of the expert chain ("Quantized communications",
+ * Figure 5: w13 GEMM, quantize, w2 GEMM): SwiGLU of the w13 output, then
+ * NVFP4 with one outer scale per row (a dispatched token row), as
+ * bsq_quantize_nvfp4 with BSQ_OUTER_ROW.
+ *
+ * h13      [rows, 2*ffn] of `dtype` (F32 or BF16): gate columns [0, ffn), up
+ *          columns [ffn, 2*ffn).
+ * flags    0 or BSQ_NVFP4_FOUR_OVER_SIX.
+ * codes    [rows, ffn/2] u8; scales [rows, ffn/16] u8; outer_out [rows] FP32.
+ * h = silu(g) * u with silu(g) = g / (1 + e^-g), each step rounded to float32;
+ * e^x = p(r) 2^n with n = round-half-even(f32(x * f32(1/ln 2))) clamped to
+ * [-300, 300], r = f32(f32(x - n * 0.693145751953125) - f32(n * f32(ln 2 -
+ * 0.693145751953125))) and p(r) = sum_{k<=7} r^k/k! in Horner form with every
+ * product and sum rounded separately (coefficients f32 of c_k = c_(k-1)/k
+ * formed in double precision).
+ * ffn % 16 == 0, ffn <= 32768. h13 and codes 16-byte aligned, outer_out 4.
+ * Errors: NULL, SHAPE, ALIGN, DTYPE, ENUM, LAUNCH.
+ * ---------------------------------------------------------------------- */
+int bsq_swiglu_quantize_nvfp4(const void* h13, int dtype, int64_t rows, int64_t ffn, int flags,
+                              uint8_t* codes, uint8_t* scales, float* outer_out, bsq_stream_t stream);
+
+/* ------------------------------------------------------------------------
  * Square-tile NVFP4 quantization ("Block-scaled backward passes": the
  * alternative the pages compare against, one scale per 16x16 tile, shown in
  * the row-vs-column and outlier figures). Because the tile is square, the
@@ -237,6 +259,22 @@ int bsq_grouped_gemm_nvfp4(const uint8_t* a_codes, const uint8_t* a_scales, cons
                            const uint8_t* b_codes, const uint8_t* b_scales, const float* b_outer,
                            const int64_t* seg_offsets, int64_t E, int64_t M_total, int64_t N,
                            int64_t K, void* out, int out_dtype, bsq_stream_t stream);
+
+/* The w2 GEMM of the expert chain with the combine codec in its epilogue
+ * ("Quantized communications": the RHT and S2F6 quantization run in the
+ * epilogue of the w2 grouped GEMM): the same product as
+ * bsq_grouped_gemm_nvfp4 (float32 sums times the two outer scales), written
+ * as bsq_rht_s2f6_encode would encode its float32 output:
+ *   out_codes  [M_total, N] u8 (S2F6), out_scales [M_total, N/32] u8 (UE8M0),
+ *   signs      the RHT's sign mask.
+ * Rows past a segment's end are not written. Arguments, limits and errors
+ * otherwise as bsq_grouped_gemm_nvfp4 (out_codes 16-byte aligned). */
+int bsq_grouped_gemm_nvfp4_s2f6(const uint8_t* a_codes, const uint8_t* a_scales, const float* a_outer,
+                                int a_outer_per_row, int64_t a_rows, const int32_t* a_row_index,
+                                const uint8_t* b_codes, const uint8_t* b_scales, const float* b_outer,
+                                const int64_t* seg_offsets, int64_t E, int64_t M_total, int64_t N,
+                                int64_t K, uint32_t signs, uint8_t* out_codes, uint8_t* out_scales,
+                                bsq_stream_t stream);
 
 /* ------------------------------------------------------------------------
  * MXFP8 expert grouped GEMMs of the backward pass (quantized linear layer

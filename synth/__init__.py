@@ -14,6 +14,9 @@ Workloads (data seed 1000 + workload number, one PCG64 sub-stream per tensor):
   5 large skewed forward: x bf16 [65536, 7168] ~ Student-t(3);
     W bf16 [128, 2048, 7168] ~ N(0, 0.02); top-8 of 128 experts with Zipf(1.1)
     popularity.
+Expert chain (w13 GEMM, SwiGLU, w2 GEMM) at workload 2's sizes: w13 bf16
+    [64, 3072, 4096] (gate rows, then up rows) and w2 bf16 [64, 4096, 1536],
+    both ~ N(0, 0.02).
 Combine payload (the expert output rows that the combine codec carries):
     workload 2's dispatched rows, bf16 [131072, 4096] ~ N(0, 1), 0.1% of
     entries scaled by 20 (outliers).
@@ -152,3 +155,15 @@ def combine_rows(rows, cols, workload=2):
         v[spike] *= np.float32(20.0)
         out[s:s + m] = bf16_bits(v)
     return out.reshape(rows, cols)
+
+
+def moe_w13(workload=2):
+    """Gate and up projections bf16 [E, 2 * ffn, hidden] ~ N(0, w_std^2)."""
+    p = WORKLOADS[workload]
+    return normal_bf16((p["experts"], 2 * p["ffn"], p["hidden"]), p["w_std"], rng_for(workload, 5))
+
+
+def moe_w2(workload=2):
+    """Down projections bf16 [E, hidden, ffn] ~ N(0, w_std^2)."""
+    p = WORKLOADS[workload]
+    return normal_bf16((p["experts"], p["hidden"], p["ffn"]), p["w_std"], rng_for(workload, 6))

@@ -1,0 +1,170 @@
+"""GPU parity of the expert chain's new steps (SwiGLU + per-row NVFP4; the w2
+GEMM with the RHT + S2F6 codec in its epilogue) and of the whole chain
+against the oracle."""
+import numpy as np
+import pytest
+import torch
+
+import block_scaled_bit_quantize_amd as bsq
+import synth
+from oracle import chain as CH
+from oracle import codec as CODEC
+from oracle import quant as Q
+from oracle.gemm import ABS_FLOOR, REL_TOL, grouped_gemm_nvfp4_ref
+from oracle.route import route as oroute
+
+from _gpu_util import DEV, bf16_t, h, log, t
+
+pytestmark = pytest.mark.gpu
+f32 = np.float32
+
+
+def _h13(rng, M, F, kind):
+    g = rng.standard_normal((M, F))
+    u = rng.standard_normal((M, F))
+    if kind == "wide":
+        g *= np.exp(rng.uniform(-6, 5, (M, F)))      # exp overflow / underflow paths: |g| up to ~150
+        u *= np.exp(rng.uniform(-20, 20, (M, F)))
+    if kind == "zeros":
+        g[::3] = 0.0
+        u[1::3] = 0.0
+    return np.concatenate([g, u], axis=1).astype(f32)
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+@pytest.mark.parametrize("fs", [True, False])
+@pytest.mark.parametrize("M,F,kind", [(1, 16, "normal"), (7, 48, "wide"), (33, 1536, "normal"), (5, 4096, "wide"),
+                                      (9, 256, "zeros"), (300, 112, "normal")])
+def test_swiglu_quantize_small(dtype, fs, M, F, kind):
+    log(f"swiglu_quantize {dtype} fs={fs} M={M} F={F} {kind}")
+    rng = np.random.default_rng(hash((dtype, fs, M, F, kind)) % 2**32)
+    x = _h13(rng, M, F, kind)
+    if dtype == "bf16":
+        bits = synth.bf16_bits(x)
+        x = synth.bf16_to_f32(bits).reshape(x.shape)
+        xd = bf16_t(bits.reshape(x.shape))
+    else:
+        xd = t(x)
+    gc, gs, go = bsq.swiglu_quantize_nvfp4(xd, four_over_six=fs)
+    hh = CH.swiglu_f32(x, F)
+    oc, os_, oo = Q.quantize_nvfp4(hh[None], Q.OUTER_ROW, four_over_six=fs)
+    assert np.array_equal(h(go), np.asarray(oo).reshape(-1))
+    assert np.array_equal(h(gs), os_[0]) and np.array_equal(h(gc), oc[0])
+
+
+def _nvfp4_operands(rng, T, K, E, N, seg):
+    x = rng.standard_normal((T, K)).astype(f32)
+    w = (rng.standard_normal((E, N, K)) * 0.05).astype(f32)
+    xc, xs, xo = Q.quantize_nvfp4(x[None], Q.OUTER_ROW, four_over_six=True)
+    wc, ws, wo = Q.quantize_nvfp4(w, Q.OUTER_TENSOR)
+    return (xc[0], xs[0], np.asarray(xo).reshape(-1)), (wc, ws, wo)
+
+
+def _check_codec_against_f64(codes, scales, y_ref, y_abs, mask):
+    """Decoded GPU codes against the float64 rotation of the exact product:
+    within half a step plus the L2 norm of the block's GEMM accept bounds (the
+    rotation is orthonormal); scales equal except one step near a boundary."""
+    z = CODEC.rht_f64(y_ref, mask)
+    dz = np.sqrt(((REL_TOL * np.abs(y_ref) + ABS_FLOOR * y_abs) ** 2).reshape(-1, 32).sum(axis=1))
+    e_gpu = scales.astype(np.int64).reshape(-1) - 127
+    amax = np.abs(z).reshape(-1, 32).max(axis=1)
+    e_ref = CODEC.s2f6_exponent(amax.astype(f32))
+    near = (np.abs(amax - 127 / 64 * np.exp2(e_ref.astype(np.float64))) <= dz) | \
+           (np.abs(amax - 127 / 64 * np.exp2(e_ref - 1.0)) <= dz)
+    assert (np.abs(e_gpu - e_ref) <= 1).all() and (e_gpu[~near] == e_ref[~near]).all()
+    v = CODEC.s2f6_dequantize(codes, scales).astype(np.float64).reshape(-1, 32)
+    step = np.exp2(e_gpu - 6.0)
+    bound = step[:, None] / 2 + dz[:, None] + 1e-30
+    assert (np.abs(v - z.reshape(-1, 32)) <= bound * 1.0001).all()
+
+
+@pytest.mark.parametrize("seg_list,N,K", [([0, 37, 37, 300], 256, 128), ([0, 1, 257, 513, 600], 512, 64),
+                                          ([0, 700], 256, 320)])
+def test_gemm_s2f6_epilogue(seg_list, N, K):
+    """The w2 GEMM with the codec epilogue: codes against the float64 product
+    (tolerance above), and bit for bit the encoder applied to the same GEMM's
+    float32 output (the staging of the two epilogues is the same)."""
+    log(f"gemm_s2f6 seg={seg_list} N={N} K={K}")
+    rng = np.random.default_rng(len(seg_list) * 1000 + N + K)
+    E = len(seg_list) - 1
+    M = seg_list[-1]
+    (xc, xs, xo), (wc, ws, wo) = _nvfp4_operands(rng, M, K, E, N, seg_list)
+    seg = np.asarray(seg_list, np.int64)
+    mask = int(rng.integers(0, 2**32))
+    args = (t(xc), t(xs), t(xo), t(wc), t(ws), t(wo), t(seg), M)
+    gc, gs = bsq.grouped_gemm_nvfp4_s2f6(*args, mask)
+    y32 = bsq.grouped_gemm_nvfp4(*args, out_dtype=torch.float32)
+    ec, es = bsq.rht_s2f6_encode(y32, mask)
+    assert torch.equal(gc, ec) and torch.equal(gs, es)
+    y_ref, y_abs = grouped_gemm_nvfp4_ref(xc, xs, xo, None, wc, ws, wo, seg)
+    _check_codec_against_f64(h(gc), h(gs), y_ref, y_abs, mask)
+
+
+def _run_chain_gpu(x_bits, ids, w13_bits, w2_bits, E, mask):
+    T, k = ids.shape
+    ri, seg, pair_row = bsq.route(t(ids), E)
+    xc, xs, xo = bsq.quantize_nvfp4(bf16_t(x_bits), "row", four_over_six=True)
+    w13c, w13s, w13o = bsq.quantize_nvfp4(bf16_t(w13_bits), "tensor")
+    w2c, w2s, w2o = bsq.quantize_nvfp4(bf16_t(w2_bits), "tensor")
+    M = T * k
+    h13 = bsq.grouped_gemm_nvfp4(xc, xs, xo, w13c, w13s, w13o, seg, M, row_index=ri)
+    hc, hs, ho = bsq.swiglu_quantize_nvfp4(h13)
+    codes, scales = bsq.grouped_gemm_nvfp4_s2f6(hc, hs, ho, w2c, w2s, w2o, seg, M, mask)
+    return bsq.rht_s2f6_combine(codes, scales, pair_row, k, mask, out_dtype=torch.float32)
+
+
+def test_chain_small_end_to_end():
+    """The whole chain on the GPU against the oracle chain and against the
+    float64 forward of the dequantized operands (the oracle's own pin bound)."""
+    log("chain small")
+    rng = np.random.default_rng(5)
+    T, H, F, E, k = 256, 256, 256, 4, 2
+    mask = 0x2468ACE1
+    x_bits = synth.bf16_bits(rng.standard_normal((T, H)).astype(f32))
+    w13_bits = synth.bf16_bits((rng.standard_normal((E, 2 * F, H)) * 0.06).astype(f32))
+    w2_bits = synth.bf16_bits((rng.standard_normal((E, H, F)) * 0.06).astype(f32))
+    ids = np.stack([rng.choice(E, k, replace=False) for _ in range(T)]).astype(np.int32)
+    out = h(_run_chain_gpu(x_bits, ids, w13_bits, w2_bits, E, mask))
+    x, w13, w2 = (synth.bf16_to_f32(b).reshape(b.shape) for b in (x_bits, w13_bits, w2_bits))
+    r = CH.expert_forward(x, ids, w13, w2, mask)
+    rel = lambda a, b: np.linalg.norm(a - b) / np.linalg.norm(b)
+    assert rel(out, r["out"]) < 0.03
+    xd = Q.dequantize_nvfp4_f64(r["x_q"][0][None], r["x_q"][1][None], r["x_q"][2][None], Q.OUTER_ROW)[0]
+    w13d = Q.dequantize_nvfp4_f64(*r["w13_q"], Q.OUTER_TENSOR)
+    w2d = Q.dequantize_nvfp4_f64(*r["w2_q"], Q.OUTER_TENSOR)
+    ref = np.zeros((T, H))
+    for tt in range(T):
+        for e in ids[tt]:
+            g_u = w13d[e] @ xd[tt]
+            ref[tt] += w2d[e] @ (g_u[:F] / (1 + np.exp(-g_u[:F])) * g_u[F:])
+    assert rel(out, ref) < 0.12
+
+
+def test_chain_workload2_full():
+    """The chain at full size (16384 tokens, hidden 4096, ffn 1536, 64 experts,
+    top-8): sampled tokens against the oracle run on just their experts."""
+    log("chain workload2 full")
+    T, H, F, E, k = 16384, 4096, 1536, 64, 8
+    mask = 0x13579BDF
+    x_bits = synth.moe_activations(2)
+    ids = synth.moe_routing(2)
+    w13_bits = synth.moe_w13(2)
+    w2_bits = synth.moe_w2(2)
+    out = _run_chain_gpu(x_bits, ids, w13_bits, w2_bits, E, mask)
+    toks = np.r_[0, 12345]
+    got = h(out[toks])
+    for n, tt in enumerate(toks):
+        xq = Q.quantize_nvfp4(synth.bf16_to_f32(x_bits[tt:tt + 1])[None], Q.OUTER_ROW, four_over_six=True)
+        agg = np.zeros(H, f32)
+        for e in ids[tt]:
+            w13c, w13s, w13o = Q.quantize_nvfp4(synth.bf16_to_f32(w13_bits[e])[None], Q.OUTER_TENSOR)
+            w2c, w2s, w2o = Q.quantize_nvfp4(synth.bf16_to_f32(w2_bits[e])[None], Q.OUTER_TENSOR)
+            seg1 = np.array([0, 1])
+            h13, _ = grouped_gemm_nvfp4_ref(xq[0][0], xq[1][0], np.asarray(xq[2]).reshape(-1), None, w13c, w13s,
+                                            w13o, seg1)
+            hc, hs, ho = CH.swiglu_quantize(CH.bf16_round(h13.astype(f32)), F)
+            y, _ = grouped_gemm_nvfp4_ref(hc, hs, ho, None, w2c, w2s, w2o, seg1)
+            codes, scales = CODEC.encode(y.astype(f32), mask)
+            agg = (agg + CODEC.s2f6_dequantize(codes, scales)[0]).astype(f32)   # slot order
+        want = CODEC.irht_f32(agg[None], mask)[0]
+        assert np.linalg.norm(got[n] - want) / np.linalg.norm(want) < 0.03, tt
