@@ -102,6 +102,10 @@ def algorithmic(seg_host):
 def stage_sources(stage, native_fp8=False):
     """HIP sources whose kernels a stage launches (their hash keys the
     committed HBM traffic figures)."""
+    if stage in ("chain_w13", "chain_w2_codec"):
+        return ("gemm.hip", "bsq_device.h", "bsq_internal.h")
+    if stage == "chain_combine":
+        return ("codec.hip", "bsq_device.h", "bsq_internal.h")
     if stage in ("fprop", "dgrad", "wgrad"):
         main = "gemm_mxfp8_native.hip" if native_fp8 and stage != "fprop" else "gemm.hip"
         return (main, "bsq_device.h", "bsq_internal.h")
@@ -241,7 +245,7 @@ def chain_forward(torch, bsq, inp, algo, dev, pair_row, reps=5):
         ach = work / (ms * 1e-3) / (1e9 if unit == "GB/s" else 1e12)
         peak = HBM_PEAK_GBS if unit == "GB/s" else MFMA_PEAK_TFLOPS["f16"]
         out[n] = {"ms": round(ms, 4), "achieved": round(ach, 2), "unit": unit, "peak": peak,
-                  "frac": round(ach / peak, 4)}
+                  "frac": round(ach / peak, 4), "traffic": read_traffic(n, kernel_sha(*stage_sources(n)))}
     out["ms_total"] = round(sum(out[n]["ms"] for n in names), 4)
     out["what"] = ("MoE expert forward (w13 GEMM -> SwiGLU + NVFP4 -> w2 GEMM with RHT-32 + S2F6 epilogue -> "
                    "combine), outside the step")
