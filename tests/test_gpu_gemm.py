@@ -13,7 +13,7 @@ from oracle import gemm as G
 from oracle import quant as Q
 from oracle.route import route as oroute
 
-from _gpu_util import DEV, filler_mxfp8, filler_nvfp4, h, log, t
+from _gpu_util import DEV, bf16_t, filler_mxfp8, filler_nvfp4, h, log, t
 
 pytestmark = pytest.mark.gpu
 f32 = np.float32
@@ -113,10 +113,22 @@ def _moe_full(wl, sample_experts):
     toks = np.unique(row_index[rows])
     qa, qs, qo = Q.quantize_nvfp4(synth.bf16_to_f32(x[toks])[None], Q.OUTER_ROW)
     ac[toks], as_[toks], ao[toks] = qa[0], qs[0], qo[0]
+    # the quantizers at this workload's full size (per token; per expert in one pass): sampled tokens and
+    # experts against the oracle
+    log(f"quantize workload{wl} activations and weights")
+    gxc, gxs, gxo = bsq.quantize_nvfp4(bf16_t(x), "row")
+    tt = t(toks)
+    assert np.array_equal(h(gxc[tt]), qa[0]) and np.array_equal(h(gxs[tt]), qs[0])
+    assert np.array_equal(h(gxo[tt]), np.asarray(qo).reshape(-1))
+    del gxc, gxs, gxo
+    gwc, gws, gwo = bsq.quantize_nvfp4(bf16_t(w), "tensor")
     for e in experts:
         qb, qbs, qbo = Q.quantize_nvfp4(synth.bf16_to_f32(w[e])[None], Q.OUTER_TENSOR)
         bc[e], bs[e], bo[e] = qb[0], qbs[0], qbo[0]
-    del x, w
+        assert np.array_equal(h(gwc[e]), qb[0]) and np.array_equal(h(gws[e]), qbs[0]), e
+        assert h(gwo)[e] == np.asarray(qbo).reshape(-1)[0]
+    del gwc, gws, gwo, x, w
+    torch.cuda.empty_cache()
     log(f"gemm nvfp4 workload{wl}: run (M_total={seg[-1]}, N={N}, K={K}, E={E})")
     y32, y16 = _nvfp4(t(ac), t(as_), t(ao), t(bc), t(bs), t(bo), t(seg), int(seg[-1]), row_index=t(row_index))
     ys = h(y32[t(rows)])
