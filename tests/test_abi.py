@@ -106,6 +106,33 @@ def test_codec_validation(lib):
     assert c(None, None, 4, 32, None, 0, 2, 0, None, 1, None) == OK            # no tokens: no work
 
 
+def test_chain_entries_validation(lib):
+    q = lib.bsq_swiglu_quantize_nvfp4
+    # h13, dtype, rows, ffn, flags, codes, scales, outer_out, stream
+    assert q(FAKE, 7, 4, 16, 0, FAKE, FAKE, FAKE, None) == E_DTYPE
+    assert q(FAKE, 1, 4, 16, 1, FAKE, FAKE, FAKE, None) == E_ENUM               # only the Four Over Six flag
+    assert q(FAKE, 1, 4, 24, 0, FAKE, FAKE, FAKE, None) == E_SHAPE
+    assert q(FAKE, 1, 4, 32784, 0, FAKE, FAKE, FAKE, None) == E_SHAPE
+    assert q(None, 1, 4, 16, 16, FAKE, FAKE, FAKE, None) == E_NULL
+    assert q(FAKE + 8, 1, 4, 16, 0, FAKE, FAKE, FAKE, None) == E_ALIGN
+    assert q(None, 1, 0, 16, 0, None, None, None, None) == OK                  # no rows: no work
+    g = lib.bsq_grouped_gemm_nvfp4_s2f6
+    # a_codes, a_scales, a_outer, per_row, a_rows, row_index, b_codes, b_scales, b_outer, seg, E, M, N, K,
+    # signs, out_codes, out_scales, stream
+    base = [FAKE, FAKE, FAKE, 1, 8, None, FAKE, FAKE, FAKE, FAKE, 2, 8, 256, 64, 0, FAKE, FAKE, None]
+    def call(**kw):
+        a = list(base)
+        for i, v in kw.items():
+            a[int(i[1:])] = v
+        return g(*a)
+    assert call(a12=100) == E_SHAPE                                              # N % 256
+    assert call(a13=48) == E_SHAPE                                               # K % 64
+    assert call(a10=0) == E_SHAPE                                                # E >= 1
+    assert call(a16=None) == E_NULL
+    assert call(a15=FAKE + 8) == E_ALIGN
+    assert call(a11=0) == OK                                                     # no rows: no work
+
+
 def test_quantize_mxfp8_validation(lib):
     q = lib.bsq_quantize_mxfp8
     assert q(FAKE, 1, 4, 48, 0, None, 0, 1, 0, 0, FAKE, FAKE, None, 0, None) == E_SHAPE
