@@ -203,6 +203,39 @@ def cpu_baseline(seg_host, row_index_host):
             "stage_seconds_equiv": {k: round(v, 3) for k, v in times.items()}}
 
 
+def latency_workload1(torch, bsq, dev, reps=50):
+    """Workload 1 (256 x 256, fits in L2: latency-bound): microseconds per call
+    of the NVFP4 quantizer (X and W, per tensor), the NVFP4 -> NVFP4 SR
+    requantization and the 256^3 grouped GEMM (one expert)."""
+    import synth
+    X, W = synth.workload1()
+    x, w = torch.from_numpy(X).to(dev), torch.from_numpy(W).to(dev)
+    xq = bsq.quantize_nvfp4(x, "tensor")
+    wq = bsq.quantize_nvfp4(w[None], "tensor")
+    seg = torch.tensor([0, 256], dtype=torch.int64, device=dev)
+    calls = {
+        "quantize_nvfp4_x": lambda: bsq.quantize_nvfp4(x, "tensor"),
+        "quantize_nvfp4_w": lambda: bsq.quantize_nvfp4(w, "tensor"),
+        "requant_nvfp4_sr": lambda: bsq.requant_transpose_sr(xq[0], xq[1], xq[2], "tensor", "nvfp4", seed=0,
+                                                             stream_id=0),
+        "gemm_nvfp4_256": lambda: bsq.grouped_gemm_nvfp4(xq[0], xq[1], xq[2], wq[0], wq[1], wq[2], seg, 256),
+    }
+    out = {}
+    for name, fn in calls.items():
+        for _ in range(5):
+            fn()
+        torch.cuda.synchronize()
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record()
+        for _ in range(reps):
+            fn()
+        b.record()
+        torch.cuda.synchronize()
+        out[name] = round(a.elapsed_time(b) / reps * 1e3, 2)
+    out["unit"] = "us per call (including the binding's output allocation)"
+    return out
+
+
 def chain_forward(torch, bsq, inp, algo, dev, pair_row, reps=5):
     """The expert forward chain (w13 GEMM, SwiGLU + per-row NVFP4, w2 GEMM with
     the RHT + S2F6 combine codec in its epilogue, combine) on the step's
@@ -418,6 +451,7 @@ def main():
                 "alternative_to": "bf16 combine payload (16 bits per value; the codec carries 8.25)"}
         del payload, enc
         alternatives["expert_chain_fwd"] = chain_forward(torch, bsq, inp, algo, dev, pair_row)
+        alternatives["workload1_latency"] = latency_workload1(torch, bsq, dev)
 
     if args.copy_calibration:
         src_buf = torch.empty(512 << 20, dtype=torch.uint8, device=dev).fill_(1)
