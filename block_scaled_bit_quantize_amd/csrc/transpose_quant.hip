@@ -235,50 +235,104 @@ __global__ __launch_bounds__(kThreads) void k_tq(
   const int cl = CPT * (t & 63);
   const int tb = t >> 6;
   const int64_t mb = m0 + 32 * tb;
-  if (mb >= Mp || c0 + cl >= C) return;
+  const bool active = mb < Mp && c0 + cl < C;
+  // MXFP8 codes are staged through LDS for whole-row stores, except from the
+  // gathered, segmented NVFP4 source (requantized activations), where direct
+  // 32-byte stores measured faster
+  constexpr bool kStage = OUTF == BSQ_MXFP8 && !(SRC == SRC_NVFP4 && SEG);
+  if constexpr (!kStage) {
+    if (!active) return;  // no barrier follows on these paths
+  }
   float z[CPT][32];
+  if (!kStage || active) {
 #pragma unroll
-  for (int i = 0; i < 32; ++i) {
-    const int m = 32 * tb + i;
-    if constexpr (SRC == SRC_F32) {
-      z[0][i] = *reinterpret_cast<const float*>(&tile[m * LROW + cl * 4]);
-    } else {
-      const uint32_t w = *reinterpret_cast<const uint32_t*>(&tile[m * LROW + cl * 2]);  // 2 channels
-      if constexpr (SRC == SRC_BF16) {
-        z[0][i] = __uint_as_float(w << 16);
-        z[1][i] = __uint_as_float(w & 0xFFFF0000u);
+    for (int i = 0; i < 32; ++i) {
+      const int m = 32 * tb + i;
+      if constexpr (SRC == SRC_F32) {
+        z[0][i] = *reinterpret_cast<const float*>(&tile[m * LROW + cl * 4]);
       } else {
-        const h2 hv = __builtin_bit_cast(h2, w);
-        z[0][i] = (float)hv[0] * rowmul[m];
-        z[1][i] = (float)hv[1] * rowmul[m];
+        const uint32_t w = *reinterpret_cast<const uint32_t*>(&tile[m * LROW + cl * 2]);  // 2 channels
+        if constexpr (SRC == SRC_BF16) {
+          z[0][i] = __uint_as_float(w << 16);
+          z[1][i] = __uint_as_float(w & 0xFFFF0000u);
+        } else {
+          const h2 hv = __builtin_bit_cast(h2, w);
+          z[0][i] = (float)hv[0] * rowmul[m];
+          z[1][i] = (float)hv[1] * rowmul[m];
+        }
       }
     }
   }
 
+  if constexpr (OUTF == BSQ_MXFP8) {
+    // Codes and scales of the tile go through LDS (the input tile's buffer, free
+    // once every phase-2 read is done) so that the output rows, 128 contiguous
+    // tokens per channel, leave as whole 128-byte runs (8 lanes per channel)
+    // instead of one 32-byte piece per lane and channel.
+    constexpr int SP = 144;  // stage pitch: one channel's 128 token codes (+16: 16-byte aligned, 2-way banks)
+    static_assert(TCH * SP + TCH * 4 <= TM * LROW, "output stage fits in the tile buffer");
+    uint32_t out[CPT][8];
+    int ex[CPT];
+    if (!kStage || active) {
+#pragma unroll
+      for (int ch = 0; ch < CPT; ++ch) {
+        const int64_t c = c0 + cl + ch;
+        const int64_t obase = base + c * Mp + mb;  // output index of z[ch][0]
+        float amax = 0.0f;
+#pragma unroll
+        for (int i = 0; i < 32; ++i) amax = fmaxf(amax, fabsf(z[ch][i]));
+        ex[ch] = e8m0_exponent(amax);
+        if constexpr (RND == BSQ_SR) {
+          sr_block_e4m3(z[ch], ex[ch], seed, stream_id, (uint64_t)(obase >> 3), out[ch]);
+        } else {
+          const float pw = pow2_neg(ex[ch]);  // |y| <= 448: the hardware convert is the nearest-even rounding
+#pragma unroll
+          for (int o = 0; o < 8; ++o)
+            out[ch][o] = e4m3_exact2(z[ch][4 * o] * pw, z[ch][4 * o + 1] * pw) |
+                         (e4m3_exact2(z[ch][4 * o + 2] * pw, z[ch][4 * o + 3] * pw) << 16);
+        }
+        if constexpr (!kStage) {  // each channel's codes leave as soon as they are ready
+          uint4* dst = reinterpret_cast<uint4*>(out_codes + obase);
+          dst[0] = make_uint4(out[ch][0], out[ch][1], out[ch][2], out[ch][3]);
+          dst[1] = make_uint4(out[ch][4], out[ch][5], out[ch][6], out[ch][7]);
+          out_scales[obase >> 5] = (uint8_t)(ex[ch] + 127);
+        }
+      }
+    }
+    if constexpr (!kStage) return;
+    __syncthreads();  // every phase-2 read of the input tile is done
+    uint8_t* const stage = tile;
+    uint8_t* const stage_sc = tile + TCH * SP;
+    if (active) {
+#pragma unroll
+      for (int ch = 0; ch < CPT; ++ch) {
+        uint4* d = reinterpret_cast<uint4*>(stage + (cl + ch) * SP + 32 * tb);
+        d[0] = make_uint4(out[ch][0], out[ch][1], out[ch][2], out[ch][3]);
+        d[1] = make_uint4(out[ch][4], out[ch][5], out[ch][6], out[ch][7]);
+        stage_sc[(cl + ch) * 4 + tb] = (uint8_t)(ex[ch] + 127);
+      }
+    }
+    __syncthreads();
+#pragma unroll
+    for (int k = 0; k < TCH * 8 / kThreads; ++k) {  // 16-byte pieces: channel id / 8, tokens 16 (id % 8) ..
+      const int id = t + k * kThreads;
+      const int ch = id >> 3, q = id & 7;
+      const int64_t c = c0 + ch;
+      if (c < C && m0 + 16 * q < Mp)
+        *reinterpret_cast<uint4*>(out_codes + base + c * Mp + m0 + 16 * q) =
+            *reinterpret_cast<const uint4*>(stage + ch * SP + 16 * q);
+    }
+    for (int id = t; id < TCH * 4; id += kThreads) {
+      const int ch = id >> 2, b = id & 3;
+      const int64_t c = c0 + ch;
+      if (c < C && m0 + 32 * b < Mp) out_scales[((base + c * Mp + m0) >> 5) + b] = stage_sc[ch * 4 + b];
+    }
+  } else {
 #pragma unroll
   for (int ch = 0; ch < CPT; ++ch) {
     const int64_t c = c0 + cl + ch;
     const int64_t obase = base + c * Mp + mb;  // output index of z[ch][0]
-    if constexpr (OUTF == BSQ_MXFP8) {
-      float amax = 0.0f;
-#pragma unroll
-      for (int i = 0; i < 32; ++i) amax = fmaxf(amax, fabsf(z[ch][i]));
-      const int ex = e8m0_exponent(amax);
-      uint32_t out[8];
-      if constexpr (RND == BSQ_SR) {
-        sr_block_e4m3(z[ch], ex, seed, stream_id, (uint64_t)(obase >> 3), out);
-      } else {
-        const float pw = pow2_neg(ex);  // |y| <= 448: the hardware convert is the nearest-even rounding
-#pragma unroll
-        for (int o = 0; o < 8; ++o)
-          out[o] = e4m3_exact2(z[ch][4 * o] * pw, z[ch][4 * o + 1] * pw) |
-                   (e4m3_exact2(z[ch][4 * o + 2] * pw, z[ch][4 * o + 3] * pw) << 16);
-      }
-      uint4* dst = reinterpret_cast<uint4*>(out_codes + obase);
-      dst[0] = make_uint4(out[0], out[1], out[2], out[3]);
-      dst[1] = make_uint4(out[4], out[5], out[6], out[7]);
-      out_scales[obase >> 5] = (uint8_t)(ex + 127);
-    } else {
+    {
       // NVFP4 target: outer s_t' from the item maximum, round-up block scales.
       const float am = __uint_as_float(amax_bits[e]);
       const float st = am > 0.0f ? am / 2688.0f : 1.0f;
@@ -323,6 +377,7 @@ __global__ __launch_bounds__(kThreads) void k_tq(
         out_scales[(obase >> 4) + 1] = (uint8_t)sc2[1];
       }
     }
+  }
   }
 }
 
