@@ -93,6 +93,14 @@ struct GemmArgs {
 
 enum { OUT_BF16 = 0, OUT_F32 = 1, OUT_S2F6 = 2 };
 
+// 16-byte output store with the non-temporal hint: the GEMM outputs (up to
+// 1.6 GB) are not read again by this kernel, and streaming them measured
+// 0.5-2% faster than ordinary stores.
+typedef unsigned int u32x4v __attribute__((ext_vector_type(4)));
+__device__ __forceinline__ void store_nt(void* p, uint4 v) {
+  __builtin_nontemporal_store(u32x4v{v.x, v.y, v.z, v.w}, reinterpret_cast<u32x4v*>(p));
+}
+
 struct Tile {
   int e;
   int64_t m0, n0;
@@ -235,7 +243,7 @@ __device__ __forceinline__ void store_tile(const GemmArgs& g, const Tile& tl, co
       if (r < rows_left) {
         const uint4 v = *reinterpret_cast<const uint4*>(stage + r * P + c * 16);
         const int64_t orow = WGRAD ? (int64_t)tl.e * g.M + tl.m0 + r : tl.seg0 + tl.m0 + r;
-        *reinterpret_cast<uint4*>(static_cast<uint16_t*>(g.out) + orow * g.N + tl.n0 + c * 8) = v;
+        store_nt(static_cast<uint16_t*>(g.out) + orow * g.N + tl.n0 + c * 8, v);
       }
     }
   } else {
@@ -267,10 +275,10 @@ __device__ __forceinline__ void store_tile(const GemmArgs& g, const Tile& tl, co
           const int id = t + k * kThreads;
           const int r = id >> 6, c = id & 63;
           if (half * 128 + r < rows_left) {
-            const float4 v = *reinterpret_cast<const float4*>(stage + r * P + c * 16);
+            const uint4 v = *reinterpret_cast<const uint4*>(stage + r * P + c * 16);
             const int64_t m = tl.m0 + half * 128 + r;
             const int64_t orow = WGRAD ? (int64_t)tl.e * g.M + m : tl.seg0 + m;
-            *reinterpret_cast<float4*>(static_cast<float*>(g.out) + orow * g.N + tl.n0 + c * 4) = v;
+            store_nt(static_cast<float*>(g.out) + orow * g.N + tl.n0 + c * 4, v);
           }
         }
       } else {
@@ -291,9 +299,9 @@ __device__ __forceinline__ void store_tile(const GemmArgs& g, const Tile& tl, co
             uint32_t w[8];
             const uint32_t sc = rht_s2f6_block(v, g.signs, w);
             const int64_t orow = tl.seg0 + tl.m0 + half * 128 + r;
-            uint4* dst = reinterpret_cast<uint4*>(static_cast<uint8_t*>(g.out) + orow * g.N + tl.n0 + b * 32);
-            dst[0] = make_uint4(w[0], w[1], w[2], w[3]);
-            dst[1] = make_uint4(w[4], w[5], w[6], w[7]);
+            uint8_t* dst = static_cast<uint8_t*>(g.out) + orow * g.N + tl.n0 + b * 32;
+            store_nt(dst, make_uint4(w[0], w[1], w[2], w[3]));
+            store_nt(dst + 16, make_uint4(w[4], w[5], w[6], w[7]));
             g.out_scales[orow * (g.N / 32) + tl.n0 / 32 + b] = (uint8_t)sc;
           }
         }
