@@ -203,6 +203,15 @@ __device__ __forceinline__ float sr_e2m1(float y, uint32_t r16) {
   return copysignf(mag, y);
 }
 
+// ---------------------------------------------------------------- stores
+// 16-byte store with the non-temporal hint, for outputs the kernel does not
+// read again (measured 0.5-3% faster than ordinary stores on the quantizers
+// and the GEMM epilogues).
+typedef unsigned int u32x4v __attribute__((ext_vector_type(4)));
+__device__ __forceinline__ void store_nt(void* p, uint4 v) {
+  __builtin_nontemporal_store(u32x4v{v.x, v.y, v.z, v.w}, reinterpret_cast<u32x4v*>(p));
+}
+
 // ---------------------------------------------------------------- RHT-32 + S2F6
 // (combine codec: the encoder kernel and the w2 GEMM's epilogue)
 constexpr uint32_t kInvSqrt32 = 0x3E3504F3u;  // float32 nearest to 1/sqrt(32)

@@ -319,8 +319,7 @@ __global__ __launch_bounds__(kThreads) void k_tq(
       const int ch = id >> 3, q = id & 7;
       const int64_t c = c0 + ch;
       if (c < C && m0 + 16 * q < Mp)
-        *reinterpret_cast<uint4*>(out_codes + base + c * Mp + m0 + 16 * q) =
-            *reinterpret_cast<const uint4*>(stage + ch * SP + 16 * q);
+        store_nt(out_codes + base + c * Mp + m0 + 16 * q, *reinterpret_cast<const uint4*>(stage + ch * SP + 16 * q));
     }
     for (int id = t; id < TCH * 4; id += kThreads) {
       const int ch = id >> 2, b = id & 3;
