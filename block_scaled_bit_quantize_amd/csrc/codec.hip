@@ -61,8 +61,9 @@ __global__ __launch_bounds__(kThreads) void k_rht_s2f6_encode(const T* __restric
   }
   uint32_t w[8];
   const uint32_t sc = rht_s2f6_block(v, signs, w);
-  store_nt(codes + blk * 32, make_uint4(w[0], w[1], w[2], w[3]));
-  store_nt(codes + blk * 32 + 16, make_uint4(w[4], w[5], w[6], w[7]));
+  uint4* dst = reinterpret_cast<uint4*>(codes + blk * 32);
+  dst[0] = make_uint4(w[0], w[1], w[2], w[3]);
+  dst[1] = make_uint4(w[4], w[5], w[6], w[7]);
   scales[blk] = (uint8_t)sc;
 }
 

@@ -292,9 +292,10 @@ __device__ __forceinline__ void store_tile(const GemmArgs& g, const Tile& tl, co
             uint32_t w[8];
             const uint32_t sc = rht_s2f6_block(v, g.signs, w);
             const int64_t orow = tl.seg0 + tl.m0 + half * 128 + r;
-            uint8_t* dst = static_cast<uint8_t*>(g.out) + orow * g.N + tl.n0 + b * 32;
-            store_nt(dst, make_uint4(w[0], w[1], w[2], w[3]));
-            store_nt(dst + 16, make_uint4(w[4], w[5], w[6], w[7]));
+            // ordinary stores: a lane's 32 bytes are half of a line (the hint measured +35% HBM writes here)
+            uint4* dst = reinterpret_cast<uint4*>(static_cast<uint8_t*>(g.out) + orow * g.N + tl.n0 + b * 32);
+            dst[0] = make_uint4(w[0], w[1], w[2], w[3]);
+            dst[1] = make_uint4(w[4], w[5], w[6], w[7]);
             g.out_scales[orow * (g.N / 32) + tl.n0 / 32 + b] = (uint8_t)sc;
           }
         }

@@ -466,8 +466,9 @@ __global__ __launch_bounds__(kThreads) void k_mxfp8_rows(const T* __restrict__ x
       out[o] = e4m3_exact2(v[0], v[1]) | (e4m3_exact2(v[2], v[3]) << 16);
     }
   }
-  store_nt(codes + blk * 32, make_uint4(out[0], out[1], out[2], out[3]));
-  store_nt(codes + blk * 32 + 16, make_uint4(out[4], out[5], out[6], out[7]));
+  uint4* dst = reinterpret_cast<uint4*>(codes + blk * 32);
+  dst[0] = make_uint4(out[0], out[1], out[2], out[3]);
+  dst[1] = make_uint4(out[4], out[5], out[6], out[7]);
   scales[blk] = (uint8_t)(e + 127);
 }
 
