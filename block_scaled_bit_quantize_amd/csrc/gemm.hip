@@ -189,7 +189,16 @@ __device__ bool tile_coords(const GemmArgs& g, const int64_t* s_cum, int64_t til
 // no wave still reads it.
 template <int NVFP4, int WGRAD, int OUT>
 __device__ __forceinline__ void store_tile(const GemmArgs& g, const Tile& tl, const f32x16 (&acc)[4][TJ], int wm,
-                                           int wn, int lane, uint8_t* stage) {
+                                           int wn, int lane_in, uint8_t* stage) {
+  // The lane's LDS and global offsets are derived here anew for every tile:
+  // hoisted out of the tile loop they stay live across the K loop, do not fit
+  // in registers beside the accumulators, and their spilled copies would be
+  // reloaded after the first half's global stores, a reload that waits for
+  // those stores to complete (one vector-memory counter orders both).
+  int lane = lane_in;
+  asm volatile("" : "+v"(lane));
+  int t = threadIdx.x;
+  asm volatile("" : "+v"(t));
   const float sw = NVFP4 ? g.b_outer[tl.e] : 1.0f;
   float rs[4];  // output scale of each of the lane's rows
 #pragma unroll
@@ -207,7 +216,6 @@ __device__ __forceinline__ void store_tile(const GemmArgs& g, const Tile& tl, co
       rs[i] = sx * sw;
     }
   }
-  const int t = threadIdx.x;
   const int64_t rows_left = WGRAD ? BM : tl.Me - tl.m0;  // rows of the tile inside the segment
   if constexpr (OUT == OUT_BF16) {
     // bf16 rows of 512 bytes at a 520-byte pitch (rows 2 banks apart)
