@@ -3,6 +3,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <atomic>
+
 #include "../../include/bsq.h"
 
 namespace bsqh {
@@ -19,17 +21,18 @@ inline int64_t tile_bound(int64_t total_rows, int64_t num_segments, int64_t tile
 }
 
 // Compute units of the current device (persistent kernels launch one
-// workgroup per CU); 256 if the query fails.
+// workgroup per CU); 256 if the query fails. The per-device cache is atomic:
+// threads calling concurrently may each query once and store the same value.
 inline int device_cus() {
-  static int cache[64];
+  static std::atomic<int> cache[64];
   int dev = 0;
   if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
-  if (cache[dev] <= 0) {
-    int n = 0;
+  int n = cache[dev].load(std::memory_order_relaxed);
+  if (n <= 0) {
     if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0) n = 256;
-    cache[dev] = n;
+    cache[dev].store(n, std::memory_order_relaxed);
   }
-  return cache[dev];
+  return n;
 }
 
 }  // namespace bsqh

@@ -14,7 +14,8 @@
  * Conventions for every entry point:
  *  - Buffers are device memory owned by the caller, except where a parameter
  *    is marked HOST. The library never allocates, frees or synchronizes, and
- *    keeps no state between calls; calls are thread-safe.
+ *    keeps no state between calls beyond a per-device cache of the
+ *    compute-unit count (sizes persistent grids); calls are thread-safe.
  *  - Work is enqueued on `stream` (0 = the null stream) and runs
  *    asynchronously. The return value reports argument validation (checked on
  *    the host before any HIP call) and launch errors only.
