@@ -236,6 +236,65 @@ def latency_workload1(torch, bsq, dev, reps=50):
     return out
 
 
+def workload5(torch, bsq, dev, reps=5):
+    """Workload 5 (65536 tokens, hidden 7168, 128 experts of 2048 x 7168, top-8 with Zipf(1.1) expert
+    popularity, Student-t(3) activations): per-token Four Over Six activation quantize, per-expert weight
+    quantize and the NVFP4 grouped GEMM over the skewed segments, each timed on its own (HIP events,
+    mean of `reps` calls). Activations and weights are drawn on the GPU from a seeded torch generator
+    (the same distributions as the parity tests' NumPy inputs); the routing is the parity tests' own."""
+    import numpy as np
+
+    import synth
+    p = synth.WORKLOADS[5]
+    T5, H5, E5, F5, k5 = p["tokens"], p["hidden"], p["experts"], p["ffn"], p["topk"]
+    gen = torch.Generator(device=dev)
+    gen.manual_seed(5)
+    # Student-t with 3 degrees of freedom: z / sqrt(chi2_3 / 3), chi2_3 the sum of three squared normals
+    chi = sum(torch.randn((T5, H5), generator=gen, device=dev) ** 2 for _ in range(3))
+    x = (torch.randn((T5, H5), generator=gen, device=dev) * torch.rsqrt(chi / 3.0)).to(torch.bfloat16)
+    del chi
+    w = (torch.randn((E5, F5, H5), generator=gen, device=dev) * p["w_std"]).to(torch.bfloat16)
+    ids = torch.from_numpy(synth.moe_routing(5)).to(dev)
+    ri, seg, _ = bsq.route(ids, E5)
+    M5 = T5 * k5
+    xq = bsq.quantize_nvfp4(x, "row", four_over_six=True)
+    wq = bsq.quantize_nvfp4(w, "tensor")
+    lens = np.diff(seg.cpu().numpy())
+    nv = lambda rows, cols: rows * (cols // 2 + cols // 16)
+    calls = {
+        "quant_x": (lambda: bsq.quantize_nvfp4(x, "row", four_over_six=True), "GB/s",
+                    T5 * H5 * 2 + nv(T5, H5) + T5 * 4),
+        "quant_w": (lambda: bsq.quantize_nvfp4(w, "tensor"), "GB/s", E5 * F5 * H5 * 2 + nv(E5 * F5, H5) + E5 * 4),
+        "fprop": (lambda: bsq.grouped_gemm_nvfp4(xq[0], xq[1], xq[2], wq[0], wq[1], wq[2], seg, M5, row_index=ri),
+                  "TFLOP/s", 2.0 * M5 * F5 * H5),
+    }
+    out = {}
+    for name, (fn, unit, work) in calls.items():
+        for _ in range(2):
+            fn()
+        torch.cuda.synchronize()
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record()
+        for _ in range(reps):
+            fn()
+        b.record()
+        torch.cuda.synchronize()
+        ms = a.elapsed_time(b) / reps
+        if unit == "GB/s":
+            ach, peak = work / (ms * 1e-3) / 1e9, HBM_PEAK_GBS
+        else:
+            ach, peak = work / (ms * 1e-3) / 1e12, MFMA_PEAK_TFLOPS["f16"]
+        out[name] = {"ms": round(ms, 4), "achieved": round(ach, 2), "unit": unit, "peak": peak,
+                     "frac": round(ach / peak, 4)}
+    out["segments"] = {"experts": int(E5), "min_rows": int(lens.min()), "max_rows": int(lens.max()),
+                       "total_rows": int(M5)}
+    out["what"] = ("workload 5 (Zipf-skewed MoE forward), outside the step; GEMM fraction against the fp16 "
+                   "MFMA peak it runs on")
+    del x, w, xq, wq
+    torch.cuda.empty_cache()
+    return out
+
+
 def chain_forward(torch, bsq, inp, algo, dev, pair_row, reps=5):
     """The expert forward chain (w13 GEMM, SwiGLU + per-row NVFP4, w2 GEMM with
     the RHT + S2F6 combine codec in its epilogue, combine) on the step's
@@ -452,6 +511,7 @@ def main():
         del payload, enc
         alternatives["expert_chain_fwd"] = chain_forward(torch, bsq, inp, algo, dev, pair_row)
         alternatives["workload1_latency"] = latency_workload1(torch, bsq, dev)
+        alternatives["workload5_fwd"] = workload5(torch, bsq, dev)
 
     if args.copy_calibration:
         src_buf = torch.empty(512 << 20, dtype=torch.uint8, device=dev).fill_(1)
