@@ -179,7 +179,11 @@ int bsq_quantize_nvfp4_square(const void* x, int dtype, int64_t batch, int64_t r
  *              from the segment start; element index of (e, c, m) is
  *              cols * sum_{e'<e} Mp_e' + c * Mp_e + m. cols % 64 == 0.
  *              seg_offsets == NULL means one segment covering all rows.
- *              Needs bsq_quantize_mxfp8_workspace() bytes of workspace.
+ *              Needs bsq_quantize_mxfp8_workspace() bytes of workspace. The
+ *              caller sizes codes for cols * sum_e Mp_e bytes and scales for
+ *              a 32nd of that; cols * (rows + 31 * num_segments) bounds the sum
+ *              for any valid seg_offsets (the sizes are not checked: they
+ *              depend on the device-side offsets).
  * rnd        BSQ_RN (nearest-even) or BSQ_SR.
  * seed, stream_id  select the random stream (SR only).
  * E8M0 rule: the smallest 2^e with a_b <= 448 * 2^e (e clamped to [-127,127];
@@ -213,7 +217,8 @@ int bsq_quantize_mxfp8(const void* x, int dtype, int64_t rows, int64_t cols, int
  *   out_fmt == BSQ_MXFP8): dispatched row m (0 <= m < rows) reads input row
  *   row_gather[m] (int32, < in_rows); rows are grouped into num_segments
  *   expert segments and written in the padded per-segment transposed layout
- *   of bsq_quantize_mxfp8(transpose=1).
+ *   of bsq_quantize_mxfp8(transpose=1), sized by the caller as described
+ *   there (cols * (rows + 31 * num_segments) bounds it).
  * out_fmt BSQ_MXFP8: E8M0/E4M3 as in bsq_quantize_mxfp8 (no outer scale).
  * out_fmt BSQ_NVFP4: new outer s_t' = f32(max|x^|/2688) per batch item
  *   (written to out_outer[batch]); block scale r = f32(a_b / f32(6 s_t'))
