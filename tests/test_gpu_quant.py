@@ -211,6 +211,60 @@ def test_quantize_mxfp8_transposed_small(dtype, rnd):
     assert np.array_equal(h(gc), oc) and np.array_equal(h(gs), os_)
 
 
+def _sr_edge_blocks(rng, nblk):
+    """MX blocks of 32 at the edges of the kernels' stochastic-rounding fast path (every value of a group of
+    8 zero or at least 2^(e-6), e >= -120, done by the hardware SR convert) and of its general path."""
+    out = np.empty((nblk, 32), f32)
+    for b in range(nblk):
+        e = int(rng.integers(-20, 21))
+        top = f32(448.0) * f32(2.0) ** e
+        kind = b % 8
+        v = (rng.uniform(2.0 ** (e - 6), float(top), 32) * rng.choice([-1.0, 1.0], 32)).astype(f32)
+        if kind == 0:    # exactly at the fast-path threshold 2^(e-6), block maximum exactly 448 2^e
+            v[:] = f32(2.0) ** (e - 6) * rng.choice([-1.0, 1.0], 32).astype(f32)
+        elif kind == 1:  # one value just below the threshold: that group of 8 takes the general path
+            v[int(rng.integers(32))] = np.nextafter(f32(2.0) ** (e - 6), f32(0.0))
+        elif kind == 2:  # all-ones mantissas: rounding up carries into the exponent
+            v = (f32(2.0) ** rng.integers(e - 6, e + 8, 32) * f32(1.99999)).astype(f32) * \
+                rng.choice([-1.0, 1.0], 32).astype(f32)
+        elif kind == 3:  # zeros of both signs among normal values
+            v[::3] = f32(0.0)
+            v[1::5] = f32(-0.0)
+        elif kind == 4:  # a tiny block: E8M0 exponent below -120, general path throughout
+            v = (rng.standard_normal(32) * 1e-39).astype(f32)
+        elif kind == 5:  # values already on the E4M3 grid (nothing dropped)
+            v = (F.e4m3_decode(rng.integers(0x08, 0x7F, 32).astype(np.uint8)) * f32(2.0) ** e).astype(f32)
+        elif kind == 6:  # block maximum just above 448 2^e: the next exponent
+            v[0] = np.nextafter(top, f32(np.inf))
+        if kind not in (2, 4, 5, 6):
+            v[int(rng.integers(32))] = top * f32(rng.choice([-1.0, 1.0]))
+        out[b] = v
+    return out
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_quantize_mxfp8_sr_fast_path_edges(dtype):
+    """SR to MXFP8 at the edges of the hardware-SR fast path, row-wise and transposed, bit-exact."""
+    log(f"quantize_mxfp8 SR fast-path edges {dtype}")
+    rng = np.random.default_rng(21)
+    blocks = _sr_edge_blocks(rng, 64 * 8)
+    if dtype == "bf16":  # round to bf16 first; both sides then see the same values
+        bits = synth.bf16_bits(blocks)
+        blocks = synth.bf16_to_f32(bits).reshape(blocks.shape)
+    dev_in = (lambda a: bf16_t(synth.bf16_bits(a))) if dtype == "bf16" else t
+    x = np.ascontiguousarray(blocks.reshape(64, 256))          # row-wise: each block along a row
+    gc, gs = bsq.quantize_mxfp8(dev_in(x), "sr", seed=9, stream_id=4)
+    oc, os_ = Q.quantize_mxfp8(x, Q.SR, 9, 4)
+    assert np.array_equal(h(gs), os_)
+    assert np.array_equal(h(gc), oc)
+    xt = np.ascontiguousarray(blocks.reshape(128, 4, 32).transpose(1, 2, 0).reshape(128, 128))  # blocks along tokens
+    _, n = bsq.padded_segment_layout([0, 128], 128)
+    gc, gs = bsq.quantize_mxfp8(dev_in(xt), "sr", seed=9, stream_id=5, transpose=True, out_elems=n)
+    oc, os_ = Q.quantize_mxfp8_transposed(xt, [0, 128], Q.SR, 9, 5)
+    assert np.array_equal(h(gs), os_)
+    assert np.array_equal(h(gc), oc)
+
+
 _REQ_SHAPES = [(2, 64, 128), (1, 160, 64), (3, 256, 192), (1, 48, 128)]
 
 
