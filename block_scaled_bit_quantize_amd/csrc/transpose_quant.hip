@@ -90,27 +90,49 @@ __global__ __launch_bounds__(1024) void k_seg_plan(const int64_t* __restrict__ s
 
 // Largest dequantized magnitude of each batch item of an NVFP4 tensor
 // (max over a block of f32(f32(max|q| * s_b) * s_t) equals the max of the
-// element-wise dequantization, rounding being monotonic).
+// element-wise dequantization, rounding being monotonic). One thread per block
+// of 16; a workgroup whose blocks all belong to one item reduces them and
+// issues one atomic (per-thread atomics on one address serialize), otherwise
+// each thread merges its own block.
 __global__ __launch_bounds__(kThreads) void k_nvfp4_item_amax(const uint8_t* __restrict__ codes,
                                                               const uint8_t* __restrict__ scales,
                                                               const float* __restrict__ outer, int in_mode,
                                                               int64_t nblk, int64_t blk_per_row, int64_t rows_per_item,
                                                               uint32_t* __restrict__ amax_bits) {
-  const int64_t blk = (int64_t)blockIdx.x * kThreads + threadIdx.x;
-  if (blk >= nblk) return;
-  const uint2 w = *reinterpret_cast<const uint2*>(codes + blk * 8);
-  uint32_t mq = 0;
+  const int64_t first = (int64_t)blockIdx.x * kThreads;
+  const int64_t blk = first + threadIdx.x;
+  float v = 0.0f;
+  int64_t item = 0;
+  if (blk < nblk) {
+    const uint2 w = *reinterpret_cast<const uint2*>(codes + blk * 8);
+    uint32_t mq = 0;
 #pragma unroll
-  for (int i = 0; i < 8; ++i) {
-    mq = max(mq, (w.x >> (4 * i)) & 7u);
-    mq = max(mq, (w.y >> (4 * i)) & 7u);
+    for (int i = 0; i < 8; ++i) {
+      mq = max(mq, (w.x >> (4 * i)) & 7u);
+      mq = max(mq, (w.y >> (4 * i)) & 7u);
+    }
+    const float qmax = mq == 0 ? 0.0f : (mq < 2 ? 0.5f * (float)mq : (mq < 4 ? 1.0f + 0.5f * (float)(mq - 2) : (mq < 6 ? (float)(mq - 2) : (mq == 6 ? 4.0f : 6.0f))));
+    const int64_t row = blk / blk_per_row;
+    item = row / rows_per_item;
+    const float st = in_mode == BSQ_OUTER_ROW ? outer[row] : outer[item];
+    v = (qmax * e4m3_val(scales[blk])) * st;
   }
-  const float qmax = mq == 0 ? 0.0f : (mq < 2 ? 0.5f * (float)mq : (mq < 4 ? 1.0f + 0.5f * (float)(mq - 2) : (mq < 6 ? (float)(mq - 2) : (mq == 6 ? 4.0f : 6.0f))));
-  const int64_t row = blk / blk_per_row;
-  const int64_t item = row / rows_per_item;
-  const float st = in_mode == BSQ_OUTER_ROW ? outer[row] : outer[item];
-  const float v = (qmax * e4m3_val(scales[blk])) * st;
-  if (v > 0.0f) atomicMax(amax_bits + item, __float_as_uint(v));
+  const int64_t last = (first + kThreads < nblk ? first + kThreads : nblk) - 1;
+  const int64_t item0 = first / blk_per_row / rows_per_item;
+  if (item0 == last / blk_per_row / rows_per_item) {  // uniform across the workgroup
+    __shared__ float red[kThreads / 64];
+    const float m = wave_max(v);
+    if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = m;
+    __syncthreads();
+    if (threadIdx.x == 0) {
+      float r = red[0];
+#pragma unroll
+      for (int i = 1; i < kThreads / 64; ++i) r = fmaxf(r, red[i]);
+      if (r > 0.0f) atomicMax(amax_bits + item0, __float_as_uint(r));
+    }
+  } else if (v > 0.0f) {
+    atomicMax(amax_bits + item, __float_as_uint(v));
+  }
 }
 
 template <int SRC> struct TileT { typedef uint16_t type; };
