@@ -33,34 +33,54 @@ __global__ __launch_bounds__(kChunk) void k_route_count(const int32_t* __restric
   for (int e = threadIdx.x; e < E; e += kChunk) counts[(int64_t)blockIdx.x * E + e] = cnt[e];
 }
 
-// One workgroup of 1024 threads: thread e turns the chunk counts of expert e
-// into exclusive bases (in place), then a scan over experts gives the offsets.
+// One workgroup of 1024 threads turns the per-chunk counts into exclusive
+// bases (in place) and the segment offsets. Thread (e, p) = (t % E, t / E),
+// p < P = 1024 / E, owns expert e's counts in a contiguous range of chunks:
+// it sums them (independent loads), the partial sums are scanned over p
+// in LDS, the expert totals over e, and each thread then writes its range's
+// bases.
 __global__ __launch_bounds__(1024) void k_route_scan(int32_t* __restrict__ counts, int64_t nchunks, int E,
                                                      int64_t* __restrict__ seg_offsets) {
+  __shared__ int64_t part[1024];
   __shared__ int64_t tot[1024];
-  const int e = threadIdx.x;
-  int64_t run = 0;
-  if (e < E) {
-    for (int64_t c = 0; c < nchunks; ++c) {
+  const int t = threadIdx.x;
+  const int P = 1024 / E;
+  const int e = t % E, p = t / E;
+  const bool own = p < P;
+  const int64_t per = (nchunks + P - 1) / P;
+  const int64_t c0 = own ? (int64_t)p * per : 0;
+  const int64_t c1 = own ? (c0 + per < nchunks ? c0 + per : nchunks) : 0;
+  int64_t sum = 0;
+  for (int64_t c = c0; c < c1; ++c) sum += counts[c * E + e];
+  part[t] = sum;  // part[p * E + e] for the owning threads
+  __syncthreads();
+  int64_t total = 0;
+  if (t < E) {  // exclusive prefix of expert t's partial sums over p
+    for (int q = 0; q < P; ++q) {
+      const int64_t v = part[q * E + t];
+      part[q * E + t] = total;
+      total += v;
+    }
+  }
+  tot[t] = total;  // zero for t >= E
+  __syncthreads();
+  for (int o = 1; o < 1024; o <<= 1) {  // inclusive scan of the expert totals
+    const int64_t v = t >= o ? tot[t - o] : 0;
+    __syncthreads();
+    tot[t] += v;
+    __syncthreads();
+  }
+  if (t < E) seg_offsets[t] = tot[t] - total;
+  if (t == E - 1) seg_offsets[E] = tot[t];
+  if (own) {
+    const int64_t start = (e ? tot[e - 1] : 0) + part[t];
+    int64_t run = start;
+    for (int64_t c = c0; c < c1; ++c) {
       const int32_t v = counts[c * E + e];
       counts[c * E + e] = (int32_t)run;
       run += v;
     }
   }
-  tot[e] = run;
-  __syncthreads();
-  for (int o = 1; o < 1024; o <<= 1) {
-    const int64_t a = e >= o ? tot[e - o] : 0;
-    __syncthreads();
-    tot[e] += a;
-    __syncthreads();
-  }
-  const int64_t start = tot[e] - run;
-  if (e < E) {
-    seg_offsets[e] = start;
-    for (int64_t c = 0; c < nchunks; ++c) counts[c * E + e] += (int32_t)start;
-  }
-  if (e == E - 1) seg_offsets[E] = tot[e];
 }
 
 __global__ __launch_bounds__(kChunk) void k_route_scatter(const int32_t* __restrict__ ids, int64_t tokens, int k, int E,
