@@ -137,13 +137,15 @@ __global__ __launch_bounds__(kThreads) void k_nvfp4_item_amax(const uint8_t* __r
 
 template <int SRC> struct TileT { typedef uint16_t type; };
 template <> struct TileT<SRC_F32> { typedef float type; };
-template <int SRC> constexpr int tile_channels() { return SRC == SRC_F32 ? 64 : 128; }
+template <int SRC> constexpr int tile_channels() { return SRC == SRC_NVFP4 ? 128 : 64; }
 
 // The transposing quantizer. SEG: tiles come from the segment plan (gather
 // and per-segment padded layout); otherwise batch item e covers input rows
 // [e*R, (e+1)*R) and is written as [cols, R]. A workgroup covers 128 tokens x
-// TCH channels (128 for 16-bit tiles, 64 for float tiles); in phase 2 a
-// thread owns CPT = TCH/64 adjacent channels x 32 tokens.
+// TCH channels (128 for NVFP4 sources, whose decoded fp16 tile is small; 64
+// for bf16 and float sources, whose 18 KB tile lets more workgroups share a
+// CU: measured 5% faster than 128 for the bf16 gradient); in phase 2 a thread
+// owns CPT = TCH/64 adjacent channels x 32 tokens.
 template <int SRC, int OUTF, int RND, bool SEG>
 __global__ __launch_bounds__(kThreads) void k_tq(
     const void* __restrict__ src, const uint8_t* __restrict__ in_scales, const float* __restrict__ in_outer,
@@ -196,10 +198,12 @@ __global__ __launch_bounds__(kThreads) void k_tq(
   // ---- phase 1: rows m0 .. m0+127 of the segment, channels c0 .. c0+TCH-1
   if constexpr (SRC == SRC_BF16) {
     const uint16_t* x = static_cast<const uint16_t*>(src);
+    constexpr int TPR = TCH / 8;          // threads per row, 8 values each
+    constexpr int RPP = kThreads / TPR;   // rows per pass
 #pragma unroll
-    for (int p = 0; p < 8; ++p) {
-      const int m = p * 16 + (t >> 4);
-      const int cc = (t & 15) * 8;
+    for (int p = 0; p < TM / RPP; ++p) {
+      const int m = p * RPP + t / TPR;
+      const int cc = (t % TPR) * 8;
       uint4 v = make_uint4(0, 0, 0, 0);
       if (m0 + m < Me && c0 + cc < C) v = *reinterpret_cast<const uint4*>(x + (seg_start + m0 + m) * C + c0 + cc);
       *reinterpret_cast<uint4*>(&tile[m * LROW + cc * 2]) = v;
@@ -273,11 +277,14 @@ __global__ __launch_bounds__(kThreads) void k_tq(
       if constexpr (SRC == SRC_F32) {
         z[0][i] = *reinterpret_cast<const float*>(&tile[m * LROW + cl * 4]);
       } else {
-        const uint32_t w = *reinterpret_cast<const uint32_t*>(&tile[m * LROW + cl * 2]);  // 2 channels
-        if constexpr (SRC == SRC_BF16) {
+        if constexpr (SRC == SRC_BF16 && CPT == 1) {
+          z[0][i] = __uint_as_float((uint32_t)*reinterpret_cast<const uint16_t*>(&tile[m * LROW + cl * 2]) << 16);
+        } else if constexpr (SRC == SRC_BF16) {
+          const uint32_t w = *reinterpret_cast<const uint32_t*>(&tile[m * LROW + cl * 2]);  // 2 channels
           z[0][i] = __uint_as_float(w << 16);
-          z[1][i] = __uint_as_float(w & 0xFFFF0000u);
+          z[CPT - 1][i] = __uint_as_float(w & 0xFFFF0000u);
         } else {
+          const uint32_t w = *reinterpret_cast<const uint32_t*>(&tile[m * LROW + cl * 2]);  // 2 channels
           const h2 hv = __builtin_bit_cast(h2, w);
           z[0][i] = (float)hv[0] * rowmul[m];
           z[1][i] = (float)hv[1] * rowmul[m];
