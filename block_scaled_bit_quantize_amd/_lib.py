@@ -11,6 +11,9 @@ c_int = ctypes.c_int
 c_size = ctypes.c_size_t
 c_vp = ctypes.c_void_p
 
+# include/bsq.h: BSQ_ROUTE_NOALLOC_MAX_BYTES
+ROUTE_NOALLOC_MAX_BYTES = 1 << 20
+
 # name -> (restype, argtypes); mirrors include/bsq.h
 SIGNATURES = {
     "bsq_status_string": (ctypes.c_char_p, [c_int]),
@@ -38,6 +41,7 @@ SIGNATURES = {
                                               c_int, c_vp]),
     "bsq_route_workspace": (c_size, [c_i64, c_i64]),
     "bsq_route": (c_int, [c_vp, c_i64, c_i64, c_i64, c_vp, c_vp, c_vp, c_vp, c_size, c_vp]),
+    "bsq_route_noalloc": (c_int, [c_vp, c_i64, c_i64, c_i64, c_vp, c_vp, c_vp, c_vp]),
     "bsq_rht_s2f6_encode": (c_int, [c_vp, c_int, c_i64, c_i64, ctypes.c_uint32, c_vp, c_vp, c_vp]),
     "bsq_rht_s2f6_combine": (c_int, [c_vp, c_vp, c_i64, c_i64, c_vp, c_i64, c_i64, ctypes.c_uint32, c_vp, c_int,
                                      c_vp]),

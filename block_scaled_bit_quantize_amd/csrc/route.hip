@@ -10,6 +10,8 @@
 // counts, one scan that turns them into segment offsets and per-chunk bases,
 // and a scatter whose within-chunk rank comes from an LDS bitmap of the
 // tokens routed to each expert (a popcount of the earlier tokens).
+#include <mutex>
+
 #include "bsq_device.h"
 #include "bsq_internal.h"
 
@@ -120,25 +122,74 @@ extern "C" size_t bsq_route_workspace(int64_t tokens, int64_t E) {
   return (size_t)((nchunks * E * 4 + 255) / 256 * 256);
 }
 
+// The three passes; `counts` holds nchunks * E int32 (every slot that the
+// scan and the scatter read is written by the count pass first).
+static int route_launch(const int32_t* topk_ids, int64_t tokens, int64_t k, int64_t E, int32_t* row_index,
+                        int64_t* seg_offsets, int32_t* pair_row, int32_t* counts, hipStream_t s) {
+  const int64_t nchunks = (tokens + kChunk - 1) / kChunk;
+  if (tokens > 0)
+    hipLaunchKernelGGL(k_route_count, dim3((unsigned)nchunks), dim3(kChunk), E * sizeof(int32_t), s, topk_ids, tokens,
+                       (int)k, (int)E, counts);
+  hipLaunchKernelGGL(k_route_scan, dim3(1), dim3(1024), 0, s, counts, nchunks, (int)E, seg_offsets);
+  if (tokens > 0)
+    hipLaunchKernelGGL(k_route_scatter, dim3((unsigned)nchunks), dim3(kChunk), E * (kChunk / 32) * sizeof(uint32_t), s,
+                       topk_ids, tokens, (int)k, (int)E, static_cast<const int32_t*>(counts), row_index, pair_row);
+  return bsqh::launch_status();
+}
+
 extern "C" int bsq_route(const int32_t* topk_ids, int64_t tokens, int64_t k, int64_t E, int32_t* row_index,
                          int64_t* seg_offsets, int32_t* pair_row, void* ws, size_t ws_bytes, bsq_stream_t stream) {
   BSQ_REQUIRE(tokens >= 0 && k >= 1 && k <= 64 && E >= 1 && E <= 1024, BSQ_E_SHAPE);
   BSQ_REQUIRE(tokens * k < (int64_t)1 << 31, BSQ_E_SHAPE);
   BSQ_REQUIRE(seg_offsets, BSQ_E_NULL);
-  hipStream_t s = bsqh::as_stream(stream);
-  const int64_t nchunks = (tokens + kChunk - 1) / kChunk;
   if (tokens > 0) {
     BSQ_REQUIRE(topk_ids && row_index && pair_row && ws, BSQ_E_NULL);
     BSQ_REQUIRE(((uintptr_t)ws & 3) == 0, BSQ_E_ALIGN);
     BSQ_REQUIRE(ws_bytes >= bsq_route_workspace(tokens, E), BSQ_E_WORKSPACE);
-    hipLaunchKernelGGL(k_route_count, dim3((unsigned)nchunks), dim3(kChunk), E * sizeof(int32_t), s, topk_ids, tokens,
-                       (int)k, (int)E, static_cast<int32_t*>(ws));
   }
-  hipLaunchKernelGGL(k_route_scan, dim3(1), dim3(1024), 0, s, static_cast<int32_t*>(ws), nchunks, (int)E, seg_offsets);
-  if (tokens > 0)
-    hipLaunchKernelGGL(k_route_scatter, dim3((unsigned)nchunks), dim3(kChunk), E * (kChunk / 32) * sizeof(uint32_t), s,
-                       topk_ids, tokens, (int)k, (int)E, static_cast<const int32_t*>(ws), row_index, pair_row);
-  return bsqh::launch_status();
+  return route_launch(topk_ids, tokens, k, E, row_index, seg_offsets, pair_row, static_cast<int32_t*>(ws),
+                      bsqh::as_stream(stream));
+}
+
+// ---------------------------------------------------------------- no-alloc
+// Routing for callers that cannot allocate: the per-chunk counts live in a
+// file-scope device array instead of a caller workspace. Each GPU holds its
+// own copy for the life of the process; host code reaches it only through
+// the address that hipGetSymbolAddress returns on that device (the array's
+// name in host code is a host-side stand-in, not a device address).
+constexpr size_t kRouteScratchBytes = BSQ_ROUTE_NOALLOC_MAX_BYTES;
+static __device__ __align__(256) uint8_t scratch[kRouteScratchBytes];
+
+constexpr int kMaxDevices = 64;
+static void* g_scratch_ptr[kMaxDevices];
+static std::mutex g_scratch_mu;
+
+// Device address of `scratch` on the current device, looked up once per device.
+static int scratch_ptr(void** out) {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return BSQ_E_LAUNCH;
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    void* p = nullptr;
+    if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || !p) return BSQ_E_LAUNCH;
+    g_scratch_ptr[dev] = p;
+  }
+  *out = g_scratch_ptr[dev];
+  return BSQ_OK;
+}
+
+extern "C" int bsq_route_noalloc(const int32_t* topk_ids, int64_t tokens, int64_t k, int64_t E, int32_t* row_index,
+                                 int64_t* seg_offsets, int32_t* pair_row, bsq_stream_t stream) {
+  BSQ_REQUIRE(tokens >= 0 && k >= 1 && k <= 64 && E >= 1 && E <= 1024, BSQ_E_SHAPE);
+  BSQ_REQUIRE(tokens * k < (int64_t)1 << 31, BSQ_E_SHAPE);
+  BSQ_REQUIRE(seg_offsets, BSQ_E_NULL);
+  if (tokens > 0) BSQ_REQUIRE(topk_ids && row_index && pair_row, BSQ_E_NULL);
+  BSQ_REQUIRE(bsq_route_workspace(tokens, E) <= kRouteScratchBytes, BSQ_E_WORKSPACE);
+  void* counts = nullptr;
+  const int st = scratch_ptr(&counts);
+  if (st != BSQ_OK) return st;
+  return route_launch(topk_ids, tokens, k, E, row_index, seg_offsets, pair_row, static_cast<int32_t*>(counts),
+                      bsqh::as_stream(stream));
 }
 
 extern "C" const char* bsq_status_string(int status) {

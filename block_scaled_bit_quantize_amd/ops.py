@@ -288,6 +288,21 @@ def route(topk_ids, num_experts):
     return row_index, seg, pair_row
 
 
+def route_noalloc(topk_ids, num_experts, row_index, seg_offsets, pair_row):
+    """route() into caller-provided outputs with no device allocation: the
+    library's own per-GPU array holds the per-chunk counts (tokens x E up to
+    the 1 MiB limit of BSQ_ROUTE_NOALLOC_MAX_BYTES). Calls on one GPU that
+    overlap in time race."""
+    lib = load_library()
+    _dev(topk_ids, row_index, seg_offsets, pair_row)
+    T, k = topk_ids.shape
+    if row_index.numel() != T * k or pair_row.numel() != T * k or seg_offsets.numel() != num_experts + 1:
+        raise BsqError("route_noalloc: output sizes do not match topk_ids and num_experts")
+    check(lib.bsq_route_noalloc(topk_ids.data_ptr(), T, k, num_experts, row_index.data_ptr(), seg_offsets.data_ptr(),
+                                pair_row.data_ptr(), _stream()), "bsq_route_noalloc")
+    return row_index, seg_offsets, pair_row
+
+
 def rht_s2f6_encode(x, signs):
     """Combine-codec sender: x [R, C] (float32 or bfloat16, C % 32 == 0) ->
     (codes u8 [R, C] two's-complement S2F6, scales u8 [R, C/32] UE8M0) of the

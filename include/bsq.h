@@ -338,6 +338,23 @@ int bsq_route(const int32_t* topk_ids, int64_t tokens, int64_t k, int64_t E, int
               int64_t* seg_offsets, int32_t* pair_row, void* ws, size_t ws_bytes,
               bsq_stream_t stream);
 
+/* bsq_route_noalloc: bsq_route for callers that cannot allocate device
+ * memory (code under HIP graph capture, tight serving loops, harnesses that
+ * forbid hipMalloc). Same arguments and outputs as bsq_route minus the
+ * workspace: the per-chunk counts live in a library-owned device array of
+ * BSQ_ROUTE_NOALLOC_MAX_BYTES per GPU (held until the process ends). Makes
+ * no hipMalloc/hipFree call. Every slot it reads is written earlier in the
+ * same call, so nothing carries over between calls; all calls on one GPU
+ * share the array, so calls that overlap in time on one GPU (other streams,
+ * other host threads) race and must be serialised by the caller.
+ * Errors: as bsq_route; WORKSPACE when bsq_route_workspace(tokens, E)
+ * exceeds BSQ_ROUTE_NOALLOC_MAX_BYTES (e.g. E = 64 allows 1,048,576 tokens).
+ * ---------------------------------------------------------------------- */
+#define BSQ_ROUTE_NOALLOC_MAX_BYTES ((size_t)1 << 20)
+int bsq_route_noalloc(const int32_t* topk_ids, int64_t tokens, int64_t k, int64_t E,
+                      int32_t* row_index, int64_t* seg_offsets, int32_t* pair_row,
+                      bsq_stream_t stream);
+
 /* ------------------------------------------------------------------------
  * Combine codec ("Quantized communications": before the combine exchange an
  * expert output row is rotated by a 32-dimensional random Hadamard transform

@@ -193,3 +193,11 @@ def test_gemm_and_route_validation(lib):
     assert rt(FAKE, 10, 2, 2000, FAKE, FAKE, FAKE, FAKE, 1 << 20, None) == E_SHAPE
     assert rt(FAKE, 10, 2, 4, FAKE, None, FAKE, FAKE, 1 << 20, None) == E_NULL
     assert rt(FAKE, 10, 2, 4, FAKE, FAKE, FAKE, FAKE, 4, None) == E_WORKSPACE
+    rn = lib.bsq_route_noalloc  # checked before any device call
+    assert rn(FAKE, 10, 0, 4, FAKE, FAKE, FAKE, None) == E_SHAPE
+    assert rn(FAKE, 10, 2, 4, FAKE, None, FAKE, None) == E_NULL
+    assert rn(None, 10, 2, 4, FAKE, FAKE, FAKE, None) == E_NULL
+    # counts need ceil(T / 256) * E int32 slots: 1 MiB holds 4096 chunks at E = 64
+    assert rn(FAKE, 4096 * 256 + 1, 1, 64, FAKE, FAKE, FAKE, None) == E_WORKSPACE
+    assert rn(FAKE, 256 * 256 + 1, 1, 1024, FAKE, FAKE, FAKE, None) == E_WORKSPACE
+    assert lib.bsq_route_workspace(4096 * 256, 64) == _lib.ROUTE_NOALLOC_MAX_BYTES
