@@ -36,6 +36,26 @@ METRIC = "quantize/requant GB/s (% HBM peak); NVFP4 expert grouped-GEMM TFLOPS (
 HBM_PEAK_GBS = 8000.0            # MI355X HBM3E, published
 MFMA_PEAK_TFLOPS = {"f16": 2500.0, "bf16": 2500.0, "fp8": 5000.0, "fp4": 10100.0}  # dense, published
 
+# The pages' contraction dtype of each GEMM stage: NVFP4 forward GEMMs against
+# the FP4 MFMA peak, MXFP8 backward GEMMs against the FP8 peak. They execute
+# on the 16-bit MFMA (exact decode), reported beside as frac_of_mfma16_peak.
+GEMM_DTYPE = {"fprop": "fp4", "chain_w13": "fp4", "chain_w2_codec": "fp4", "w5_fprop": "fp4",
+              "dgrad": "fp8", "wgrad": "fp8"}
+
+
+def rate_entry(name, ms, unit, work):
+    """ms, achieved, peak and fraction of one stage (HBM or MFMA roofline)."""
+    if unit == "GB/s":
+        ach = work / (ms * 1e-3) / 1e9
+        return {"ms": round(ms, 4), "achieved": round(ach, 2), "unit": unit, "peak": HBM_PEAK_GBS,
+                "frac": round(ach / HBM_PEAK_GBS, 4)}
+    ach = work / (ms * 1e-3) / 1e12
+    dt = GEMM_DTYPE[name]
+    peak = MFMA_PEAK_TFLOPS[dt]
+    return {"ms": round(ms, 4), "achieved": round(ach, 2), "unit": unit, "peak": peak, "peak_dtype": dt,
+            "frac": round(ach / peak, 4), "frac_of_mfma16_peak": round(ach / MFMA_PEAK_TFLOPS["f16"], 4)}
+
+
 T, H, E, K_TOP, F = 16384, 4096, 64, 8, 1536
 M = T * K_TOP
 
@@ -46,7 +66,6 @@ def parse():
     p.add_argument("--steps", type=int, default=10)
     p.add_argument("--warmup", type=int, default=3)
     p.add_argument("--no-cpu-baseline", action="store_true")
-    p.add_argument("--native-fp8", action="store_true", help="backward GEMMs on the scaled-FP8 MFMA variant")
     p.add_argument("--stages", default="", help="comma list of stages to run (profiling aid); default all")
     p.add_argument("--copy-calibration", action="store_true",
                    help="after timing, run a plain 512 MiB device copy three times (reference for HBM byte counters)")
@@ -99,16 +118,15 @@ def algorithmic(seg_host):
     }
 
 
-def stage_sources(stage, native_fp8=False):
+def stage_sources(stage):
     """HIP sources whose kernels a stage launches (their hash keys the
     committed HBM traffic figures)."""
     if stage in ("chain_w13", "chain_w2_codec"):
         return ("gemm.hip", "bsq_device.h", "bsq_internal.h")
     if stage == "chain_combine":
         return ("codec.hip", "bsq_device.h", "bsq_internal.h")
-    if stage in ("fprop", "dgrad", "wgrad"):
-        main = "gemm_mxfp8_native.hip" if native_fp8 and stage != "fprop" else "gemm.hip"
-        return (main, "bsq_device.h", "bsq_internal.h")
+    if stage in ("fprop", "dgrad", "wgrad", "w5_fprop"):
+        return ("gemm.hip", "bsq_device.h", "bsq_internal.h")
     if stage == "route":
         return ("route.hip", "bsq_internal.h")
     if stage.startswith("combine_"):
@@ -196,9 +214,9 @@ def cpu_baseline(seg_host, row_index_host):
     step_s = sum(times.values())
     flops = 3 * 2.0 * M * F * H
     return {"value": round(flops / step_s / 1e12, 6), "unit": "TFLOP/s", "cores": int(blas_threads), "kind": "oracle",
-            "sample": ("each stage on a slice of the step (2048 rows/tokens for quantize, requant and WGRAD; "
-                       "512 x 512 outputs for FPROP and DGRAD), NumPy oracle, time scaled by full/sample work; "
-                       "GEMM references are float64 BLAS"),
+            "sample": ("extrapolated: each stage timed on a slice of the step (2048 rows/tokens for quantize, "
+                       "requant and WGRAD; 512 x 512 outputs for FPROP and DGRAD), NumPy oracle, time scaled by "
+                       "full/sample work; GEMM references are float64 BLAS"),
             "step_seconds_equiv": round(step_s, 3),
             "stage_seconds_equiv": {k: round(v, 3) for k, v in times.items()}}
 
@@ -240,20 +258,16 @@ def workload5(torch, bsq, dev, reps=5):
     """Workload 5 (65536 tokens, hidden 7168, 128 experts of 2048 x 7168, top-8 with Zipf(1.1) expert
     popularity, Student-t(3) activations): per-token Four Over Six activation quantize, per-expert weight
     quantize and the NVFP4 grouped GEMM over the skewed segments, each timed on its own (HIP events,
-    mean of `reps` calls). Activations and weights are drawn on the GPU from a seeded torch generator
-    (the same distributions as the parity tests' NumPy inputs); the routing is the parity tests' own."""
+    mean of `reps` calls), on the seeded inputs the parity tests use (synth). Carries its own roofline
+    object for its dominant kernel, the GEMM."""
     import numpy as np
 
     import synth
     p = synth.WORKLOADS[5]
     T5, H5, E5, F5, k5 = p["tokens"], p["hidden"], p["experts"], p["ffn"], p["topk"]
-    gen = torch.Generator(device=dev)
-    gen.manual_seed(5)
-    # Student-t with 3 degrees of freedom: z / sqrt(chi2_3 / 3), chi2_3 the sum of three squared normals
-    chi = sum(torch.randn((T5, H5), generator=gen, device=dev) ** 2 for _ in range(3))
-    x = (torch.randn((T5, H5), generator=gen, device=dev) * torch.rsqrt(chi / 3.0)).to(torch.bfloat16)
-    del chi
-    w = (torch.randn((E5, F5, H5), generator=gen, device=dev) * p["w_std"]).to(torch.bfloat16)
+    to_bf16 = lambda a: torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).to(dev).view(torch.bfloat16)
+    x = to_bf16(synth.moe_activations(5))
+    w = to_bf16(synth.moe_weights(5))
     ids = torch.from_numpy(synth.moe_routing(5)).to(dev)
     ri, seg, _ = bsq.route(ids, E5)
     M5 = T5 * k5
@@ -265,8 +279,8 @@ def workload5(torch, bsq, dev, reps=5):
         "quant_x": (lambda: bsq.quantize_nvfp4(x, "row", four_over_six=True), "GB/s",
                     T5 * H5 * 2 + nv(T5, H5) + T5 * 4),
         "quant_w": (lambda: bsq.quantize_nvfp4(w, "tensor"), "GB/s", E5 * F5 * H5 * 2 + nv(E5 * F5, H5) + E5 * 4),
-        "fprop": (lambda: bsq.grouped_gemm_nvfp4(xq[0], xq[1], xq[2], wq[0], wq[1], wq[2], seg, M5, row_index=ri),
-                  "TFLOP/s", 2.0 * M5 * F5 * H5),
+        "w5_fprop": (lambda: bsq.grouped_gemm_nvfp4(xq[0], xq[1], xq[2], wq[0], wq[1], wq[2], seg, M5, row_index=ri),
+                     "TFLOP/s", 2.0 * M5 * F5 * H5),
     }
     out = {}
     for name, (fn, unit, work) in calls.items():
@@ -279,17 +293,14 @@ def workload5(torch, bsq, dev, reps=5):
             fn()
         b.record()
         torch.cuda.synchronize()
-        ms = a.elapsed_time(b) / reps
-        if unit == "GB/s":
-            ach, peak = work / (ms * 1e-3) / 1e9, HBM_PEAK_GBS
-        else:
-            ach, peak = work / (ms * 1e-3) / 1e12, MFMA_PEAK_TFLOPS["f16"]
-        out[name] = {"ms": round(ms, 4), "achieved": round(ach, 2), "unit": unit, "peak": peak,
-                     "frac": round(ach / peak, 4)}
+        out[name] = rate_entry(name, a.elapsed_time(b) / reps, unit, work)
+    g = out["w5_fprop"]
+    out["roofline"] = {"bound": "mfma", "kernel": "w5_fprop", "achieved": g["achieved"], "peak": g["peak"],
+                       "unit": g["unit"], "frac": g["frac"], "frac_of_mfma16_peak": g["frac_of_mfma16_peak"],
+                       "traffic": read_traffic("w5_fprop", kernel_sha(*stage_sources("w5_fprop")))}
     out["segments"] = {"experts": int(E5), "min_rows": int(lens.min()), "max_rows": int(lens.max()),
                        "total_rows": int(M5)}
-    out["what"] = ("workload 5 (Zipf-skewed MoE forward), outside the step; GEMM fraction against the fp16 "
-                   "MFMA peak it runs on")
+    out["what"] = "workload 5 (Zipf-skewed MoE forward, seeded synth inputs), outside the step"
     del x, w, xq, wq
     torch.cuda.empty_cache()
     return out
@@ -298,12 +309,14 @@ def workload5(torch, bsq, dev, reps=5):
 def chain_forward(torch, bsq, inp, algo, dev, pair_row, reps=5):
     """The expert forward chain (w13 GEMM, SwiGLU + per-row NVFP4, w2 GEMM with
     the RHT + S2F6 combine codec in its epilogue, combine) on the step's
-    tokens and routing with seeded w13 [E, 2F, H] and w2 [E, H, F]; each
+    tokens and routing with the seeded w13 [E, 2F, H] and w2 [E, H, F]; each
     stage timed with HIP events, median over `reps` passes."""
-    gen = torch.Generator(device=dev)
-    gen.manual_seed(3)
-    w13 = (torch.randn((E, 2 * F, H), generator=gen, device=dev) * 0.02).to(torch.bfloat16)
-    w2 = (torch.randn((E, H, F), generator=gen, device=dev) * 0.02).to(torch.bfloat16)
+    import numpy as np
+
+    import synth
+    to_bf16 = lambda a: torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).to(dev).view(torch.bfloat16)
+    w13 = to_bf16(synth.moe_w13(2))
+    w2 = to_bf16(synth.moe_w2(2))
     ri, seg, _ = bsq.route(inp["ids"], E)
     xc, xs, xo = bsq.quantize_nvfp4(inp["x"], "row", four_over_six=True)
     signs = 0x13579BDF
@@ -329,15 +342,11 @@ def chain_forward(torch, bsq, inp, algo, dev, pair_row, reps=5):
         if it:  # the first pass is warm-up
             for i, n in enumerate(names):
                 times[n].append(ev[i].elapsed_time(ev[i + 1]))
-    import numpy as np
     out = {}
     for n in names:
-        ms = float(np.median(times[n]))
         unit, work = algo[n]
-        ach = work / (ms * 1e-3) / (1e9 if unit == "GB/s" else 1e12)
-        peak = HBM_PEAK_GBS if unit == "GB/s" else MFMA_PEAK_TFLOPS["f16"]
-        out[n] = {"ms": round(ms, 4), "achieved": round(ach, 2), "unit": unit, "peak": peak,
-                  "frac": round(ach / peak, 4), "traffic": read_traffic(n, kernel_sha(*stage_sources(n)))}
+        out[n] = rate_entry(n, float(np.median(times[n])), unit, work)
+        out[n]["traffic"] = read_traffic(n, kernel_sha(*stage_sources(n)))
     out["ms_total"] = round(sum(out[n]["ms"] for n in names), 4)
     out["what"] = ("MoE expert forward (w13 GEMM -> SwiGLU + NVFP4 -> w2 GEMM with RHT-32 + S2F6 epilogue -> "
                    "combine), outside the step")
@@ -410,12 +419,11 @@ def main():
             mark("requant_x")
         wtc, wts = state["wt"]
         if run("dgrad"):
-            state["dx"] = bsq.grouped_gemm_mxfp8(False, state["gq"][0], state["gq"][1], wtc, wts, seg_, M, H, F,
-                                                 native=args.native_fp8)
+            state["dx"] = bsq.grouped_gemm_mxfp8(False, state["gq"][0], state["gq"][1], wtc, wts, seg_, M, H, F)
             mark("dgrad")
         if run("wgrad"):
             state["dw"] = bsq.grouped_gemm_mxfp8(True, state["gt"][0], state["gt"][1], state["xt"][0], state["xt"][1],
-                                                 seg_, F, H, native=args.native_fp8)
+                                                 seg_, F, H)
             mark("wgrad")
 
     for _ in range(args.warmup):
@@ -438,27 +446,19 @@ def main():
     algo = algorithmic(seg_host)
     kernels = {}
     for name, ts in per_stage.items():
-        ms = float(np.median(ts))
         unit, work = algo[name]
-        if unit == "GB/s":
-            ach = work / (ms * 1e-3) / 1e9
-            peak = HBM_PEAK_GBS
-        else:
-            ach = work / (ms * 1e-3) / 1e12
-            peak = MFMA_PEAK_TFLOPS["f16" if name == "fprop" else ("fp8" if args.native_fp8 else "bf16")]
-        kernels[name] = {"ms": round(ms, 4), "achieved": round(ach, 2), "unit": unit, "peak": peak,
-                         "frac": round(ach / peak, 4)}
-        if unit != "GB/s":  # the contraction also against the block-scaled FP8 and FP4 MFMA peaks
-            kernels[name]["frac_of_fp8_peak"] = round(ach / MFMA_PEAK_TFLOPS["fp8"], 4)
-            kernels[name]["frac_of_fp4_peak"] = round(ach / MFMA_PEAK_TFLOPS["fp4"], 4)
+        kernels[name] = rate_entry(name, float(np.median(ts)), unit, work)
 
     gemm_flops = sum(algo[n][1] for n in ("fprop", "dgrad", "wgrad") if n in kernels)
     value = gemm_flops / (ms_per_step * 1e-3) / 1e12
     dom = max(kernels, key=lambda n: kernels[n]["ms"])
     dk = kernels[dom]
-    traffic = read_traffic(dom, kernel_sha(*stage_sources(dom, args.native_fp8)))
+    traffic = read_traffic(dom, kernel_sha(*stage_sources(dom)))
     roofline = {"bound": "hbm" if dk["unit"] == "GB/s" else "mfma", "kernel": dom, "achieved": dk["achieved"],
                 "peak": dk["peak"], "unit": dk["unit"], "frac": dk["frac"], "traffic": traffic}
+    if "frac_of_mfma16_peak" in dk:
+        roofline["peak_dtype"] = dk["peak_dtype"]
+        roofline["frac_of_mfma16_peak"] = dk["frac_of_mfma16_peak"]
 
     # Alternatives to a step stage, timed on their own after the step (not in
     # ms_per_step): the 16x16 square-tile weight quantizer writing W and W^T.
@@ -483,11 +483,8 @@ def main():
             "alternative_to": "quant_w + requant_w where the backward reads W^T in NVFP4 (square tiles) instead of SR MXFP8"}
         # the combine codec (RHT-32 + block-scaled S2F6) on the expert output
         # rows of the layer's combine: [tokens * topk, hidden] bf16, seeded
-        gen = torch.Generator(device=dev)
-        gen.manual_seed(2)
-        payload = torch.randn((M, H), generator=gen, device=dev, dtype=torch.float32)
-        payload = torch.where(torch.rand((M, H), generator=gen, device=dev) < 1e-3, payload * 20.0, payload)
-        payload = payload.to(torch.bfloat16)
+        import synth
+        payload = torch.from_numpy(synth.combine_rows(M, H).view(np.int16)).to(dev).view(torch.bfloat16)
         _, _, pair_row = bsq.route(inp["ids"], E)
         signs = 0x9E3779B9
         enc = bsq.rht_s2f6_encode(payload, signs)
@@ -528,11 +525,11 @@ def main():
     line = {
         "metric": METRIC, "value": round(value, 3), "unit": "TFLOP/s", "n_gpus": 1, "steps": args.steps,
         "warmup": args.warmup, "ms_per_step": round(ms_per_step, 4), "higher_is_better": True, "scaling": "weak",
-        "vs_baseline": None, "dtype": "f16/bf16 MFMA (fp8 MFMA with --native-fp8), f32 accumulate",
+        "vs_baseline": None,
+        "dtype": "f16 (NVFP4) / bf16 (MXFP8) MFMA on exactly decoded operands, f32 accumulate",
         "data": "synthetic (seeded; bf16 N(0,1) activations, N(0,0.02) weights, N(0,1e-3) gradients with 0.1% x50)",
         "config": {"workload": "moe_expert_fwd_bwd", "tokens": T, "hidden": H, "experts": E, "topk": K_TOP,
-                   "ffn": F, "global_batch": T, "parallelism": "none (1 GPU)",
-                   "backward_gemm": "native-fp8" if args.native_fp8 else "exact-bf16"},
+                   "ffn": F, "global_batch": T, "parallelism": "none (1 GPU)"},
         "kernels": kernels,
         "roofline": roofline,
         "alternatives": alternatives,

@@ -253,12 +253,10 @@ def grouped_gemm_nvfp4_s2f6(a_codes, a_scales, a_outer, b_codes, b_scales, b_out
 
 
 def grouped_gemm_mxfp8(wgrad, a_codes, a_scales, b_codes, b_scales, seg_offsets, M, N, K=0, out=None,
-                       out_dtype=None, native=False):
+                       out_dtype=None):
     """wgrad=False (DGRAD): a [M_total(=M), K], b [E, N, K] -> [M, N] (bf16
     by default). wgrad=True (WGRAD): a, b flat padded per-segment transposed
-    layouts with M and N rows per expert -> [E, M, N] (float32 by default).
-    native=True runs the scaled-FP8-MFMA variant (faster, less accurate
-    accumulation inside each instruction)."""
+    layouts with M and N rows per expert -> [E, M, N] (float32 by default)."""
     lib = load_library()
     _dev(a_codes, a_scales, b_codes, b_scales, seg_offsets)
     E = seg_offsets.numel() - 1
@@ -266,8 +264,7 @@ def grouped_gemm_mxfp8(wgrad, a_codes, a_scales, b_codes, b_scales, seg_offsets,
         dt = out_dtype or (torch.float32 if wgrad else torch.bfloat16)
         shape = (E, M, N) if wgrad else (M, N)
         out = torch.empty(shape, dtype=dt, device=a_codes.device)
-    fn = lib.bsq_grouped_gemm_mxfp8_native if native else lib.bsq_grouped_gemm_mxfp8
-    check(fn(1 if wgrad else 0, a_codes.data_ptr(), a_scales.data_ptr(), b_codes.data_ptr(), b_scales.data_ptr(),
+    check(lib.bsq_grouped_gemm_mxfp8(1 if wgrad else 0, a_codes.data_ptr(), a_scales.data_ptr(), b_codes.data_ptr(), b_scales.data_ptr(),
              seg_offsets.data_ptr(), E, M, N, K, out.data_ptr(), _OUT[out.dtype], _stream()), "bsq_grouped_gemm_mxfp8")
     return out
 

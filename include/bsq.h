@@ -302,22 +302,11 @@ int bsq_grouped_gemm_nvfp4_s2f6(const uint8_t* a_codes, const uint8_t* a_scales,
  * accumulated in FP32; out_dtype BSQ_BF16 (round to nearest even) or BSQ_F32.
  * Codes and out 16-byte aligned.
  * Errors: NULL, SHAPE, ALIGN, DTYPE, ENUM, LAUNCH.
- *
- * bsq_grouped_gemm_mxfp8_native: the same operation on CDNA4's scaled FP8
- * MFMA (E8M0 per 32 natively, no decode, FP8 MFMA rate). Measured on gfx950,
- * the FP8 dot product inside one instruction keeps about 15 bits below its
- * largest product, so outputs that nearly cancel can carry relative errors
- * above 2e-3; K % 128 == 0 for DGRAD; A/B scales 4-byte aligned for DGRAD.
  * ---------------------------------------------------------------------- */
 int bsq_grouped_gemm_mxfp8(int wgrad, const uint8_t* a_codes, const uint8_t* a_scales,
                            const uint8_t* b_codes, const uint8_t* b_scales,
                            const int64_t* seg_offsets, int64_t E, int64_t M_total, int64_t N,
                            int64_t K, void* out, int out_dtype, bsq_stream_t stream);
-int bsq_grouped_gemm_mxfp8_native(int wgrad, const uint8_t* a_codes, const uint8_t* a_scales,
-                                  const uint8_t* b_codes, const uint8_t* b_scales,
-                                  const int64_t* seg_offsets, int64_t E, int64_t M_total,
-                                  int64_t N, int64_t K, void* out, int out_dtype,
-                                  bsq_stream_t stream);
 
 /* ------------------------------------------------------------------------
  * Routing of tokens to expert segments ("Quantized communications": a router

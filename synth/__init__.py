@@ -3,7 +3,9 @@ benchmark. Holds no arithmetic of the quantization method: only random draws
 with the shapes and distributions of the five workloads, bf16 rounding of the
 draws, and routing draws.
 
-Workloads (data seed 1000 + workload number, one PCG64 sub-stream per tensor):
+Workloads (data seed 1000 + workload number; tensor t of a workload is drawn in
+chunks of 2^24 elements, chunk c from its own PCG64 stream seeded with
+[1000 + workload, t, c], so that chunks are generated in parallel threads):
   1 single tensor: X, W float32 [256, 256] ~ N(0,1), 8 distinct seeded
     positions of each scaled by 100.
   2 MoE expert forward: x bf16 [16384, 4096] ~ N(0,1); W bf16 [64, 1536, 4096]
@@ -21,6 +23,9 @@ Combine payload (the expert output rows that the combine codec carries):
     workload 2's dispatched rows, bf16 [131072, 4096] ~ N(0, 1), 0.1% of
     entries scaled by 20 (outliers).
 """
+import os
+from concurrent.futures import ThreadPoolExecutor
+
 import numpy as np
 
 WORKLOADS = {
@@ -49,6 +54,31 @@ def bf16_bits(f32):
 def bf16_to_f32(bits):
     """bfloat16 bit patterns -> float32 (exact)."""
     return (np.asarray(bits, dtype=np.uint16).astype(np.uint32) << np.uint32(16)).view(np.float32)
+
+
+def _par_bf16(workload, stream, shape, draw):
+    """bf16 bits [shape] whose chunk c of 2^24 elements is draw(rng_c, m), rng_c
+    seeded with [1000 + workload, stream, c]; chunks run on a thread pool
+    (NumPy's fills and ufuncs release the GIL). The result does not depend on
+    the number of threads."""
+    n = int(np.prod(shape))
+    out = np.empty(n, dtype=np.uint16)
+
+    def one(c):
+        s = c * _CHUNK
+        m = min(_CHUNK, n - s)
+        rng = np.random.Generator(np.random.PCG64(np.random.SeedSequence([1000 + int(workload), int(stream), c])))
+        out[s:s + m] = bf16_bits(draw(rng, m))
+
+    chunks = (n + _CHUNK - 1) // _CHUNK
+    workers = max(1, min(16, os.cpu_count() or 1, chunks))
+    if workers == 1:
+        for c in range(chunks):
+            one(c)
+    else:
+        with ThreadPoolExecutor(max_workers=workers) as ex:
+            list(ex.map(one, range(chunks)))
+    return out.reshape(shape)
 
 
 def normal_bf16(shape, std, rng):
@@ -108,14 +138,15 @@ def moe_activations(workload, tokens=None, hidden=None):
     p = WORKLOADS[workload]
     shape = (tokens or p["tokens"], hidden or p["hidden"])
     if workload == 5:
-        return student_t_bf16(shape, 3, rng_for(5, 0))
-    return normal_bf16(shape, 1.0, rng_for(workload, 0))
+        return _par_bf16(5, 0, shape, lambda rng, m: rng.standard_t(3, m).astype(np.float32))
+    return _par_bf16(workload, 0, shape, lambda rng, m: rng.standard_normal(m, dtype=np.float32))
 
 
 def moe_weights(workload, experts=None, ffn=None, hidden=None):
     p = WORKLOADS[workload]
     shape = (experts or p["experts"], ffn or p["ffn"], hidden or p["hidden"])
-    return normal_bf16(shape, p["w_std"], rng_for(workload, 1))
+    std = np.float32(p["w_std"])
+    return _par_bf16(workload, 1, shape, lambda rng, m: rng.standard_normal(m, dtype=np.float32) * std)
 
 
 def moe_routing(workload, tokens=None, experts=None):
@@ -130,40 +161,37 @@ def moe_routing(workload, tokens=None, experts=None):
 def output_grad(rows, cols, workload=4):
     """g bf16 [rows, cols] ~ N(0, 1e-3) with 0.1% of entries scaled by 50."""
     p = WORKLOADS[4]
-    rng = rng_for(workload, 3)
-    n = rows * cols
-    out = np.empty(n, dtype=np.uint16)
-    for s in range(0, n, _CHUNK):
-        m = min(_CHUNK, n - s)
+
+    def draw(rng, m):
         v = rng.standard_normal(m, dtype=np.float32) * np.float32(p["g_std"])
         spike = rng.random(m) < p["spike_frac"]
         v[spike] *= np.float32(p["spike_scale"])
-        out[s:s + m] = bf16_bits(v)
-    return out.reshape(rows, cols)
+        return v
+    return _par_bf16(workload, 3, (rows, cols), draw)
 
 
 def combine_rows(rows, cols, workload=2):
     """Expert output rows bf16 [rows, cols] ~ N(0, 1) with 0.1% of entries
     scaled by 20."""
-    rng = rng_for(workload, 4)
-    n = rows * cols
-    out = np.empty(n, dtype=np.uint16)
-    for s in range(0, n, _CHUNK):
-        m = min(_CHUNK, n - s)
+    def draw(rng, m):
         v = rng.standard_normal(m, dtype=np.float32)
         spike = rng.random(m) < 1e-3
         v[spike] *= np.float32(20.0)
-        out[s:s + m] = bf16_bits(v)
-    return out.reshape(rows, cols)
+        return v
+    return _par_bf16(workload, 4, (rows, cols), draw)
 
 
 def moe_w13(workload=2):
     """Gate and up projections bf16 [E, 2 * ffn, hidden] ~ N(0, w_std^2)."""
     p = WORKLOADS[workload]
-    return normal_bf16((p["experts"], 2 * p["ffn"], p["hidden"]), p["w_std"], rng_for(workload, 5))
+    std = np.float32(p["w_std"])
+    return _par_bf16(workload, 5, (p["experts"], 2 * p["ffn"], p["hidden"]),
+                     lambda rng, m: rng.standard_normal(m, dtype=np.float32) * std)
 
 
 def moe_w2(workload=2):
     """Down projections bf16 [E, hidden, ffn] ~ N(0, w_std^2)."""
     p = WORKLOADS[workload]
-    return normal_bf16((p["experts"], p["hidden"], p["ffn"]), p["w_std"], rng_for(workload, 6))
+    std = np.float32(p["w_std"])
+    return _par_bf16(workload, 6, (p["experts"], p["hidden"], p["ffn"]),
+                     lambda rng, m: rng.standard_normal(m, dtype=np.float32) * std)

@@ -182,9 +182,6 @@ def test_gemm_and_route_validation(lib):
     m = lib.bsq_grouped_gemm_mxfp8
     assert m(2, FAKE, FAKE, FAKE, FAKE, FAKE, 2, 256, 256, 128, FAKE, 1, None) == E_ENUM
     assert m(0, FAKE, FAKE, FAKE, FAKE, FAKE, 2, 256, 256, 100, FAKE, 1, None) == E_SHAPE
-    mn = lib.bsq_grouped_gemm_mxfp8_native
-    assert mn(0, FAKE, FAKE, FAKE, FAKE, FAKE, 2, 256, 256, 64, FAKE, 1, None) == E_SHAPE   # K % 128
-    assert mn(0, FAKE, FAKE, FAKE, FAKE, FAKE, 2, 256, 256, 128, FAKE, 3, None) == E_DTYPE
     assert m(1, FAKE, FAKE, FAKE, FAKE, FAKE, 2, 200, 256, 0, FAKE, 0, None) == E_SHAPE
     assert m(0, FAKE, None, FAKE, FAKE, FAKE, 2, 256, 256, 128, FAKE, 1, None) == E_NULL
     assert m(0, FAKE, FAKE, FAKE, FAKE, FAKE, 2, 256, 256, 128, FAKE, 5, None) == E_DTYPE

@@ -19,12 +19,6 @@ pytestmark = pytest.mark.gpu
 f32 = np.float32
 
 
-# The scaled-FP8 MFMA keeps about 15 bits below the largest product of each
-# instruction (measured on gfx950), so its variant of the MXFP8 GEMM is held
-# to a floor of 2^-14 * sum|x w| instead of 2^-20.
-NATIVE_FP8_FLOOR = 2.0 ** -14
-
-
 def _check(y, yref, yabs, what, floor=G.ABS_FLOOR):
     """y: the float32 GEMM result (before output rounding) vs the float64 reference."""
     ok, ratio = G.within_tolerance(y, yref, yabs, floor)
@@ -150,10 +144,8 @@ def _mxfp8_from(rng, x, rnd=Q.SR):
     return Q.quantize_mxfp8(x, rnd, int(rng.integers(1 << 30)), 1)
 
 
-@pytest.mark.parametrize("native", [False, True])
-def test_gemm_mxfp8_dgrad_small(native):
-    log(f"gemm mxfp8 dgrad small native={native}")
-    floor = NATIVE_FP8_FLOOR if native else G.ABS_FLOOR
+def test_gemm_mxfp8_dgrad_small():
+    log("gemm mxfp8 dgrad small")
     rng = np.random.default_rng(6)
     E, N, K = 4, 512, 384
     seg = np.array([0, 100, 100, 357, 613], dtype=np.int64)
@@ -162,18 +154,15 @@ def test_gemm_mxfp8_dgrad_small(native):
     ac, as_ = _mxfp8_from(rng, g)
     bc, bs = _mxfp8_from(rng, wt)
     bc, bs = bc.reshape(E, N, K), bs.reshape(E, N, K // 32)
-    y = bsq.grouped_gemm_mxfp8(False, t(ac), t(as_), t(bc), t(bs), t(seg), 613, N, K, out_dtype=torch.float32,
-                               native=native)
-    y16 = bsq.grouped_gemm_mxfp8(False, t(ac), t(as_), t(bc), t(bs), t(seg), 613, N, K, native=native)
+    y = bsq.grouped_gemm_mxfp8(False, t(ac), t(as_), t(bc), t(bs), t(seg), 613, N, K, out_dtype=torch.float32)
+    y16 = bsq.grouped_gemm_mxfp8(False, t(ac), t(as_), t(bc), t(bs), t(seg), 613, N, K)
     yref, yabs = G.mxfp8_dgrad_ref(ac, as_, bc, bs, seg)
-    _check(h(y), yref, yabs, f"mxfp8 dgrad small native={native}", floor)
+    _check(h(y), yref, yabs, "mxfp8 dgrad small")
     _check_bf16(h(y16.view(torch.int16)), h(y), "mxfp8 dgrad small")
 
 
-@pytest.mark.parametrize("native", [False, True])
-def test_gemm_mxfp8_wgrad_small(native):
-    log(f"gemm mxfp8 wgrad small native={native}")
-    floor = NATIVE_FP8_FLOOR if native else G.ABS_FLOOR
+def test_gemm_mxfp8_wgrad_small():
+    log("gemm mxfp8 wgrad small")
     rng = np.random.default_rng(7)
     M, N = 256, 512
     seg = np.array([0, 0, 45, 245, 245, 374], dtype=np.int64)       # Kp = 0, 64, 224, 0, 160
@@ -181,20 +170,18 @@ def test_gemm_mxfp8_wgrad_small(native):
     xb = rng.standard_normal((374, N)).astype(f32)
     ac, as_ = Q.quantize_mxfp8_transposed(ga, seg, Q.SR, 1, 2)
     bc, bs = Q.quantize_mxfp8_transposed(xb, seg, Q.SR, 1, 3)
-    y = bsq.grouped_gemm_mxfp8(True, t(ac), t(as_), t(bc), t(bs), t(seg), M, N, native=native)
+    y = bsq.grouped_gemm_mxfp8(True, t(ac), t(as_), t(bc), t(bs), t(seg), M, N)
     yref, yabs = G.mxfp8_wgrad_ref(ac, as_, bc, bs, seg, M, N)
-    _check(h(y), yref, yabs, f"mxfp8 wgrad small native={native}", floor)
-    y16 = bsq.grouped_gemm_mxfp8(True, t(ac), t(as_), t(bc), t(bs), t(seg), M, N, native=native,
+    _check(h(y), yref, yabs, "mxfp8 wgrad small")
+    y16 = bsq.grouped_gemm_mxfp8(True, t(ac), t(as_), t(bc), t(bs), t(seg), M, N,
                                  out_dtype=torch.bfloat16)
     assert torch.equal(y16, y.to(torch.bfloat16))
 
 
-@pytest.mark.parametrize("native", [False, True])
-def test_gemm_mxfp8_workload4_full(native):
+def test_gemm_mxfp8_workload4_full():
     """DGRAD dx[131072, 4096] = g w_q and WGRAD dw[64, 1536, 4096] = g^T x_q at
     full size with workload 2's routing; sampled rows / experts."""
-    log(f"gemm mxfp8 workload4 native={native}: setup")
-    floor = NATIVE_FP8_FLOOR if native else G.ABS_FLOOR
+    log("gemm mxfp8 workload4: setup")
     E, T, Kx, Ng = 64, 16384, 4096, 1536
     ids = synth.moe_routing(2)
     row_index, seg, _ = oroute(ids, E)
@@ -217,12 +204,11 @@ def test_gemm_mxfp8_workload4_full(native):
         c, sc = Q.requant_transpose_sr(p, s, o, Q.OUTER_TENSOR, Q.MXFP8, 42, 0, item0=e)
         bc[e], bs[e] = c[0], sc[0]
     log("gemm mxfp8 workload4: dgrad")
-    y = bsq.grouped_gemm_mxfp8(False, t(ac), t(as_), t(bc), t(bs), t(seg), M_total, Kx, Ng, out_dtype=torch.float32,
-                               native=native)
+    y = bsq.grouped_gemm_mxfp8(False, t(ac), t(as_), t(bc), t(bs), t(seg), M_total, Kx, Ng, out_dtype=torch.float32)
     ys = h(y[t(rows)])
     del y
     yref, yabs = G.mxfp8_dgrad_ref(ac, as_, bc, bs, seg, rows=rows)
-    _check(ys, yref, yabs, f"mxfp8 dgrad workload4 native={native}", floor)
+    _check(ys, yref, yabs, "mxfp8 dgrad workload4")
     # WGRAD: A = g^T per expert [1536, Kp_e], B = x_q^T per expert [4096, Kp_e]
     log("gemm mxfp8 workload4: wgrad setup")
     mpa, na = bsq.padded_segment_layout(seg, Ng)
@@ -244,8 +230,8 @@ def test_gemm_mxfp8_workload4_full(native):
         B[baseb[e]:baseb[e] + c.size], Bs[baseb[e] // 32:baseb[e] // 32 + sc.size] = c, sc
     del gf, x, g
     log("gemm mxfp8 workload4: wgrad")
-    dw = bsq.grouped_gemm_mxfp8(True, t(A), t(As), t(B), t(Bs), t(seg), Ng, Kx, native=native)
+    dw = bsq.grouped_gemm_mxfp8(True, t(A), t(As), t(B), t(Bs), t(seg), Ng, Kx)
     for e in experts:
         ys = h(dw[e])
         yref, yabs = G.mxfp8_wgrad_ref(A, As, B, Bs, seg, Ng, Kx, experts=[e])
-        _check(ys, yref[0], yabs[0], f"mxfp8 wgrad workload4 expert {e} native={native}", floor)
+        _check(ys, yref[0], yabs[0], f"mxfp8 wgrad workload4 expert {e}")

@@ -111,6 +111,25 @@ def test_mxfp8_dgrad_wgrad_brute_force():
                 assert abs(Fraction(float(dw[e, m, n])) - acc) <= abs(acc) * Fraction(1, 1 << 50)
 
 
+def test_dequantize_mxfp8_every_code_and_scale_against_torch():
+    """x = q * 2^(s - 127) for all 256 E4M3 codes under all 255 finite E8M0
+    scales, against torch's own float8_e4m3fn and float8_e8m0fnu decoders (a
+    library decode of both formats, independent of the oracle's tables); the
+    two NaN codes stay NaN."""
+    import torch
+    codes = np.tile(np.arange(256, dtype=np.uint8), (255, 1))                  # [scale, code]
+    scales = np.repeat(np.arange(255, dtype=np.uint8)[:, None], 256 // 32, axis=1)
+    got = Q.dequantize_mxfp8_f64(codes, scales)
+    q = torch.from_numpy(np.arange(256, dtype=np.uint8)).view(torch.float8_e4m3fn).to(torch.float64).numpy()
+    sv = torch.from_numpy(np.arange(255, dtype=np.uint8)).view(torch.float8_e8m0fnu).to(torch.float64).numpy()
+    want = sv[:, None] * q[None, :]             # exact: a 4-bit significand times a power of two
+    nan = np.isnan(want)
+    assert nan.sum() == 2 * 255 and np.array_equal(np.isnan(got), nan)
+    assert np.array_equal(got[~nan], want[~nan])
+    # the smallest and largest magnitudes: 2^-9 * 2^-127 and 448 * 2^127
+    assert got[0, 1] == 2.0 ** -136 and got[254, 0x7E] == 448.0 * 2.0 ** 127
+
+
 def test_tolerance_rule():
     y_ref = np.array([1.0, -2.0, 1e-9])
     ya = np.array([1.0, 2.0, 1.0])

@@ -327,6 +327,53 @@ def test_segmented_transposed_layout_and_padding():
     assert np.array_equal(blk, c2)
 
 
+def _token_table(rng, T, C):
+    """NVFP4 token rows with per-row outer scales over a wide range."""
+    x = rng.standard_normal((T, C)).astype(f32) * np.exp2(rng.integers(-6, 7, (T, 1))).astype(f32)
+    p, s, o = Q.quantize_nvfp4(x[None], Q.OUTER_ROW)
+    return p[0], s[0], o[0]
+
+
+@pytest.mark.parametrize("rnd", [Q.RN, Q.SR])
+def test_requant_segmented_gather_equals_pregathered_batch(rnd):
+    """Dispatched row m reads token row_gather[m] with that token's outer
+    scale. Segments of equal length R (a multiple of 32) start at element
+    e*C*R of the output, so segment e must equal the batch requantizer (item
+    e) applied to the table gathered here with NumPy indexing: a swapped or
+    shifted gather index, or an outer scale taken from the wrong row, breaks
+    the equality (SR draws included)."""
+    rng = np.random.default_rng(21)
+    T, C, R, nseg = 50, 64, 32, 3
+    p, s, o = _token_table(rng, T, C)
+    gather = rng.integers(0, T, nseg * R)                    # repeats and any order
+    seg = np.arange(nseg + 1, dtype=np.int64) * R
+    codes, scales = Q.requant_transpose_sr_segmented(p, s, o, Q.OUTER_ROW, gather, seg, 7, 3, rnd=rnd)
+    for e in range(nseg):
+        g = gather[e * R:(e + 1) * R]
+        c2, s2 = Q.requant_transpose_sr(p[g][None], s[g][None], o[g][None], Q.OUTER_ROW, Q.MXFP8, 7, 3, rnd=rnd,
+                                        item0=e)
+        assert np.array_equal(codes[e * C * R:(e + 1) * C * R], c2.reshape(-1))
+        assert np.array_equal(scales[e * C * R // 32:(e + 1) * C * R // 32], s2.reshape(-1))
+
+
+def test_requant_segmented_gather_ragged_equals_dequantize_then_gather():
+    """Ragged and empty segments: the result equals the transposed MXFP8
+    quantizer applied to the rows of the dequantized token table taken in
+    gather order (the whole table dequantized first, then indexed)."""
+    rng = np.random.default_rng(22)
+    T, C = 40, 64
+    p, s, o = _token_table(rng, T, C)
+    seg = np.array([0, 7, 7, 70, 101], dtype=np.int64)
+    gather = rng.integers(0, T, 101)
+    codes, scales = Q.requant_transpose_sr_segmented(p, s, o, Q.OUTER_ROW, gather, seg, 9, 3)
+    table = Q.dequantize_nvfp4(p[None], s[None], o[None], Q.OUTER_ROW)[0]
+    c2, s2 = Q.quantize_mxfp8_transposed(table[gather], seg, Q.SR, 9, 3)
+    assert np.array_equal(codes, c2) and np.array_equal(scales, s2)
+    # a shifted gather gives a different result (the check can fail)
+    c3, _ = Q.quantize_mxfp8_transposed(table[np.roll(gather, 1)], seg, Q.SR, 9, 3)
+    assert not np.array_equal(codes, c3)
+
+
 # ---------------------------------------------------------------- Four Over Six
 def _given(x):
     return Q.quantize_nvfp4(np.asarray(x, np.float32).reshape(1, 1, -1), Q.OUTER_GIVEN,
