@@ -38,7 +38,9 @@ __host__ __device__ inline int64_t pad32(int64_t n) { return (n + 31) / 32 * 32;
 
 // Tile plan for segmented layouts: slot -> (segment, token tile), and per
 // segment its start row, length and output element base (cols * sum of
-// earlier padded lengths). Offsets are clamped to [0, rows], so a malformed
+// earlier padded lengths). Offsets are clamped to [0, rows] and then replaced
+// by their running maximum, so segments never overlap and their padded
+// lengths sum to at most rows + 31 * nseg: a malformed (e.g. decreasing)
 // table cannot send a later kernel outside its buffers.
 // One workgroup of 1024 threads; num_segments <= 1024.
 __global__ __launch_bounds__(1024) void k_seg_plan(const int64_t* __restrict__ seg_offsets, int nseg, int64_t rows,
@@ -48,12 +50,23 @@ __global__ __launch_bounds__(1024) void k_seg_plan(const int64_t* __restrict__ s
                                                    int64_t* __restrict__ seg_len) {
   __shared__ int64_t s_tiles[1024];
   __shared__ int64_t s_pad[1024];
+  __shared__ int64_t s_hi[1024];
   const int t = threadIdx.x;
+  auto clampr = [&](int64_t v) { return v < 0 ? 0 : (v > rows ? rows : v); };
+  // running maximum of the clamped offsets 0..t (inclusive max scan)
+  s_hi[t] = t < nseg ? clampr(seg_offsets[t]) : 0;
+  __syncthreads();
+  for (int o = 1; o < 1024; o <<= 1) {
+    const int64_t v = t >= o ? s_hi[t - o] : 0;
+    __syncthreads();
+    s_hi[t] = s_hi[t] > v ? s_hi[t] : v;
+    __syncthreads();
+  }
   int64_t mp = 0, nt = 0;
   if (t < nseg) {
-    int64_t a = seg_offsets[t], b = seg_offsets[t + 1];
-    a = a < 0 ? 0 : (a > rows ? rows : a);
-    b = b < a ? a : (b > rows ? rows : b);
+    const int64_t a = s_hi[t];
+    int64_t b = clampr(seg_offsets[t + 1]);
+    b = b < a ? a : b;
     seg_start[t] = a;
     seg_len[t] = b - a;
     mp = pad32(b - a);

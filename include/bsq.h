@@ -182,8 +182,12 @@ int bsq_quantize_nvfp4_square(const void* x, int dtype, int64_t batch, int64_t r
  *              Needs bsq_quantize_mxfp8_workspace() bytes of workspace. The
  *              caller sizes codes for cols * sum_e Mp_e bytes and scales for
  *              a 32nd of that; cols * (rows + 31 * num_segments) bounds the sum
- *              for any valid seg_offsets (the sizes are not checked: they
- *              depend on the device-side offsets).
+ *              for any seg_offsets (the sizes are not checked: they depend on
+ *              the device-side offsets). Malformed offsets are read as
+ *              clamped to [0, rows] and then replaced by their running
+ *              maximum (a decreasing offset ends the earlier segments'
+ *              coverage: [0, R, 0, R] acts as [0, R, R, R]), so segments
+ *              never overlap and the bound holds.
  * rnd        BSQ_RN (nearest-even) or BSQ_SR.
  * seed, stream_id  select the random stream (SR only).
  * E8M0 rule: the smallest 2^e with a_b <= 448 * 2^e (e clamped to [-127,127];

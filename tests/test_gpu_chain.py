@@ -140,6 +140,61 @@ def test_chain_small_end_to_end():
     assert rel(out, ref) < 0.12
 
 
+def test_chain_stagewise_elementwise():
+    """The chain checked element by element: every GPU stage against the
+    oracle's stage applied to the GPU's own input for that stage. Quantizers,
+    SwiGLU + NVFP4 and the combine bit-exact; GEMMs within the accept rule
+    (and bf16 RNE of their fp32 result); the codec epilogue against the
+    float64 rotation of the exact product. The combined output is therefore
+    the oracle combine of the GPU's codes, element for element."""
+    log("chain stagewise")
+    rng = np.random.default_rng(15)
+    T, H, F, E, k = 300, 256, 256, 5, 2
+    mask = 0x0F1E2D3C
+    x_bits = synth.bf16_bits(rng.standard_normal((T, H)).astype(f32))
+    w13_bits = synth.bf16_bits((rng.standard_normal((E, 2 * F, H)) * 0.06).astype(f32))
+    w2_bits = synth.bf16_bits((rng.standard_normal((E, H, F)) * 0.06).astype(f32))
+    ids = np.stack([rng.choice(E, k, replace=False) for _ in range(T)]).astype(np.int32)
+    x, w13, w2 = (synth.bf16_to_f32(b).reshape(b.shape) for b in (x_bits, w13_bits, w2_bits))
+    row_index, seg, pair_row = oroute(ids, E)
+    ri, sg, pr = bsq.route(t(ids), E)
+    assert np.array_equal(h(ri), row_index) and np.array_equal(h(sg), seg) and np.array_equal(h(pr), pair_row)
+    M = T * k
+    # quantizers
+    xc, xs, xo = bsq.quantize_nvfp4(bf16_t(x_bits), "row", four_over_six=True)
+    oc, os_, oo = Q.quantize_nvfp4(x[None], Q.OUTER_ROW, four_over_six=True)
+    assert np.array_equal(h(xc), oc[0]) and np.array_equal(h(xs), os_[0])
+    assert np.array_equal(h(xo), np.asarray(oo).reshape(-1))
+    w13q = bsq.quantize_nvfp4(bf16_t(w13_bits), "tensor")
+    w2q = bsq.quantize_nvfp4(bf16_t(w2_bits), "tensor")
+    for gq, wf in ((w13q, w13), (w2q, w2)):
+        wc, ws, wo = Q.quantize_nvfp4(wf, Q.OUTER_TENSOR)
+        assert np.array_equal(h(gq[0]), wc) and np.array_equal(h(gq[1]), ws)
+        assert np.array_equal(h(gq[2]), np.asarray(wo).reshape(-1))
+    # w13 GEMM (bf16 out) on the quantized operands
+    h13 = bsq.grouped_gemm_nvfp4(xc, xs, xo, *w13q, sg, M, row_index=ri)
+    h13_32 = bsq.grouped_gemm_nvfp4(xc, xs, xo, *w13q, sg, M, row_index=ri, out_dtype=torch.float32)
+    yref, yabs = grouped_gemm_nvfp4_ref(oc[0], os_[0], np.asarray(oo).reshape(-1), row_index,
+                                        *(h(v) for v in w13q), seg)
+    bound = REL_TOL * np.abs(yref) + ABS_FLOOR * yabs
+    assert (np.abs(h(h13_32).astype(np.float64) - yref) <= bound).all()
+    assert torch.equal(h13, h13_32.to(torch.bfloat16))
+    # SwiGLU + per-row NVFP4 of the GPU's h13
+    hc, hs, ho = bsq.swiglu_quantize_nvfp4(h13)
+    h13_f = synth.bf16_to_f32(h(h13.view(torch.int16)).view(np.uint16)).reshape(M, 2 * F)
+    qc, qs, qo = CH.swiglu_quantize(h13_f, F)
+    assert np.array_equal(h(hc), qc) and np.array_equal(h(hs), qs)
+    assert np.array_equal(h(ho), np.asarray(qo).reshape(-1))
+    # w2 GEMM with the codec epilogue on the GPU's quantized hidden rows
+    codes, scales = bsq.grouped_gemm_nvfp4_s2f6(hc, hs, ho, *w2q, sg, M, mask)
+    y_ref, y_abs = grouped_gemm_nvfp4_ref(h(hc), h(hs), h(ho), None, *(h(v) for v in w2q), seg)
+    _check_codec_against_f64(h(codes), h(scales), y_ref, y_abs, mask)
+    # combine of the GPU's codes, bit-exact
+    out = bsq.rht_s2f6_combine(codes, scales, pr, k, mask, out_dtype=torch.float32)
+    want = CODEC.combine(h(codes), h(scales), pair_row, k, mask)
+    assert np.array_equal(h(out).view(np.uint32), want.view(np.uint32))
+
+
 def test_chain_workload2_full():
     """The chain at full size (16384 tokens, hidden 4096, ffn 1536, 64 experts,
     top-8): sampled tokens against the oracle run on just their experts."""

@@ -81,8 +81,10 @@ def test_gemm_nvfp4_workload1():
     _check_bf16(h(y16.view(torch.int16)), h(y32), "nvfp4 workload1 forward")
 
 
-def _moe_full(wl, sample_experts):
-    """Full-size NVFP4 grouped GEMM of workload 2 or 5 with sampled rows."""
+def _moe_full(wl, sample_experts, four_over_six=False):
+    """Full-size NVFP4 grouped GEMM of workload 2 or 5 with sampled rows. The
+    activations are quantized per token with Four Over Six block scales when
+    four_over_six is set (the forward's activation quantizer, as timed)."""
     p = synth.WORKLOADS[wl]
     T, K, E, N = p["tokens"], p["hidden"], p["experts"], p["ffn"]
     log(f"gemm nvfp4 workload{wl}: generate inputs")
@@ -105,15 +107,21 @@ def _moe_full(wl, sample_experts):
         rows.extend(cand.tolist())
     rows = np.unique(np.array(rows, dtype=np.int64))
     toks = np.unique(row_index[rows])
-    qa, qs, qo = Q.quantize_nvfp4(synth.bf16_to_f32(x[toks])[None], Q.OUTER_ROW)
+    fos = dict(four_over_six=four_over_six)
+    qa, qs, qo = Q.quantize_nvfp4(synth.bf16_to_f32(x[toks])[None], Q.OUTER_ROW, **fos)
     ac[toks], as_[toks], ao[toks] = qa[0], qs[0], qo[0]
     # the quantizers at this workload's full size (per token; per expert in one pass): sampled tokens and
     # experts against the oracle
-    log(f"quantize workload{wl} activations and weights")
-    gxc, gxs, gxo = bsq.quantize_nvfp4(bf16_t(x), "row")
+    log(f"quantize workload{wl} activations (four_over_six={four_over_six}) and weights")
+    gxc, gxs, gxo = bsq.quantize_nvfp4(bf16_t(x), "row", **fos)
     tt = t(toks)
     assert np.array_equal(h(gxc[tt]), qa[0]) and np.array_equal(h(gxs[tt]), qs[0])
     assert np.array_equal(h(gxo[tt]), np.asarray(qo).reshape(-1))
+    more = np.unique(np.r_[rng.choice(T, 256, replace=False), 0, T - 1])   # and 256 more tokens
+    ma, ms, mo = Q.quantize_nvfp4(synth.bf16_to_f32(x[more])[None], Q.OUTER_ROW, **fos)
+    tm = t(more)
+    assert np.array_equal(h(gxc[tm]), ma[0]) and np.array_equal(h(gxs[tm]), ms[0])
+    assert np.array_equal(h(gxo[tm]), np.asarray(mo).reshape(-1))
     del gxc, gxs, gxo
     gwc, gws, gwo = bsq.quantize_nvfp4(bf16_t(w), "tensor")
     for e in experts:
@@ -137,7 +145,7 @@ def test_gemm_nvfp4_workload2_full():
 
 
 def test_gemm_nvfp4_workload5_full():
-    _moe_full(5, [0, 64, 127])
+    _moe_full(5, [0, 64, 127], four_over_six=True)
 
 
 def _mxfp8_from(rng, x, rnd=Q.SR):

@@ -9,6 +9,7 @@ import pytest
 import torch
 
 import block_scaled_bit_quantize_amd as bsq
+from block_scaled_bit_quantize_amd import _lib
 import synth
 from oracle import formats as F
 from oracle import quant as Q
@@ -211,6 +212,51 @@ def test_quantize_mxfp8_transposed_small(dtype, rnd):
     assert np.array_equal(h(gc), oc) and np.array_equal(h(gs), os_)
 
 
+@pytest.mark.parametrize("seg", [[0, 256, 0, 256], [-10, 100, 50, 400], [0, 300, 200, 100, 256]])
+def test_segmented_malformed_offsets_stay_in_bounds(seg):
+    """Decreasing or out-of-range offsets are read as clamped to [0, rows]
+    and replaced by their running maximum: the result equals the oracle on
+    that table, and nothing is written past the documented output bound
+    cols * (rows + 31 * num_segments) (a guard region after it keeps its fill)."""
+    log(f"segmented malformed offsets {seg}")
+    rng = np.random.default_rng(31)
+    R, C = 256, 64
+    nseg = len(seg) - 1
+    x = _data(rng, (R, C), "normal")
+    norm = np.maximum.accumulate(np.clip(np.asarray(seg, np.int64), 0, R))
+    lib = _lib.load_library()
+    cap = C * (R + 31 * nseg)
+    guard = 4096
+    codes = torch.full((cap + guard,), 0xA5, dtype=torch.uint8, device=DEV)
+    scales = torch.full((cap // 32 + guard,), 0xA5, dtype=torch.uint8, device=DEV)
+    wsb = lib.bsq_quantize_mxfp8_workspace(R, 1, nseg)
+    ws = torch.zeros(max(wsb, 1), dtype=torch.uint8, device=DEV)
+    xd, segd = t(x), t(np.asarray(seg, np.int64))
+    st = lib.bsq_quantize_mxfp8(xd.data_ptr(), 0, R, C, 1, segd.data_ptr(), nseg, 1, 5, 2, codes.data_ptr(),
+                                scales.data_ptr(), ws.data_ptr(), wsb, None)
+    assert st == 0
+    oc, os_ = Q.quantize_mxfp8_transposed(x, norm, Q.SR, 5, 2)
+    gc, gs = h(codes), h(scales)
+    assert np.array_equal(gc[:oc.size], oc) and np.array_equal(gs[:os_.size], os_)
+    assert np.all(gc[cap:] == 0xA5) and np.all(gs[cap // 32:] == 0xA5)
+    # the gathered NVFP4 -> MXFP8 requant shares the plan
+    p, s_, o = Q.quantize_nvfp4(x[None], Q.OUTER_ROW)
+    gather = rng.integers(0, R, R).astype(np.int32)
+    codes.fill_(0xA5)
+    scales.fill_(0xA5)
+    wsb = lib.bsq_requant_workspace(1, R, nseg, Q.MXFP8, 1)
+    ws = torch.zeros(max(wsb, 1), dtype=torch.uint8, device=DEV)
+    pd, sd, od, gd = t(p[0]), t(s_[0]), t(o.reshape(-1)), t(gather)
+    st = lib.bsq_requant_transpose_sr(pd.data_ptr(), sd.data_ptr(), od.data_ptr(), 1, 1, R, C, R, gd.data_ptr(),
+                                      segd.data_ptr(), nseg, 1, 1, 3, 3, codes.data_ptr(), scales.data_ptr(), None,
+                                      ws.data_ptr(), wsb, None)
+    assert st == 0
+    wc, wsc = Q.requant_transpose_sr_segmented(p[0], s_[0], o.reshape(-1), Q.OUTER_ROW, gather, norm, 3, 3)
+    gc, gs = h(codes), h(scales)
+    assert np.array_equal(gc[:wc.size], wc) and np.array_equal(gs[:wsc.size], wsc)
+    assert np.all(gc[cap:] == 0xA5) and np.all(gs[cap // 32:] == 0xA5)
+
+
 def _sr_edge_blocks(rng, nblk):
     """MX blocks of 32 at the edges of the kernels' stochastic-rounding fast path (every value of a group of
     8 zero or at least 2^(e-6), e >= -120, done by the hardware SR convert) and of its general path."""
@@ -265,7 +311,9 @@ def test_quantize_mxfp8_sr_fast_path_edges(dtype):
     assert np.array_equal(h(gc), oc)
 
 
-_REQ_SHAPES = [(2, 64, 128), (1, 160, 64), (3, 256, 192), (1, 48, 128)]
+# (3, 48, 64) and (2, 80, 64): 192 and 320 blocks of 16 per item, so workgroups of
+# 256 blocks span two items in the NVFP4-target maximum pass
+_REQ_SHAPES = [(2, 64, 128), (1, 160, 64), (3, 256, 192), (1, 48, 128), (3, 48, 64), (2, 80, 64)]
 
 
 @pytest.mark.parametrize("rnd", ["rn", "sr"])
