@@ -67,6 +67,8 @@ def parse():
     p.add_argument("--warmup", type=int, default=3)
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--stages", default="", help="comma list of stages to run (profiling aid); default all")
+    p.add_argument("--scale-handling-only", action="store_true",
+                   help="run only the NVFP4 scale-handling comparison (decode16 vs inreg_scale) and print it (profiling aid)")
     p.add_argument("--copy-calibration", action="store_true",
                    help="after timing, run a plain 512 MiB device copy three times (reference for HBM byte counters)")
     return p.parse_args()
@@ -306,6 +308,71 @@ def workload5(torch, bsq, dev, reps=5):
     return out
 
 
+def _time(torch, fn, reps):
+    for _ in range(2):
+        fn()
+    torch.cuda.synchronize()
+    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    a.record()
+    for _ in range(reps):
+        fn()
+    b.record()
+    torch.cuda.synchronize()
+    return a.elapsed_time(b) / reps
+
+
+def scale_handling(torch, bsq, inp, xq, dev, reps=5):
+    """The two ways to handle NVFP4's E4M3 block scales on CDNA4, timed on one
+    dense problem with the forward GEMM's work: the step's quantized tokens
+    x_q [16384, 4096] against eight experts' weights stacked as one
+    [12288, 4096] NVFP4 tensor (2 * 16384 * 12288 * 4096 = 1.649 TFLOP, fp32
+    out). decode16: the library's kernel (exact fp16 operands, 16-bit MFMA);
+    inreg_scale: one FP8 MFMA per 16-value block with the partial sums scaled
+    in fp32 registers."""
+    xc, xs, xo = xq
+    w = inp["w"][:8].reshape(1, 8 * F, H)
+    wc, ws, wo = bsq.quantize_nvfp4(w, "tensor")
+    seg = torch.tensor([0, T], dtype=torch.int64, device=dev)
+    flops = 2.0 * T * 8 * F * H
+    calls = {"decode16": lambda: bsq.grouped_gemm_nvfp4(xc, xs, xo, wc, ws, wo, seg, T, out_dtype=torch.float32),
+             "inreg_scale": lambda: bsq.gemm_nvfp4_inreg_scale(xc, xs, xo, wc[0], ws[0], wo)}
+    out = {}
+    for name, fn in calls.items():
+        ms = _time(torch, fn, reps)
+        ach = flops / (ms * 1e-3) / 1e12
+        out[name] = {"ms": round(ms, 4), "achieved": round(ach, 2), "unit": "TFLOP/s",
+                     "frac_of_fp4_peak": round(ach / MFMA_PEAK_TFLOPS["fp4"], 4),
+                     "frac_of_fp8_peak": round(ach / MFMA_PEAK_TFLOPS["fp8"], 4),
+                     "frac_of_mfma16_peak": round(ach / MFMA_PEAK_TFLOPS["f16"], 4)}
+    out["shape"] = "dense M=16384, N=12288, K=4096 (1.649 TFLOP, the forward GEMM's work)"
+    del w, wc, ws, wo
+    return out
+
+
+def dense_library_gemm(torch, dev, reps=5):
+    """A practical 16-bit reference: torch.matmul (hipBLASLt) on dense bf16
+    operands (no decode, no grouping) at the step's three GEMM shapes."""
+    gen = torch.Generator(device=dev)
+    gen.manual_seed(7)
+    out = {}
+    x = torch.randn((M, H), generator=gen, device=dev).to(torch.bfloat16)
+    w = torch.randn((H, F), generator=gen, device=dev).to(torch.bfloat16)
+    out["fprop_shape"] = _time(torch, lambda: x @ w, reps)
+    g = torch.randn((M, F), generator=gen, device=dev).to(torch.bfloat16)
+    wt = torch.randn((F, H), generator=gen, device=dev).to(torch.bfloat16)
+    out["dgrad_shape"] = _time(torch, lambda: g @ wt, reps)
+    gt = g.t().contiguous()
+    out["wgrad_shape"] = _time(torch, lambda: gt @ x, reps)
+    del x, w, g, wt, gt
+    torch.cuda.empty_cache()
+    flops = 2.0 * M * F * H
+    res = {k: {"ms": round(v, 4), "achieved": round(flops / (v * 1e-3) / 1e12, 2), "unit": "TFLOP/s"}
+           for k, v in out.items()}
+    res["what"] = ("torch.matmul bf16 [131072,4096]x[4096,1536], [131072,1536]x[1536,4096], "
+                   "[1536,131072]x[131072,4096]: dense, no block scales")
+    return res
+
+
 def chain_forward(torch, bsq, inp, algo, dev, pair_row, reps=5):
     """The expert forward chain (w13 GEMM, SwiGLU + per-row NVFP4, w2 GEMM with
     the RHT + S2F6 combine codec in its epilogue, combine) on the step's
@@ -371,6 +438,10 @@ def main():
     inp = make_inputs(torch, dev)
     outer_one = torch.ones(1, dtype=torch.float32, device=dev)
 
+    if args.scale_handling_only:
+        xq = bsq.quantize_nvfp4(inp["x"], "row", four_over_six=True)
+        print(json.dumps({"nvfp4_scale_handling": scale_handling(torch, bsq, inp, xq, dev)}))
+        return
     # routing is deterministic: read the segment sizes once (outside timing) for byte accounting
     ri, seg, _ = bsq.route(inp["ids"], E)
     torch.cuda.synchronize()
@@ -509,6 +580,8 @@ def main():
         alternatives["expert_chain_fwd"] = chain_forward(torch, bsq, inp, algo, dev, pair_row)
         alternatives["workload1_latency"] = latency_workload1(torch, bsq, dev)
         alternatives["workload5_fwd"] = workload5(torch, bsq, dev)
+        alternatives["nvfp4_scale_handling"] = scale_handling(torch, bsq, inp, state["xq"], dev)
+        alternatives["dense_bf16_library_gemm"] = dense_library_gemm(torch, dev)
 
     if args.copy_calibration:
         src_buf = torch.empty(512 << 20, dtype=torch.uint8, device=dev).fill_(1)

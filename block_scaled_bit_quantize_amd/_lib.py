@@ -37,6 +37,7 @@ SIGNATURES = {
                                             c_i64, c_i64, ctypes.c_uint32, c_vp, c_vp, c_vp]),
     "bsq_grouped_gemm_mxfp8": (c_int, [c_int, c_vp, c_vp, c_vp, c_vp, c_vp, c_i64, c_i64, c_i64, c_i64, c_vp,
                                        c_int, c_vp]),
+    "bsq_gemm_nvfp4_inreg_scale": (c_int, [c_vp, c_vp, c_vp, c_vp, c_vp, c_vp, c_i64, c_i64, c_i64, c_vp, c_vp]),
     "bsq_route_workspace": (c_size, [c_i64, c_i64]),
     "bsq_route": (c_int, [c_vp, c_i64, c_i64, c_i64, c_vp, c_vp, c_vp, c_vp, c_size, c_vp]),
     "bsq_route_noalloc": (c_int, [c_vp, c_i64, c_i64, c_i64, c_vp, c_vp, c_vp, c_vp]),

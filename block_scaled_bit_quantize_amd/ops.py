@@ -269,6 +269,21 @@ def grouped_gemm_mxfp8(wgrad, a_codes, a_scales, b_codes, b_scales, seg_offsets,
     return out
 
 
+def gemm_nvfp4_inreg_scale(a_codes, a_scales, a_outer, b_codes, b_scales, b_outer):
+    """Dense NVFP4 product with the block scales applied in registers (FP8
+    MFMA per 16-value block, fp32 scaling): a_* [M, K/2], [M, K/16], [M];
+    b_* [N, K/2], [N, K/16], [1] -> float32 [M, N]. The alternative to the
+    exact 16-bit decode of grouped_gemm_nvfp4, kept for comparison."""
+    lib = load_library()
+    _dev(a_codes, a_scales, a_outer, b_codes, b_scales, b_outer)
+    M, N, K = a_codes.shape[0], b_codes.shape[0], 2 * a_codes.shape[1]
+    out = torch.empty((M, N), dtype=torch.float32, device=a_codes.device)
+    check(lib.bsq_gemm_nvfp4_inreg_scale(a_codes.data_ptr(), a_scales.data_ptr(), a_outer.data_ptr(),
+                                         b_codes.data_ptr(), b_scales.data_ptr(), b_outer.data_ptr(), M, N, K,
+                                         out.data_ptr(), _stream()), "bsq_gemm_nvfp4_inreg_scale")
+    return out
+
+
 def route(topk_ids, num_experts):
     """topk_ids int32 [T, k] -> (row_index int32 [T*k], seg_offsets int64 [E+1], pair_row int32 [T*k])."""
     lib = load_library()

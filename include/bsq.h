@@ -257,7 +257,8 @@ int bsq_requant_transpose_sr(const uint8_t* codes, const uint8_t* scales, const 
  * a_codes [a_rows, K/2], a_scales [a_rows, K/16]; a_outer [a_rows] when
  * a_outer_per_row != 0, else [1].
  * b_codes [E, N, K/2], b_scales [E, N, K/16], b_outer [E].
- * seg_offsets device int64 [E+1]; M_total = seg_offsets[E] rows of output.
+ * seg_offsets device int64 [E+1]; M_total = seg_offsets[E] rows of output,
+ * M_total < 2^31 - 1.
  * out [M_total, N] of out_dtype. Rows of a segment past M_total are not
  * written (malformed offsets never reach outside the buffers).
  * Constraints: K % 64 == 0, N % 256 == 0, 1 <= E <= 1024 (BSQ_E_SHAPE).
@@ -292,6 +293,7 @@ int bsq_grouped_gemm_nvfp4_s2f6(const uint8_t* a_codes, const uint8_t* a_scales,
  *
  * wgrad == 0 (DGRAD, segments along M): for row r of expert e
  *   out[r, n] = sum_k A[r, k] * B[e, n, k]
+ *   (M_total < 2^31 - 1)
  *   A codes [M_total, K], scales [M_total, K/32]; B codes [E, N, K], scales
  *   [E, N, K/32]; out [M_total, N]. K % 64 == 0, N % 256 == 0.
  * wgrad == 1 (WGRAD, segments along K): for expert e with padded token count
@@ -307,6 +309,25 @@ int bsq_grouped_gemm_nvfp4_s2f6(const uint8_t* a_codes, const uint8_t* a_scales,
  * Codes and out 16-byte aligned.
  * Errors: NULL, SHAPE, ALIGN, DTYPE, ENUM, LAUNCH.
  * ---------------------------------------------------------------------- */
+/* bsq_gemm_nvfp4_inreg_scale: the NVFP4 product with the block scales
+ * applied in registers instead of decoded into the operands ("Kernels for
+ * low-precision training": the two ways to handle NVFP4 scales without a
+ * native NVFP4 MMA), kept to measure that choice against
+ * bsq_grouped_gemm_nvfp4 on the same data. Dense, one expert:
+ *   out[m, n] = a_outer[m] * b_outer[0] * sum_k xq[m, k] * wq[n, k]
+ * Each 16-value block pair is one FP8 MFMA over the E2M1 values (exact
+ * partial sum), scaled by s_a * s_w and accumulated in FP32.
+ * a_codes [M, K/2], a_scales [M, K/16], a_outer [M]; b_codes [N, K/2],
+ * b_scales [N, K/16], b_outer [1]; out float32 [M, N].
+ * M % 128 == 0 (M / 128 <= 65535), N % 128 == 0, K % 64 == 0; codes and out
+ * 16-byte aligned, scales 4-byte aligned.
+ * Errors: NULL, SHAPE, ALIGN, LAUNCH.
+ * ---------------------------------------------------------------------- */
+int bsq_gemm_nvfp4_inreg_scale(const uint8_t* a_codes, const uint8_t* a_scales, const float* a_outer,
+                               const uint8_t* b_codes, const uint8_t* b_scales, const float* b_outer,
+                               int64_t M, int64_t N, int64_t K, float* out, bsq_stream_t stream);
+
+/* ------------------------------------------------------------------------ */
 int bsq_grouped_gemm_mxfp8(int wgrad, const uint8_t* a_codes, const uint8_t* a_scales,
                            const uint8_t* b_codes, const uint8_t* b_scales,
                            const int64_t* seg_offsets, int64_t E, int64_t M_total, int64_t N,

@@ -185,6 +185,12 @@ def test_gemm_and_route_validation(lib):
     assert m(1, FAKE, FAKE, FAKE, FAKE, FAKE, 2, 200, 256, 0, FAKE, 0, None) == E_SHAPE
     assert m(0, FAKE, None, FAKE, FAKE, FAKE, 2, 256, 256, 128, FAKE, 1, None) == E_NULL
     assert m(0, FAKE, FAKE, FAKE, FAKE, FAKE, 2, 256, 256, 128, FAKE, 5, None) == E_DTYPE
+    ir = lib.bsq_gemm_nvfp4_inreg_scale
+    assert ir(FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 100, 128, 64, FAKE, None) == E_SHAPE     # M % 128
+    assert ir(FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 128, 128, 32, FAKE, None) == E_SHAPE     # K % 64
+    assert ir(FAKE, FAKE, FAKE, None, FAKE, FAKE, 128, 128, 64, FAKE, None) == E_NULL
+    assert ir(FAKE, FAKE + 1, FAKE, FAKE, FAKE, FAKE, 128, 128, 64, FAKE, None) == E_ALIGN
+    assert ir(None, None, None, None, None, None, 0, 128, 64, None, None) == 0              # empty
     rt = lib.bsq_route
     assert rt(FAKE, 10, 0, 4, FAKE, FAKE, FAKE, FAKE, 1 << 20, None) == E_SHAPE
     assert rt(FAKE, 10, 2, 2000, FAKE, FAKE, FAKE, FAKE, 1 << 20, None) == E_SHAPE

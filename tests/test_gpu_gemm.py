@@ -148,6 +148,29 @@ def test_gemm_nvfp4_workload5_full():
     _moe_full(5, [0, 64, 127], four_over_six=True)
 
 
+@pytest.mark.parametrize("M,N,K", [(128, 128, 64), (256, 384, 192), (384, 512, 320)])
+def test_gemm_nvfp4_inreg_scale(M, N, K):
+    """The in-register scale variant (FP8 MFMA per 16-value block, fp32 scale
+    products) against the float64 oracle (accept rule) and against the exact
+    16-bit decode kernel on the same operands (both within the rule)."""
+    log(f"gemm nvfp4 inreg-scale M={M} N={N} K={K}")
+    rng = np.random.default_rng(M + N + K)
+    x = rng.standard_t(3, (M, K)).astype(f32)
+    w = (rng.standard_normal((1, N, K)) * 0.02).astype(f32)
+    ap, as_, ao = Q.quantize_nvfp4(x[None], Q.OUTER_ROW, four_over_six=True)
+    bp, bs, bo = Q.quantize_nvfp4(w, Q.OUTER_TENSOR)
+    ao = np.asarray(ao).reshape(-1)
+    seg = np.array([0, M], dtype=np.int64)
+    yref, yabs = G.grouped_gemm_nvfp4_ref(ap[0], as_[0], ao, None, bp, bs, bo, seg)
+    y = bsq.gemm_nvfp4_inreg_scale(t(ap[0]), t(as_[0]), t(ao), t(bp[0]), t(bs[0]), t(np.asarray(bo).reshape(-1)))
+    _check(h(y), yref, yabs, f"nvfp4 inreg-scale {M}x{N}x{K}")
+    if N % 256:  # the grouped kernel's tiles are 256 wide
+        return
+    y16 = bsq.grouped_gemm_nvfp4(t(ap[0]), t(as_[0]), t(ao), t(bp), t(bs), t(np.asarray(bo).reshape(-1)), t(seg), M,
+                                 out_dtype=torch.float32)
+    _check(h(y16), yref, yabs, f"nvfp4 decode16 {M}x{N}x{K}")
+
+
 def _mxfp8_from(rng, x, rnd=Q.SR):
     return Q.quantize_mxfp8(x, rnd, int(rng.integers(1 << 30)), 1)
 
