@@ -304,8 +304,13 @@ int bsq_grouped_gemm_nvfp4_s2f6(const uint8_t* a_codes, const uint8_t* a_scales,
  *   mode): A_e [M, Kp_e], B_e [N, Kp_e]; here M is the `M_total` argument
  *   and K is ignored. out [E, M, N]. M % 256 == 0, N % 256 == 0.
  * Values are E4M3 times the E8M0 block scale. Every product is formed
- * exactly (each value is decoded to bf16, exact for scale codes 10..246) and
- * accumulated in FP32; out_dtype BSQ_BF16 (round to nearest even) or BSQ_F32.
+ * exactly and accumulated in FP32: each value is decoded to bf16 (subnormals
+ * kept), which is exact for every E4M3 value under scale codes 3..246 (the
+ * MXFP8 quantizer's codes for any block maximum up to 1.75 * 2^127). Under
+ * codes 0..2 a decoded value rounds to the nearest multiple of 2^-133 (error
+ * at most 2^-134 per value); under codes 247..254 a decoded magnitude of
+ * 2^128 or more becomes infinite; code 255 (NaN) propagates.
+ * out_dtype BSQ_BF16 (round to nearest even) or BSQ_F32.
  * Codes and out 16-byte aligned.
  * Errors: NULL, SHAPE, ALIGN, DTYPE, ENUM, LAUNCH.
  * ---------------------------------------------------------------------- */

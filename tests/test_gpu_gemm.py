@@ -9,6 +9,7 @@ import torch
 
 import block_scaled_bit_quantize_amd as bsq
 import synth
+from oracle import formats as F
 from oracle import gemm as G
 from oracle import quant as Q
 from oracle.route import route as oroute
@@ -173,6 +174,40 @@ def test_gemm_nvfp4_inreg_scale(M, N, K):
 
 def _mxfp8_from(rng, x, rnd=Q.SR):
     return Q.quantize_mxfp8(x, rnd, int(rng.integers(1 << 30)), 1)
+
+
+def test_gemm_mxfp8_scale_code_range():
+    """The bf16 decode of MXFP8 operands over the whole E8M0 range: row r of A
+    holds 32 copies of one E4M3 value q under scale code c_r (block 0; block 1
+    is zero) and B is all ones, so y[r, n] = 32 * dec(q, c_r) with dec the
+    bf16 value of q * 2^(c - 127). Codes 3..246: dec is exact, so y equals the
+    float64 product. Codes 0..2: dec is the round-to-nearest-even of the exact
+    value onto bf16's subnormal grid (multiples of 2^-133). Codes 247..254:
+    magnitudes of 2^128 and more decode to infinity."""
+    log("gemm mxfp8 scale code range")
+    codes = list(range(0, 13)) + list(range(240, 255))
+    M, N, K = 256, 256, 64
+    seg = np.array([0, M], dtype=np.int64)
+    bc = np.full((1, N, K), 0x38, np.uint8)                 # 1.0
+    bs = np.full((1, N, K // 32), 127, np.uint8)
+    for q in (0x01, 0x07, 0x38, 0x3F, 0x77, 0x7E, 0xB9):
+        ac = np.zeros((M, K), np.uint8)
+        ac[:, :32] = q
+        asc = np.full((M, K // 32), 127, np.uint8)
+        asc[:len(codes), 0] = codes
+        y = h(bsq.grouped_gemm_mxfp8(False, t(ac), t(asc), t(bc), t(bs), t(seg), M, N, K, out_dtype=torch.float32))
+        qv = float(F.e4m3_decode(np.array([q], np.uint8))[0])
+        for r, c in enumerate(codes):
+            exact = qv * 2.0 ** (c - 127)
+            dec = float(torch.tensor(exact, dtype=torch.float64).to(torch.bfloat16).to(torch.float64))
+            want = np.float32(32.0 * dec)                  # a power-of-two multiple: exact unless it overflows
+            assert np.all(y[r] == want), (hex(q), c, y[r, 0], want)
+            if 3 <= c <= 246:
+                assert dec == exact, (hex(q), c)
+            if c < 3:
+                assert abs(dec - exact) <= 2.0 ** -134
+            if c >= 247 and abs(exact) >= 2.0 ** 128:
+                assert np.isinf(want)
 
 
 def test_gemm_mxfp8_dgrad_small():
