@@ -104,7 +104,7 @@ def _moe_full(wl, sample_experts, four_over_six=False):
     for e in experts:
         if lens[e] == 0:
             continue
-        cand = np.r_[seg[e], seg[e + 1] - 1, rng.integers(seg[e], seg[e + 1], size=2)]
+        cand = np.r_[seg[e], seg[e + 1] - 1, rng.integers(seg[e], seg[e + 1], size=14)]
         rows.extend(cand.tolist())
     rows = np.unique(np.array(rows, dtype=np.int64))
     toks = np.unique(row_index[rows])
@@ -261,7 +261,8 @@ def test_gemm_mxfp8_workload4_full():
     ac, as_ = ac.reshape(M_total, Ng), as_.reshape(M_total, Ng // 32)
     bc, bs = filler_mxfp8(rng, E * Kx * Ng)
     bc, bs = bc.reshape(E, Kx, Ng), bs.reshape(E, Kx, Ng // 32)
-    rows = np.unique(np.concatenate([[seg[e], seg[e + 1] - 1, rng.integers(seg[e], seg[e + 1])] for e in experts]))
+    rows = np.unique(np.concatenate([np.r_[seg[e], seg[e + 1] - 1, rng.integers(seg[e], seg[e + 1], size=14)]
+                                     for e in experts]))
     g = synth.output_grad(M_total, Ng)
     gq, gs = Q.quantize_mxfp8(synth.bf16_to_f32(g[rows]), Q.SR, 42, 1)
     ac[rows], as_[rows] = gq, gs
