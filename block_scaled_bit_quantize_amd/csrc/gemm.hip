@@ -378,9 +378,80 @@ template <int FMT> struct Slab {
   static constexpr int CPR = FMT == FMT_NVFP4 ? 2 : 4;
   static constexpr int R = (BM + BN) * CPR / kThreads;  // rows per thread
   uint4 c[R];      // NVFP4: 32 E2M1 codes; MXFP8: 16 E4M3 codes of each row
-  uint32_t sc[R];  // NVFP4: the chunk's two E4M3 scales; MXFP8: its E8M0 scale
   uint32_t m;      // MXFP8: all ones, or 0 when the chunk lies past the K extent
 };
+
+// Block scales, fetched for four K steps at a time: the CPR threads that
+// share a thread's rows (CPR = R) each load one of those rows' scales of the
+// four steps, 16 bytes (NVFP4: 4 E4M3 scales per step) or 8 (MXFP8: 2 E8M0
+// scales per step), with one buffer load (reads past the scale array return
+// zeros); every step, a broadcast within the group of CPR lanes gives each
+// thread its rows' scales of the step. One scale request per row and four
+// steps instead of one per row, chunk and step (measured: the per-step
+// scale loads cost 0.14-0.17 ms per GEMM beside the code loads).
+template <int FMT> struct ScaleGrp;
+template <> struct ScaleGrp<FMT_NVFP4> {
+  uint32_t w[4];  // the row's scale bytes of steps 4j .. 4j+3 (4 per step)
+};
+template <> struct ScaleGrp<FMT_MXFP8> {
+  uint32_t d[3];  // 12 bytes from the 4-byte boundary at or below the row's scales of step 4j
+  uint32_t sh;    // bit offset of those scales in d
+};
+typedef __amdgpu_buffer_rsrc_t brsrc_t;
+typedef int v3i __attribute__((ext_vector_type(3)));
+typedef int v4i __attribute__((ext_vector_type(4)));
+
+// Lane c of a group of CPR loads the scales of its row c (A rows for c < R/2)
+// for K steps 4j .. 4j+3.
+__device__ __forceinline__ void load_group(ScaleGrp<FMT_NVFP4>& gr, brsrc_t ra, brsrc_t rb, const uint32_t* off32,
+                                           int c, int64_t j) {
+  const uint32_t o = (off32[c] << 2) + 16u * (uint32_t)j;  // scale bytes are an 8th of the code bytes
+  const v4i v = c < 1 ? __builtin_amdgcn_raw_buffer_load_b128(ra, (int)o, 0, 0)
+                      : __builtin_amdgcn_raw_buffer_load_b128(rb, (int)o, 0, 0);
+  gr.w[0] = (uint32_t)v.x; gr.w[1] = (uint32_t)v.y; gr.w[2] = (uint32_t)v.z; gr.w[3] = (uint32_t)v.w;
+}
+__device__ __forceinline__ void load_group(ScaleGrp<FMT_MXFP8>& gr, brsrc_t ra, brsrc_t rb, const uint32_t* off32,
+                                           int c, int64_t j) {
+  const uint32_t o = off32[c] + 8u * (uint32_t)j;  // scale bytes are a 32nd of the code bytes
+  const v3i v = c < 2 ? __builtin_amdgcn_raw_buffer_load_b96(ra, (int)(o & ~3u), 0, 0)
+                      : __builtin_amdgcn_raw_buffer_load_b96(rb, (int)(o & ~3u), 0, 0);
+  gr.d[0] = (uint32_t)v.x; gr.d[1] = (uint32_t)v.y; gr.d[2] = (uint32_t)v.z;
+  gr.sh = 8u * (o & 3u);
+}
+
+// The thread's rows' scales of step s (s % 4 of its group), in the per-row
+// form the decode takes: NVFP4 the chunk's two E4M3 bytes, MXFP8 the E8M0
+// byte of the chunk's block. Lane i of the group holds row i's scales.
+template <int I> __device__ __forceinline__ uint32_t bcast4(uint32_t v) {  // lane I of each group of 4
+  return (uint32_t)__builtin_amdgcn_mov_dpp((int)v, I | (I << 2) | (I << 4) | (I << 6), 0xF, 0xF, false);
+}
+template <int I> __device__ __forceinline__ uint32_t bcast2(uint32_t v) {  // lane I of each pair
+  return (uint32_t)__builtin_amdgcn_mov_dpp((int)v, I | (I << 2) | ((2 + I) << 4) | ((2 + I) << 6), 0xF, 0xF, false);
+}
+// The group's word holding step s4's scales (the lane's own row), and the
+// shift of the thread's chunk's scales in it.
+__device__ __forceinline__ uint32_t step_word(const ScaleGrp<FMT_NVFP4>& gr, int s4) {
+  return s4 == 0 ? gr.w[0] : (s4 == 1 ? gr.w[1] : (s4 == 2 ? gr.w[2] : gr.w[3]));
+}
+__device__ __forceinline__ uint32_t step_word(const ScaleGrp<FMT_MXFP8>& gr, int s4) {
+  return s4 < 2 ? __builtin_amdgcn_alignbit(gr.d[1], gr.d[0], gr.sh)   // steps 0, 1 of the group
+                : __builtin_amdgcn_alignbit(gr.d[2], gr.d[1], gr.sh);  // steps 2, 3
+}
+template <int FMT> __device__ __forceinline__ uint32_t step_shift(int s4, int c) {
+  return FMT == FMT_NVFP4 ? 16u * (uint32_t)c : 8u * (uint32_t)(2 * (s4 & 1) + (c >> 1));
+}
+// Row i's scales of the step (i a constant after unrolling): NVFP4 the
+// chunk's two E4M3 bytes, MXFP8 the E8M0 byte of the chunk's block.
+template <int FMT> __device__ __forceinline__ uint32_t row_scale(uint32_t w, uint32_t shift, int i) {
+  uint32_t v;
+  if constexpr (FMT == FMT_NVFP4) {
+    v = i == 0 ? bcast2<0>(w) : bcast2<1>(w);
+    return (v >> shift) & 0xFFFFu;
+  } else {
+    v = i == 0 ? bcast4<0>(w) : (i == 1 ? bcast4<1>(w) : (i == 2 ? bcast4<2>(w) : bcast4<3>(w)));
+    return (v >> shift) & 0xFFu;
+  }
+}
 
 __device__ __forceinline__ void load_slab(Slab<FMT_NVFP4>& r, const GemmArgs& g, const uint32_t* off32, int c,
                                           int64_t k0, int64_t) {
@@ -388,10 +459,8 @@ __device__ __forceinline__ void load_slab(Slab<FMT_NVFP4>& r, const GemmArgs& g,
 #pragma unroll
   for (int i = 0; i < R; ++i) {
     const uint8_t* codes = i < R / 2 ? g.a_codes : g.b_codes;
-    const uint8_t* scales = i < R / 2 ? g.a_scales : g.b_scales;
     const int64_t off = (int64_t)off32[i] << 5;
     r.c[i] = *reinterpret_cast<const uint4*>(codes + off + (k0 >> 1) + 16 * c);
-    r.sc[i] = *reinterpret_cast<const uint16_t*>(scales + (off >> 3) + (k0 >> 4) + 2 * c);
   }
 }
 // MXFP8 rows of WGRAD end where the expert's padded token count ends, a
@@ -406,10 +475,8 @@ __device__ __forceinline__ void load_slab(Slab<FMT_MXFP8>& r, const GemmArgs& g,
 #pragma unroll
   for (int i = 0; i < R; ++i) {
     const uint8_t* codes = i < R / 2 ? g.a_codes : g.b_codes;
-    const uint8_t* scales = i < R / 2 ? g.a_scales : g.b_scales;
     const int64_t off = (int64_t)off32[i] << 5;
     r.c[i] = *reinterpret_cast<const uint4*>(codes + off + k);
-    r.sc[i] = scales[(off >> 5) + (k >> 5)];
   }
 }
 
@@ -417,11 +484,13 @@ __device__ __forceinline__ void load_slab(Slab<FMT_MXFP8>& r, const GemmArgs& g,
 //   NVFP4: row q / 2, values 16 (q & 1) .. of its chunk, at byte 64c + 32(q & 1);
 //   MXFP8: row q, at byte 32c.
 template <int FMT> constexpr int quarters() { return FMT == FMT_NVFP4 ? 2 * Slab<FMT>::R : Slab<FMT>::R; }
-__device__ __forceinline__ void decode_quarter(const Slab<FMT_NVFP4>& r, uint8_t* dst, int q) {
+template <int FMT> constexpr int quarter_row(int q) { return FMT == FMT_NVFP4 ? q >> 1 : q; }
+// `scr` is the quarter's row's scales of the step (row_scale).
+__device__ __forceinline__ void decode_quarter(const Slab<FMT_NVFP4>& r, uint32_t scr, uint8_t* dst, int q) {
   const int i = q >> 1, h = q & 1;
   const uint32_t w0 = h ? r.c[i].z : r.c[i].x;
   const uint32_t w1 = h ? r.c[i].w : r.c[i].y;
-  const _Float16 s = (_Float16)e4m3_val((r.sc[i] >> (8 * h)) & 0xFFu);  // one E4M3 scale per 16
+  const _Float16 s = (_Float16)e4m3_val((scr >> (8 * h)) & 0xFFu);  // one E4M3 scale per 16
   const h2 sv = {s, s};
 #define BSQ_DEC4(w, v0, v1, v2, v3)                                 \
   const h2 v0 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, 1.0f, 0) * sv; \
@@ -437,11 +506,11 @@ __device__ __forceinline__ void decode_quarter(const Slab<FMT_NVFP4>& r, uint8_t
   d[1] = make_uint4(__builtin_bit_cast(uint32_t, b0), __builtin_bit_cast(uint32_t, b1), __builtin_bit_cast(uint32_t, b2),
                     __builtin_bit_cast(uint32_t, b3));
 }
-__device__ __forceinline__ void decode_quarter(const Slab<FMT_MXFP8>& r, uint8_t* dst, int q) {
+__device__ __forceinline__ void decode_quarter(const Slab<FMT_MXFP8>& r, uint32_t scr, uint8_t* dst, int q) {
   const uint4 v = make_uint4(r.c[q].x & r.m, r.c[q].y & r.m, r.c[q].z & r.m, r.c[q].w & r.m);
   // 2^(s-127) as a float: the scaled convert applies its exponent (code 127,
   // a factor of one, for a masked chunk)
-  const uint32_t code = (r.sc[q] & r.m) | (127u & ~r.m);
+  const uint32_t code = (scr & r.m) | (127u & ~r.m);
   const float s = __uint_as_float(code << 23);
 #define BSQ_DEC2(w, p, q_)                                              \
   const bf2 p = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w, s, false); \
@@ -488,6 +557,27 @@ __global__ __launch_bounds__(kThreads) void k_gemm(const GemmArgs g) {
   const int64_t per_xcd = (total + kXcds - 1) / kXcds;
   const int64_t wpx = gridDim.x / kXcds;  // workgroups per XCD (the grid is a multiple of kXcds)
   const int64_t tile0 = (int64_t)(blockIdx.x % kXcds) * per_xcd;
+
+  // ---- the scale arrays as buffers (reads past them return zeros; the
+  // range is rounded up to whole 4-byte words)
+  int64_t sa_bytes, sb_bytes;
+  if constexpr (FMT == FMT_NVFP4) {
+    sa_bytes = g.a_rows * (g.K / 16);
+    sb_bytes = (int64_t)g.E * g.N * (g.K / 16);
+  } else if constexpr (WGRAD) {
+    const int64_t kpt = s_cum[g.E - 1];  // padded tokens of all experts
+    sa_bytes = g.M * kpt / 32;
+    sb_bytes = g.N * kpt / 32;
+  } else {
+    sa_bytes = g.M * (g.K / 32);
+    sb_bytes = (int64_t)g.E * g.N * (g.K / 32);
+  }
+  auto nrec = [](int64_t b) -> int {
+    b = (b + 3) & ~(int64_t)3;
+    return (int)(uint32_t)(b < 0xFFFFFFFCll ? b : 0xFFFFFFFCll);
+  };
+  const brsrc_t rsa = __builtin_amdgcn_make_buffer_rsrc((void*)g.a_scales, (short)0, nrec(sa_bytes), 0x00020000);
+  const brsrc_t rsb = __builtin_amdgcn_make_buffer_rsrc((void*)g.b_scales, (short)0, nrec(sb_bytes), 0x00020000);
 
   // ---- the slab this thread loads and decodes each K step
   const int t = threadIdx.x;
@@ -552,11 +642,19 @@ __global__ __launch_bounds__(kThreads) void k_gemm(const GemmArgs g) {
     // end of the step publishes that buffer (every read of it from the previous
     // step finished before the previous barrier). The two register sets swap
     // roles every step (the loop body is unrolled twice).
+    // Scale groups: group j (steps 4j .. 4j+3) is loaded with step 4j's codes
+    // (at step 4j - 2) into gnext and becomes gcur when step 4j is decoded.
     Slab<FMT> r0, r1;
+    ScaleGrp<FMT> gcur, gnext;
     auto step = [&](int kt, Slab<FMT>& cur, Slab<FMT>& nxt) {
       const int buf = kt & 1;
       load_slab(nxt, g, off, chunk, (int64_t)(kt + 2 < nk ? kt + 2 : nk - 1) * BK, tl.klen);
+      if (kt + 2 < nk && ((kt + 2) & 3) == 0) load_group(gnext, rsa, rsb, off, chunk, (kt + 2) >> 2);
       __builtin_amdgcn_sched_barrier(0);  // keep the loads here: a whole step ahead of their use
+      const int dstep = kt + 1 < nk ? kt + 1 : nk - 1;  // the step `cur` holds
+      if (kt + 1 < nk && (dstep & 3) == 0) gcur = gnext;
+      const uint32_t sw = step_word(gcur, dstep & 3);
+      const uint32_t ssh = step_shift<FMT>(dstep & 3, chunk);
 #pragma unroll
       for (int ks = 0; ks < 4; ++ks) {
         if (ks < 3) {
@@ -567,7 +665,8 @@ __global__ __launch_bounds__(kThreads) void k_gemm(const GemmArgs g) {
 #pragma unroll
           for (int j = 0; j < TJ; ++j) acc[i][j] = mfma16(fb[ks & 1][j], fa[ks & 1][i], acc[i][j]);
 #pragma unroll
-        for (int q = ks * QK; q < (ks + 1) * QK; ++q) decode_quarter(cur, qdst(buf ^ 1, q), q);
+        for (int q = ks * QK; q < (ks + 1) * QK; ++q)
+          decode_quarter(cur, row_scale<FMT>(sw, ssh, quarter_row<FMT>(q)), qdst(buf ^ 1, q), q);
         // interleave each MFMA with a few decode VALU ops, the fragment reads and the decode stores
 #pragma unroll
         for (int m = 0; m < 4 * TJ; ++m) {
@@ -582,8 +681,13 @@ __global__ __launch_bounds__(kThreads) void k_gemm(const GemmArgs g) {
     };
     if (nk > 0) {
       load_slab(r0, g, off, chunk, 0, tl.klen);
+      load_group(gnext, rsa, rsb, off, chunk, 0);
+      gcur = gnext;
+      const uint32_t sw = step_word(gcur, 0);
+      const uint32_t ssh = step_shift<FMT>(0, chunk);
 #pragma unroll
-      for (int q = 0; q < quarters<FMT>(); ++q) decode_quarter(r0, qdst(0, q), q);
+      for (int q = 0; q < quarters<FMT>(); ++q)
+        decode_quarter(r0, row_scale<FMT>(sw, ssh, quarter_row<FMT>(q)), qdst(0, q), q);
       load_slab(r0, g, off, chunk, nk > 1 ? BK : 0, tl.klen);
       __syncthreads();
       BSQ_LOAD_FRAGS(0, 0, 0)

@@ -311,7 +311,10 @@ int bsq_grouped_gemm_nvfp4_s2f6(const uint8_t* a_codes, const uint8_t* a_scales,
  * at most 2^-134 per value); under codes 247..254 a decoded magnitude of
  * 2^128 or more becomes infinite; code 255 (NaN) propagates.
  * out_dtype BSQ_BF16 (round to nearest even) or BSQ_F32.
- * Codes and out 16-byte aligned.
+ * Codes and out 16-byte aligned. Scales are read in aligned 4-byte words:
+ * A's scale array (M_total * K / 32 bytes, not a multiple of 4 only when
+ * K % 128 == 64 and M_total is odd) must stay readable up to the next 4-byte
+ * boundary past its end, as any allocation of whole 4-byte words is.
  * Errors: NULL, SHAPE, ALIGN, DTYPE, ENUM, LAUNCH.
  * ---------------------------------------------------------------------- */
 /* bsq_gemm_nvfp4_inreg_scale: the NVFP4 product with the block scales
