@@ -176,6 +176,37 @@ def _mxfp8_from(rng, x, rnd=Q.SR):
     return Q.quantize_mxfp8(x, rnd, int(rng.integers(1 << 30)), 1)
 
 
+@pytest.mark.parametrize("K", [64, 192, 320])
+def test_gemm_short_k(K):
+    """1, 3 and 5 K steps of 64: the block scales come in groups of four K
+    steps, so these cover a group cut short, a single partial group and a
+    full group followed by a partial one, for the NVFP4 forward (gathered
+    rows) and the MXFP8 DGRAD (odd row count: its scale array ends off a
+    4-byte boundary when K % 128 == 64)."""
+    log(f"gemm short K={K}")
+    rng = np.random.default_rng(K)
+    T, E, N = 97, 3, 256
+    seg = np.array([0, 40, 41, 195], dtype=np.int64)
+    row_index = rng.integers(0, T, size=195).astype(np.int32)
+    x = rng.standard_t(3, (T, K)).astype(f32)
+    w = (rng.standard_normal((E, N, K)) * 0.02).astype(f32)
+    ap, as_, ao = Q.quantize_nvfp4(x[None], Q.OUTER_ROW, four_over_six=True)
+    bp, bs, bo = Q.quantize_nvfp4(w, Q.OUTER_TENSOR)
+    ao, bo = np.asarray(ao).reshape(-1), np.asarray(bo).reshape(-1)
+    y32, y16 = _nvfp4(t(ap[0]), t(as_[0]), t(ao), t(bp), t(bs), t(bo), t(seg), 195, row_index=t(row_index))
+    yref, yabs = G.grouped_gemm_nvfp4_ref(ap[0], as_[0], ao, row_index, bp, bs, bo, seg)
+    _check(h(y32), yref, yabs, f"nvfp4 short K={K}")
+    assert torch.equal(y16, y32.to(torch.bfloat16))
+    g = (rng.standard_normal((195, K)) * 1e-3).astype(f32)
+    ac, as2 = _mxfp8_from(rng, g)
+    wt = (rng.standard_normal((E * N, K)) * 0.02).astype(f32)
+    bc, bs2 = _mxfp8_from(rng, wt)
+    bc, bs2 = bc.reshape(E, N, K), bs2.reshape(E, N, K // 32)
+    y = bsq.grouped_gemm_mxfp8(False, t(ac), t(as2), t(bc), t(bs2), t(seg), 195, N, K, out_dtype=torch.float32)
+    yref, yabs = G.mxfp8_dgrad_ref(ac, as2, bc, bs2, seg)
+    _check(h(y), yref, yabs, f"mxfp8 dgrad short K={K}")
+
+
 def test_gemm_mxfp8_scale_code_range():
     """The bf16 decode of MXFP8 operands over the whole E8M0 range: row r of A
     holds 32 copies of one E4M3 value q under scale code c_r (block 0; block 1
