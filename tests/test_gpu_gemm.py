@@ -142,11 +142,11 @@ def _moe_full(wl, sample_experts, four_over_six=False):
 
 
 def test_gemm_nvfp4_workload2_full():
-    _moe_full(2, [0, 21, 63])
+    _moe_full(2, [0, 5, 11, 21, 28, 34, 40, 47, 55, 63])
 
 
 def test_gemm_nvfp4_workload5_full():
-    _moe_full(5, [0, 64, 127], four_over_six=True)
+    _moe_full(5, [0, 9, 33, 64, 90, 101, 116, 127], four_over_six=True)
 
 
 @pytest.mark.parametrize("M,N,K", [(128, 128, 64), (256, 384, 192), (384, 512, 320)])
