@@ -542,9 +542,12 @@ __device__ __forceinline__ f32x16 mfma16(bf16x8 b, bf16x8 a, f32x16 acc) {
 // (workgroup w runs on XCD w % 8, so each XCD works on a contiguous range of
 // tiles: an expert's weights and token rows stay in that XCD's L2), with one
 // segment scan per workgroup and no launch or scan cost per tile.
+template <bool B> struct Split { static constexpr bool value = B; };
+
 template <int FMT, int WGRAD, int OUT>
 __global__ __launch_bounds__(kThreads) void k_gemm(const GemmArgs g) {
   static_assert(BM == BN, "A and B LDS buffers share one layout");
+  static_assert(WN * 4 * TJ * 4 * 64 * 16 <= 4 * BM * kRow, "tail-tile partial sums fit in the operand buffers");
   static_assert(2 * BM % (kThreads / Slab<FMT>::CPR) == 0, "whole slab rows per thread");
   static_assert(BM * (BN * 2 + 8) <= 4 * BM * kRow && 128 * (BN * 4 + 16) <= 4 * BM * kRow, "epilogue staging fits");
   __shared__ __attribute__((aligned(16))) uint8_t s_ab[4][BM * kRow];  // A buffers 0, 1; B buffers 0, 1
@@ -606,102 +609,177 @@ __global__ __launch_bounds__(kThreads) void k_gemm(const GemmArgs g) {
   const int frag_off = (lane & 31) * kRow + (lane >> 5) * 16;
   const int a_off = wm * 128 * kRow + frag_off;
   const int b_off = wn * 32 * TJ * kRow + frag_off;
-#define BSQ_LOAD_FRAGS(slot, buf, ks)                                                              \
+  // Tail tiles (segments along M, at most 128 rows of the tile inside the
+  // segment): both halves of the waves multiply rows 0..127, half wm taking the
+  // k slices 2 wm and 2 wm + 1 of every step; the two partial sums are added
+  // after the K loop. Half the MFMA work of a full tile, whose second 128 rows
+  // would all lie past the segment.
+  const int a_off_s = frag_off + 64 * wm;
+  const int b_off_s = b_off + 64 * wm;
+#define BSQ_LOAD_FRAGS(slot, buf, ks, ao, bo)                                                      \
   _Pragma("unroll") for (int i_ = 0; i_ < 4; ++i_) fa[slot][i_] =                                  \
-      *reinterpret_cast<const V8*>(&sA[buf][a_off + i_ * 32 * kRow + (ks) * 32]);                  \
+      *reinterpret_cast<const V8*>(&sA[buf][(ao) + i_ * 32 * kRow + (ks) * 32]);                   \
   _Pragma("unroll") for (int j_ = 0; j_ < TJ; ++j_) fb[slot][j_] =                                 \
-      *reinterpret_cast<const V8*>(&sB[buf][b_off + j_ * 32 * kRow + (ks) * 32]);
+      *reinterpret_cast<const V8*>(&sB[buf][(bo) + j_ * 32 * kRow + (ks) * 32]);
 
+  // One tile: full (256 output rows) or tail (SPLIT); the two K-loop
+  // variants are separate instantiations inside the one tile walk below.
+  auto tile_body = [&](auto split_tag, const Tile& tl) {
+    constexpr bool SPLIT = decltype(split_tag)::value;
+    {
+      // The thread's slab rows, derived anew per tile from an opaque copy of
+      // the thread index: hoisted out of the tile loop they stay live across
+      // the K loop and spill, and the reload in the next tile's prologue waits
+      // for the previous tile's stores (one counter orders both).
+      int tr = t;
+      asm volatile("" : "+v"(tr));
+      uint32_t off[SR];  // row code offsets in units of 32 bytes (every row starts at a multiple of 32)
+#pragma unroll
+      for (int i = 0; i < SR; ++i)
+        off[i] = (uint32_t)(row_off<WGRAD, FMT == FMT_NVFP4 ? 2 : 1>(g, tl, i < SR / 2,
+                                                                      (tr / CPR + (kThreads / CPR) * i) & (BM - 1)) >> 5);
+
+      f32x16 acc[4][TJ];
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int j = 0; j < TJ; ++j)
+#pragma unroll
+          for (int q = 0; q < 16; ++q) acc[i][j][q] = 0.0f;
+      V8 fa[2][4], fb[2][TJ];
+      const int nk = (int)((tl.klen + BK - 1) / BK);
+
+      // Software pipeline. At the start of step kt, `cur` holds step kt + 1 as
+      // loaded and the loads of step kt + 2 go out into `nxt` (clamped: the last
+      // steps load and decode a duplicate that is never read). Each 16-wide k
+      // slice then reads the next slice's fragments, runs this slice's MFMAs and
+      // decodes one quarter of `cur` into the other LDS buffer; the barrier at the
+      // end of the step publishes that buffer (every read of it from the previous
+      // step finished before the previous barrier). The two register sets swap
+      // roles every step (the loop body is unrolled twice). Tail tiles (SPLIT)
+      // run two slices per step, each over two iterations.
+      // Scale groups: group j (steps 4j .. 4j+3) is loaded with step 4j's codes
+      // (at step 4j - 2) into gnext and becomes gcur when step 4j is decoded.
+      Slab<FMT> r0, r1;
+      ScaleGrp<FMT> gcur, gnext;
+      auto step = [&](int kt, Slab<FMT>& cur, Slab<FMT>& nxt) {
+        const int ao = SPLIT ? a_off_s : a_off;
+        const int bo = SPLIT ? b_off_s : b_off;
+        const int buf = kt & 1;
+        load_slab(nxt, g, off, chunk, (int64_t)(kt + 2 < nk ? kt + 2 : nk - 1) * BK, tl.klen);
+        if (kt + 2 < nk && ((kt + 2) & 3) == 0) load_group(gnext, rsa, rsb, off, chunk, (kt + 2) >> 2);
+        __builtin_amdgcn_sched_barrier(0);  // keep the loads here: a whole step ahead of their use
+        const int dstep = kt + 1 < nk ? kt + 1 : nk - 1;  // the step `cur` holds
+        if (kt + 1 < nk && (dstep & 3) == 0) gcur = gnext;
+        const uint32_t sw = step_word(gcur, dstep & 3);
+        const uint32_t ssh = step_shift<FMT>(dstep & 3, chunk);
+#pragma unroll
+        for (int ks = 0; ks < 4; ++ks) {
+          if constexpr (SPLIT) {
+            // the wave's two slices (fragment slots 0, 1), each in two
+            // iterations of half its MFMAs (rows 64 (ks & 1) .. of the 128),
+            // so that every iteration still decodes one quarter
+            const int sl = ks >> 1, ih = ks & 1;
+            if (ks == 1) {
+              BSQ_LOAD_FRAGS(1, buf, 1, ao, bo)
+            }
+#pragma unroll
+            for (int i = 2 * ih; i < 2 * ih + 2; ++i)
+#pragma unroll
+              for (int j = 0; j < TJ; ++j) acc[i][j] = mfma16(fb[sl][j], fa[sl][i], acc[i][j]);
+          } else {
+            if (ks < 3) {
+              BSQ_LOAD_FRAGS((ks + 1) & 1, buf, ks + 1, ao, bo)
+            }
+#pragma unroll
+            for (int i = 0; i < 4; ++i)
+#pragma unroll
+              for (int j = 0; j < TJ; ++j) acc[i][j] = mfma16(fb[ks & 1][j], fa[ks & 1][i], acc[i][j]);
+          }
+#pragma unroll
+          for (int q = ks * QK; q < (ks + 1) * QK; ++q)
+            decode_quarter(cur, row_scale<FMT>(sw, ssh, quarter_row<FMT>(q)), qdst(buf ^ 1, q), q);
+          // interleave each MFMA with a few decode VALU ops, the fragment reads and the decode stores
+          constexpr int NM = SPLIT ? 2 * TJ : 4 * TJ;  // MFMAs of the iteration
+#pragma unroll
+          for (int m = 0; m < NM; ++m) {
+            __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);                          // MFMA
+            __builtin_amdgcn_sched_group_barrier(0x002, 48 / NM, 0);                    // VALU
+            if (SPLIT ? (ks == 1 && 2 * m < 4 + TJ) : (m < 4 + TJ))
+              __builtin_amdgcn_sched_group_barrier(0x100, SPLIT ? 2 : 1, 0);            // DS read
+            if (m >= NM - 2 * QK) __builtin_amdgcn_sched_group_barrier(0x200, 1, 0);    // DS write
+          }
+        }
+        __syncthreads();
+        BSQ_LOAD_FRAGS(0, buf ^ 1, 0, ao, bo)
+      };
+      if (nk > 0) {
+        load_slab(r0, g, off, chunk, 0, tl.klen);
+        load_group(gnext, rsa, rsb, off, chunk, 0);
+        gcur = gnext;
+        const uint32_t sw = step_word(gcur, 0);
+        const uint32_t ssh = step_shift<FMT>(0, chunk);
+#pragma unroll
+        for (int q = 0; q < quarters<FMT>(); ++q)
+          decode_quarter(r0, row_scale<FMT>(sw, ssh, quarter_row<FMT>(q)), qdst(0, q), q);
+        load_slab(r0, g, off, chunk, nk > 1 ? BK : 0, tl.klen);
+        __syncthreads();
+        BSQ_LOAD_FRAGS(0, 0, 0, SPLIT ? a_off_s : a_off, SPLIT ? b_off_s : b_off)
+      }
+      int kt = 0;
+      for (; kt + 1 < nk; kt += 2) {
+        step(kt, r0, r1);
+        step(kt + 1, r1, r0);
+      }
+      if (kt < nk) step(kt, r0, r1);
+
+      __syncthreads();  // every wave is done with the operand buffers
+      if constexpr (SPLIT) {
+        // the partial sums of half 1 (slices 2, 3) join those of half 0 through LDS
+        float4* red = reinterpret_cast<float4*>(lds0);
+        if (wm == 1) {
+#pragma unroll
+          for (int i = 0; i < 4; ++i)
+#pragma unroll
+            for (int j = 0; j < TJ; ++j)
+#pragma unroll
+              for (int q = 0; q < 4; ++q)
+                red[(((wn * 4 + i) * TJ + j) * 4 + q) * 64 + lane] =
+                    make_float4(acc[i][j][4 * q], acc[i][j][4 * q + 1], acc[i][j][4 * q + 2], acc[i][j][4 * q + 3]);
+        }
+        __syncthreads();
+        if (wm == 0) {
+#pragma unroll
+          for (int i = 0; i < 4; ++i)
+#pragma unroll
+            for (int j = 0; j < TJ; ++j)
+#pragma unroll
+              for (int q = 0; q < 4; ++q) {
+                const float4 p = red[(((wn * 4 + i) * TJ + j) * 4 + q) * 64 + lane];
+                acc[i][j][4 * q] += p.x;
+                acc[i][j][4 * q + 1] += p.y;
+                acc[i][j][4 * q + 2] += p.z;
+                acc[i][j][4 * q + 3] += p.w;
+              }
+        }
+        __syncthreads();  // the partial sums are read before the epilogue stages into LDS
+      }
+      store_tile<FMT == FMT_NVFP4, WGRAD, OUT>(g, tl, acc, wm, wn, lane, lds0);
+      __syncthreads();  // the staging reads are done before the next tile decodes into LDS
+    }
+  };
   for (int64_t lt = blockIdx.x / kXcds; lt < per_xcd; lt += wpx) {
     const int64_t tile = tile0 + lt;
     if (tile >= total) break;
     Tile tl;
     constexpr int GN = FMT == FMT_NVFP4 ? 1 << 20 : 4;  // n-tiles per group (above)
     if (!tile_coords<WGRAD, BM, GN>(g, s_cum, s_seg, tile, tl)) continue;  // uniform across the workgroup
-    uint32_t off[SR];  // row code offsets in units of 32 bytes (every row starts at a multiple of 32)
-#pragma unroll
-    for (int i = 0; i < SR; ++i)
-      off[i] = (uint32_t)(row_off<WGRAD, FMT == FMT_NVFP4 ? 2 : 1>(g, tl, i < SR / 2,
-                                                                    (t / CPR + (kThreads / CPR) * i) & (BM - 1)) >> 5);
-
-    f32x16 acc[4][TJ];
-#pragma unroll
-    for (int i = 0; i < 4; ++i)
-#pragma unroll
-      for (int j = 0; j < TJ; ++j)
-#pragma unroll
-        for (int q = 0; q < 16; ++q) acc[i][j][q] = 0.0f;
-    V8 fa[2][4], fb[2][TJ];
-    const int nk = (int)((tl.klen + BK - 1) / BK);
-
-    // Software pipeline. At the start of step kt, `cur` holds step kt + 1 as
-    // loaded and the loads of step kt + 2 go out into `nxt` (clamped: the last
-    // steps load and decode a duplicate that is never read). Each 16-wide k
-    // slice then reads the next slice's fragments, runs this slice's MFMAs and
-    // decodes one quarter of `cur` into the other LDS buffer; the barrier at the
-    // end of the step publishes that buffer (every read of it from the previous
-    // step finished before the previous barrier). The two register sets swap
-    // roles every step (the loop body is unrolled twice).
-    // Scale groups: group j (steps 4j .. 4j+3) is loaded with step 4j's codes
-    // (at step 4j - 2) into gnext and becomes gcur when step 4j is decoded.
-    Slab<FMT> r0, r1;
-    ScaleGrp<FMT> gcur, gnext;
-    auto step = [&](int kt, Slab<FMT>& cur, Slab<FMT>& nxt) {
-      const int buf = kt & 1;
-      load_slab(nxt, g, off, chunk, (int64_t)(kt + 2 < nk ? kt + 2 : nk - 1) * BK, tl.klen);
-      if (kt + 2 < nk && ((kt + 2) & 3) == 0) load_group(gnext, rsa, rsb, off, chunk, (kt + 2) >> 2);
-      __builtin_amdgcn_sched_barrier(0);  // keep the loads here: a whole step ahead of their use
-      const int dstep = kt + 1 < nk ? kt + 1 : nk - 1;  // the step `cur` holds
-      if (kt + 1 < nk && (dstep & 3) == 0) gcur = gnext;
-      const uint32_t sw = step_word(gcur, dstep & 3);
-      const uint32_t ssh = step_shift<FMT>(dstep & 3, chunk);
-#pragma unroll
-      for (int ks = 0; ks < 4; ++ks) {
-        if (ks < 3) {
-          BSQ_LOAD_FRAGS((ks + 1) & 1, buf, ks + 1)
-        }
-#pragma unroll
-        for (int i = 0; i < 4; ++i)
-#pragma unroll
-          for (int j = 0; j < TJ; ++j) acc[i][j] = mfma16(fb[ks & 1][j], fa[ks & 1][i], acc[i][j]);
-#pragma unroll
-        for (int q = ks * QK; q < (ks + 1) * QK; ++q)
-          decode_quarter(cur, row_scale<FMT>(sw, ssh, quarter_row<FMT>(q)), qdst(buf ^ 1, q), q);
-        // interleave each MFMA with a few decode VALU ops, the fragment reads and the decode stores
-#pragma unroll
-        for (int m = 0; m < 4 * TJ; ++m) {
-          __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);                     // MFMA
-          __builtin_amdgcn_sched_group_barrier(0x002, 12 / TJ, 0);               // VALU
-          if (m < 4 + TJ) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);     // DS read
-          if (m >= 4 * TJ - 2 * QK) __builtin_amdgcn_sched_group_barrier(0x200, 1, 0);  // DS write
-        }
-      }
-      __syncthreads();
-      BSQ_LOAD_FRAGS(0, buf ^ 1, 0)
-    };
-    if (nk > 0) {
-      load_slab(r0, g, off, chunk, 0, tl.klen);
-      load_group(gnext, rsa, rsb, off, chunk, 0);
-      gcur = gnext;
-      const uint32_t sw = step_word(gcur, 0);
-      const uint32_t ssh = step_shift<FMT>(0, chunk);
-#pragma unroll
-      for (int q = 0; q < quarters<FMT>(); ++q)
-        decode_quarter(r0, row_scale<FMT>(sw, ssh, quarter_row<FMT>(q)), qdst(0, q), q);
-      load_slab(r0, g, off, chunk, nk > 1 ? BK : 0, tl.klen);
-      __syncthreads();
-      BSQ_LOAD_FRAGS(0, 0, 0)
+    if constexpr (WGRAD) {
+      tile_body(Split<false>{}, tl);
+    } else {
+      if (tl.Me - tl.m0 <= 128) tile_body(Split<true>{}, tl);  // uniform: at most 128 rows left
+      else tile_body(Split<false>{}, tl);
     }
-    int kt = 0;
-    for (; kt + 1 < nk; kt += 2) {
-      step(kt, r0, r1);
-      step(kt + 1, r1, r0);
-    }
-    if (kt < nk) step(kt, r0, r1);
-
-    __syncthreads();  // every wave is done with the operand buffers
-    store_tile<FMT == FMT_NVFP4, WGRAD, OUT>(g, tl, acc, wm, wn, lane, lds0);
-    __syncthreads();  // the staging reads are done before the next tile decodes into LDS
   }
 #undef BSQ_LOAD_FRAGS
 }

@@ -207,6 +207,41 @@ def test_gemm_short_k(K):
     _check(h(y), yref, yabs, f"mxfp8 dgrad short K={K}")
 
 
+@pytest.mark.parametrize("K", [128, 192])
+def test_gemm_tail_tiles(K):
+    """Segments whose last 256-row tile holds 1, 127, 128 or 129..255 rows:
+    a last tile with at most 128 rows runs as a tail tile (both halves of the
+    workgroup on its first 128 rows, each over half of every K step, partial
+    sums added at the end); 129 rows and more run as a full tile. NVFP4
+    forward (gathered rows, bf16 = RNE of the float32 result) and MXFP8 DGRAD,
+    with an even and an odd number of K steps."""
+    log(f"gemm tail tiles K={K}")
+    rng = np.random.default_rng(900 + K)
+    lens = [128, 129, 1, 255, 256, 384, 385, 127, 0, 640]
+    seg = np.concatenate([[0], np.cumsum(lens)]).astype(np.int64)
+    M, E, N, T = int(seg[-1]), len(lens), 256, 700
+    row_index = rng.integers(0, T, size=M).astype(np.int32)
+    x = rng.standard_t(3, (T, K)).astype(f32)
+    w = (rng.standard_normal((E, N, K)) * 0.02).astype(f32)
+    ap, as_, ao = Q.quantize_nvfp4(x[None], Q.OUTER_ROW, four_over_six=True)
+    bp, bs, bo = Q.quantize_nvfp4(w, Q.OUTER_TENSOR)
+    ao, bo = np.asarray(ao).reshape(-1), np.asarray(bo).reshape(-1)
+    y32, y16 = _nvfp4(t(ap[0]), t(as_[0]), t(ao), t(bp), t(bs), t(bo), t(seg), M, row_index=t(row_index))
+    yref, yabs = G.grouped_gemm_nvfp4_ref(ap[0], as_[0], ao, row_index, bp, bs, bo, seg)
+    _check(h(y32), yref, yabs, f"nvfp4 tail tiles K={K}")
+    _check_bf16(h(y16.view(torch.int16)), h(y32), f"nvfp4 tail tiles K={K}")
+    g = (rng.standard_normal((M, K)) * 1e-3).astype(f32)
+    ac, as2 = _mxfp8_from(rng, g)
+    wt = (rng.standard_normal((E * N, K)) * 0.02).astype(f32)
+    bc, bs2 = _mxfp8_from(rng, wt)
+    bc, bs2 = bc.reshape(E, N, K), bs2.reshape(E, N, K // 32)
+    y = bsq.grouped_gemm_mxfp8(False, t(ac), t(as2), t(bc), t(bs2), t(seg), M, N, K, out_dtype=torch.float32)
+    y16 = bsq.grouped_gemm_mxfp8(False, t(ac), t(as2), t(bc), t(bs2), t(seg), M, N, K)
+    yref, yabs = G.mxfp8_dgrad_ref(ac, as2, bc, bs2, seg)
+    _check(h(y), yref, yabs, f"mxfp8 dgrad tail tiles K={K}")
+    _check_bf16(h(y16.view(torch.int16)), h(y), f"mxfp8 dgrad tail tiles K={K}")
+
+
 def test_gemm_mxfp8_scale_code_range():
     """The bf16 decode of MXFP8 operands over the whole E8M0 range: row r of A
     holds 32 copies of one E4M3 value q under scale code c_r (block 0; block 1
