@@ -36,7 +36,9 @@
 // two register sets. Persistent workgroups (one per CU) walk contiguous tile
 // ranges of their XCD (workgroup w runs on XCD w % 8), keeping an expert's
 // weights and token rows in that XCD's L2; tiles map to (expert, m-tile,
-// n-tile) through one in-workgroup scan of the segment offsets.
+// n-tile) through one in-workgroup scan of the segment offsets. A segment's
+// last m-tile with at most 128 rows runs as a tail tile: both wave halves
+// on its first 128 rows, each over half of every K step's slices.
 //   FPROP/DGRAD (segments along M): row r of expert e reads A row a_row(r)
 //     (gathered token for FPROP) and B[e]; out[r, n].
 //   WGRAD (segments along K): A_e [M, Kp_e], B_e [N, Kp_e] in the padded
