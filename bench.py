@@ -373,6 +373,33 @@ def dense_library_gemm(torch, dev, reps=5):
     return res
 
 
+def gemm_operand_data(torch, bsq, state, seg, ri, reps=5):
+    """FPROP and DGRAD launched on the step's operands and on copies whose
+    codes are all zero (same shapes, block scales, tiles and instruction
+    stream; only the values the MFMAs and decode see differ). The GEMMs run
+    at the chip's power limit, so the time depends on the data's switching
+    activity: the zero-coded launches show how much of the gap to the
+    16-bit peak is the clock, not the kernel."""
+    xc, xs, xo = state["xq"]
+    wc, ws, wo = state["wq"]
+    gc, gs = state["gq"]
+    wtc, wts = state["wt"]
+    out = {"fprop": _time(torch, lambda: bsq.grouped_gemm_nvfp4(xc, xs, xo, wc, ws, wo, seg, M, row_index=ri), reps)}
+    zx, zw = torch.zeros_like(xc), torch.zeros_like(wc)
+    out["fprop_zero_codes"] = _time(
+        torch, lambda: bsq.grouped_gemm_nvfp4(zx, xs, xo, zw, ws, wo, seg, M, row_index=ri), reps)
+    del zx, zw
+    out["dgrad"] = _time(torch, lambda: bsq.grouped_gemm_mxfp8(False, gc, gs, wtc, wts, seg, M, H, F), reps)
+    zg, zt = torch.zeros_like(gc), torch.zeros_like(wtc)
+    out["dgrad_zero_codes"] = _time(torch, lambda: bsq.grouped_gemm_mxfp8(False, zg, gs, zt, wts, seg, M, H, F), reps)
+    del zg, zt
+    torch.cuda.empty_cache()
+    res = {k: round(v, 4) for k, v in out.items()}
+    res["unit"] = "ms"
+    res["what"] = "the step's FPROP and DGRAD on its operands and on all-zero codes (same scales and launches)"
+    return res
+
+
 def chain_forward(torch, bsq, inp, algo, dev, pair_row, reps=5):
     """The expert forward chain (w13 GEMM, SwiGLU + per-row NVFP4, w2 GEMM with
     the RHT + S2F6 combine codec in its epilogue, combine) on the step's
@@ -582,6 +609,7 @@ def main():
         alternatives["workload5_fwd"] = workload5(torch, bsq, dev)
         alternatives["nvfp4_scale_handling"] = scale_handling(torch, bsq, inp, state["xq"], dev)
         alternatives["dense_bf16_library_gemm"] = dense_library_gemm(torch, dev)
+        alternatives["gemm_operand_data"] = gemm_operand_data(torch, bsq, state, seg, ri)
 
     if args.copy_calibration:
         src_buf = torch.empty(512 << 20, dtype=torch.uint8, device=dev).fill_(1)
