@@ -160,8 +160,9 @@ __device__ int64_t scan_units(const GemmArgs& g, int64_t* s_cum, int64_t* s_part
 // run about 32 consecutive tiles at a time, roughly in step along K, so a
 // group keeps (rows of the group's m-tiles + rows of its n-tiles) per K step
 // in that XCD's L2 rather than every n-tile of the expert. Measured: groups
-// of 4 take 1-3% off the MXFP8 GEMMs (16 n-tiles of 256); the NVFP4 forward
-// (6 n-tiles) is best ungrouped.
+// of 4 take 1-3% off the MXFP8 GEMMs (16 n-tiles of 256) and 0-2% off the
+// NVFP4 forward (6 n-tiles; 8 n-tiles at hidden 7168: 1-2%); groups of 2 no
+// better.
 template <int GN>
 __device__ __forceinline__ void group_mn(int64_t li, int64_t mt, int64_t ntn, int64_t& m, int64_t& n) {
   const int64_t grp = li / (mt * GN);               // the groups before it are whole
@@ -774,7 +775,7 @@ __global__ __launch_bounds__(kThreads) void k_gemm(const GemmArgs g) {
     const int64_t tile = tile0 + lt;
     if (tile >= total) break;
     Tile tl;
-    constexpr int GN = FMT == FMT_NVFP4 ? 1 << 20 : 4;  // n-tiles per group (above)
+    constexpr int GN = 4;  // n-tiles per group (above)
     if (!tile_coords<WGRAD, BM, GN>(g, s_cum, s_seg, tile, tl)) continue;  // uniform across the workgroup
     if constexpr (WGRAD) {
       tile_body(Split<false>{}, tl);
