@@ -400,6 +400,31 @@ def gemm_operand_data(torch, bsq, state, seg, ri, reps=5):
     return res
 
 
+def mfma_rates(torch, bsq, reps=3, iters=20000):
+    """Per-instruction MFMA throughput (bsq_mfma_rate_probe): two workgroups
+    of 4 waves per CU, each wave running only MFMAs on register operands,
+    for the 16-bit instructions the GEMMs use, the K = 16 FP8 instruction and
+    the block-scaled FP8 / FP4 instructions, on random, two-significant-bit
+    and zero operand data. Against the nominal dense peaks (2.5 / 5.0 / 10.1
+    PFLOP/s at 2.4 GHz) these give the sustained rate of each instruction on
+    this chip and how much of it is power (data dependence)."""
+    wg = 2 * torch.cuda.get_device_properties(0).multi_processor_count
+    names = {0: ("f16_32x32x16", 32768, 2500.0), 1: ("bf16_32x32x16", 32768, 2500.0),
+             2: ("fp8_32x32x16", 32768, 5000.0), 3: ("scaled_fp8_32x32x64", 131072, 5000.0),
+             4: ("scaled_fp4_32x32x64", 131072, 10100.0)}
+    datas = {0: "random", 2: "two_bit", 1: "zero"}
+    out = {}
+    for kind, (name, flop, peak) in names.items():
+        row = {"nominal_peak_tflops": peak}
+        for data, dname in datas.items():
+            ms = _time(torch, lambda: bsq.mfma_rate_probe(kind, data, iters, wg), reps)
+            tf = wg * 4 * iters * 4 * flop / (ms * 1e-3) / 1e12
+            row[dname] = {"ms": round(ms, 4), "tflops": round(tf, 1), "frac": round(tf / peak, 4)}
+        out[name] = row
+    out["what"] = f"{wg} workgroups x 4 waves x {iters} rounds of 4 independent MFMA chains, register operands"
+    return out
+
+
 def chain_forward(torch, bsq, inp, algo, dev, pair_row, reps=5):
     """The expert forward chain (w13 GEMM, SwiGLU + per-row NVFP4, w2 GEMM with
     the RHT + S2F6 combine codec in its epilogue, combine) on the step's
@@ -610,6 +635,7 @@ def main():
         alternatives["nvfp4_scale_handling"] = scale_handling(torch, bsq, inp, state["xq"], dev)
         alternatives["dense_bf16_library_gemm"] = dense_library_gemm(torch, dev)
         alternatives["gemm_operand_data"] = gemm_operand_data(torch, bsq, state, seg, ri)
+        alternatives["mfma_rate"] = mfma_rates(torch, bsq)
 
     if args.copy_calibration:
         src_buf = torch.empty(512 << 20, dtype=torch.uint8, device=dev).fill_(1)

@@ -47,6 +47,7 @@ SIGNATURES = {
     "bsq_dequantize_nvfp4": (c_int, [c_vp, c_vp, c_vp, c_int, c_i64, c_i64, c_i64, c_vp, c_vp]),
     "bsq_dequantize_mxfp8": (c_int, [c_vp, c_vp, c_i64, c_i64, c_vp, c_vp]),
     "bsq_rng_bits16": (c_int, [c_u64, c_u64, c_u64, c_i64, c_vp, c_vp]),
+    "bsq_mfma_rate_probe": (c_int, [c_int, c_int, c_i64, c_i64, c_vp, c_vp]),
 }
 
 

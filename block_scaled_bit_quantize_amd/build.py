@@ -8,7 +8,7 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(HERE, "csrc")
 BUILD = os.path.join(HERE, "_build")
 LIB = os.path.join(HERE, "libbsq.so")
-SOURCES = ["quantize.hip", "transpose_quant.hip", "route.hip", "gemm.hip", "gemm_inreg.hip", "codec.hip"]
+SOURCES = ["quantize.hip", "transpose_quant.hip", "route.hip", "gemm.hip", "gemm_inreg.hip", "codec.hip", "probe.hip"]
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 FLAGS = [

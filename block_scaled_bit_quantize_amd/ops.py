@@ -375,3 +375,12 @@ def rng_bits16(seed, stream_id, first, n, device="cuda"):
     out = torch.empty((n,), dtype=torch.int16, device=device)
     check(lib.bsq_rng_bits16(seed, stream_id, first, n, out.data_ptr(), _stream()), "bsq_rng_bits16")
     return out
+
+
+def mfma_rate_probe(kind, data, iters, workgroups, device="cuda"):
+    """Launch the per-instruction MFMA throughput probe (see bsq.h) and
+    return its output tensor [workgroups * 256]; the caller times the launch."""
+    lib = load_library()
+    out = torch.empty((workgroups * 256,), dtype=torch.float32, device=device)
+    check(lib.bsq_mfma_rate_probe(kind, data, iters, workgroups, out.data_ptr(), _stream()), "bsq_mfma_rate_probe")
+    return out

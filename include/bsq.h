@@ -430,6 +430,26 @@ int bsq_dequantize_mxfp8(const uint8_t* codes, const uint8_t* scales, int64_t ro
 int bsq_rng_bits16(uint64_t seed, uint64_t stream_id, uint64_t first, int64_t n, uint16_t* out,
                    bsq_stream_t stream);
 
+/* ------------------------------------------------------------------------
+ * Measurement support: per-instruction MFMA throughput ("Kernels for
+ * low-precision training": the matrix instructions set the GEMMs' rate).
+ * Launches `workgroups` workgroups of 256 threads; every wave runs `iters`
+ * rounds of four independent accumulator chains of one MFMA instruction on
+ * operands held in registers (nothing but MFMAs in the loop):
+ *   kind 0 v_mfma_f32_32x32x16_f16, 1 ..._bf16, 2 ..._fp8_fp8 (2*32*32*16
+ *   FLOP each); 3 v_mfma_scale_f32_32x32x64_f8f6f4 on E4M3, 4 the same on
+ *   E2M1 (2*32*32*64 FLOP each; E8M0 scales of one).
+ *   data 0 random finite operands, 1 zeros, 2 values with at most two
+ *   significant bits (the GEMMs run at the chip's power limit, so the rate
+ *   depends on how many operand bits switch).
+ * Total FLOP = workgroups * 4 waves * iters * 4 * FLOP per instruction; the
+ * caller times the launch. out: workgroups * 256 floats (one accumulator
+ * element per thread, so no MFMA is dead code; the values are not meaningful).
+ * 1 <= iters <= 2^24, 1 <= workgroups <= 65535. Errors: NULL, SHAPE, ALIGN,
+ * ENUM, LAUNCH.
+ * ---------------------------------------------------------------------- */
+int bsq_mfma_rate_probe(int kind, int data, int64_t iters, int64_t workgroups, float* out, bsq_stream_t stream);
+
 #ifdef __cplusplus
 }
 #endif

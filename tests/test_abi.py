@@ -204,3 +204,14 @@ def test_gemm_and_route_validation(lib):
     assert rn(FAKE, 4096 * 256 + 1, 1, 64, FAKE, FAKE, FAKE, None) == E_WORKSPACE
     assert rn(FAKE, 256 * 256 + 1, 1, 1024, FAKE, FAKE, FAKE, None) == E_WORKSPACE
     assert lib.bsq_route_workspace(4096 * 256, 64) == _lib.ROUTE_NOALLOC_MAX_BYTES
+
+
+def test_mfma_rate_probe_validation(lib):
+    p = lib.bsq_mfma_rate_probe  # checked before any device call
+    assert p(5, 0, 10, 8, FAKE, None) == E_ENUM
+    assert p(0, 3, 10, 8, FAKE, None) == E_ENUM
+    assert p(0, 0, 0, 8, FAKE, None) == E_SHAPE
+    assert p(0, 0, 10, 0, FAKE, None) == E_SHAPE
+    assert p(0, 0, 10, 70000, FAKE, None) == E_SHAPE
+    assert p(0, 0, 10, 8, None, None) == E_NULL
+    assert p(0, 0, 10, 8, FAKE + 2, None) == E_ALIGN

@@ -369,3 +369,15 @@ def test_gemm_mxfp8_workload4_full():
         ys = h(dw[e])
         yref, yabs = G.mxfp8_wgrad_ref(A, As, B, Bs, seg, Ng, Kx, experts=[e])
         _check(ys, yref[0], yabs[0], f"mxfp8 wgrad workload4 expert {e}")
+
+
+@pytest.mark.parametrize("kind", [0, 1, 2, 3, 4])
+def test_mfma_rate_probe_runs(kind):
+    """The throughput probe's launches complete and keep every accumulator:
+    zero operands give exactly zero, the other data kinds finite values."""
+    log(f"mfma rate probe kind={kind}")
+    z = h(bsq.mfma_rate_probe(kind, 1, 8, 4))
+    assert z.shape == (1024,) and np.all(z == 0.0)
+    for data in (0, 2):
+        r = h(bsq.mfma_rate_probe(kind, data, 8, 4))
+        assert np.all(np.isfinite(r)) and np.any(r != 0.0)
