@@ -108,6 +108,7 @@ def algorithmic(seg_host):
         # not step stages: the square-tile weight quantizer (both layouts from one
         # read) and the combine codec on the dispatched expert output rows [M, H]
         "quant_w_square": ("GB/s", E * F * H * 2 + 2 * nv(E * F, H) + E * 4),
+        "quant_g_dual": ("GB/s", M * F * 2 + mx(M * F) + mx(F * smp)),
         "combine_encode": ("GB/s", M * H * 2 + M * H + M * H // 32),
         "combine_decode": ("GB/s", M * H + M * H // 32 + M * 4 + T * H * 2),
         # the expert forward chain (w13 GEMM, SwiGLU + quantize, w2 GEMM + codec)
@@ -604,6 +605,17 @@ def main():
             "frac": round(ach / HBM_PEAK_GBS, 4),
             "traffic": read_traffic("quant_w_square", kernel_sha(*stage_sources("quant_w_square"))),
             "alternative_to": "quant_w + requant_w where the backward reads W^T in NVFP4 (square tiles) instead of SR MXFP8"}
+        # both MXFP8 quantizations of g from one read (the step times them as
+        # two stages, quant_g_rows and quant_g_t)
+        ms = _time(torch, lambda: bsq.quantize_mxfp8_dual(inp["g"], "sr", seed=42, stream_rows=1, stream_t=2,
+                                                           seg_offsets=seg, out_elems=n_gt), reps)
+        ach = algo["quant_g_dual"][1] / (ms * 1e-3) / 1e9
+        alternatives["quant_g_dual"] = {
+            "ms": round(ms, 4), "achieved": round(ach, 2), "unit": "GB/s", "peak": HBM_PEAK_GBS,
+            "frac": round(ach / HBM_PEAK_GBS, 4),
+            "traffic": read_traffic("quant_g_dual", kernel_sha(*stage_sources("quant_g_dual"))),
+            "separate_ms": round(kernels["quant_g_rows"]["ms"] + kernels["quant_g_t"]["ms"], 4),
+            "alternative_to": "quant_g_rows + quant_g_t (g read once instead of twice)"}
         # the combine codec (RHT-32 + block-scaled S2F6) on the expert output
         # rows of the layer's combine: [tokens * topk, hidden] bf16, seeded
         import synth

@@ -28,6 +28,8 @@ SIGNATURES = {
     "bsq_quantize_mxfp8_workspace": (c_size, [c_i64, c_int, c_i64]),
     "bsq_quantize_mxfp8": (c_int, [c_vp, c_int, c_i64, c_i64, c_int, c_vp, c_i64, c_int, c_u64, c_u64, c_vp, c_vp,
                                    c_vp, c_size, c_vp]),
+    "bsq_quantize_mxfp8_dual": (c_int, [c_vp, c_int, c_i64, c_i64, c_vp, c_i64, c_int, c_u64, c_u64, c_u64, c_vp,
+                                        c_vp, c_vp, c_vp, c_vp, c_size, c_vp]),
     "bsq_requant_workspace": (c_size, [c_i64, c_i64, c_i64, c_int, c_int]),
     "bsq_requant_transpose_sr": (c_int, [c_vp, c_vp, c_vp, c_int, c_i64, c_i64, c_i64, c_i64, c_vp, c_vp, c_i64,
                                          c_int, c_int, c_u64, c_u64, c_vp, c_vp, c_vp, c_vp, c_size, c_vp]),

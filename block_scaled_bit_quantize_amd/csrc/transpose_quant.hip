@@ -159,14 +159,25 @@ template <int SRC> constexpr int tile_channels() { return SRC == SRC_NVFP4 ? 128
 // for bf16 and float sources, whose 18 KB tile lets more workgroups share a
 // CU: measured 5% faster than 128 for the bf16 gradient); in phase 2 a thread
 // owns CPT = TCH/64 adjacent channels x 32 tokens.
-template <int SRC, int OUTF, int RND, bool SEG>
+// ROWS (bf16 and float sources, segmented MXFP8 output): the same launch also
+// writes the row-wise MXFP8 quantization of the tile's rows (blocks of 32
+// along channels, element index row * C + channel, its own random stream), so
+// that a gradient quantized both ways is read from HBM once.
+struct RowOut {
+  uint8_t* codes = nullptr;   // [rows, C]
+  uint8_t* scales = nullptr;  // [rows, C / 32]
+  uint64_t stream_id = 0;
+};
+
+template <int SRC, int OUTF, int RND, bool SEG, bool ROWS = false>
 __global__ __launch_bounds__(kThreads) void k_tq(
     const void* __restrict__ src, const uint8_t* __restrict__ in_scales, const float* __restrict__ in_outer,
     int in_mode, int64_t C, int64_t R, const int32_t* __restrict__ gather, const int64_t* __restrict__ seg_start_p,
     const int64_t* __restrict__ seg_len_p, const int32_t* __restrict__ slot_seg, const int32_t* __restrict__ slot_mt,
     const int64_t* __restrict__ seg_base, const uint32_t* __restrict__ amax_bits, uint64_t seed, uint64_t stream_id,
     uint8_t* __restrict__ out_codes, uint8_t* __restrict__ out_scales, float* __restrict__ out_outer,
-    int64_t ntiles) {
+    int64_t ntiles, RowOut rows = RowOut{}) {
+  static_assert(!ROWS || (SRC != SRC_NVFP4 && OUTF == BSQ_MXFP8 && SEG), "row output: bf16/float source, segmented MXFP8");
   typedef typename TileT<SRC>::type TT;
   constexpr int TCH = tile_channels<SRC>();
   constexpr int CPT = TCH / 64;
@@ -269,6 +280,48 @@ __global__ __launch_bounds__(kThreads) void k_tq(
     }
   }
   __syncthreads();
+
+  // ---- phase R (ROWS): thread -> tile row t / 2, channels c0 + 32 (t % 2) .. +31
+  // (reads the tile only; the phase-2 barrier below orders these reads before
+  // the tile buffer is reused as the output stage)
+  if constexpr (ROWS) {
+    const int m = t >> 1, cb = 32 * (t & 1);
+    if (m0 + m < Me && c0 + cb < C) {
+      float z[32];
+#pragma unroll
+      for (int q = 0; q < (SRC == SRC_F32 ? 8 : 4); ++q) {
+        const uint4 v = *reinterpret_cast<const uint4*>(&tile[m * LROW + (cb * (int)sizeof(TT)) + 16 * q]);
+        const uint32_t w[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+          if constexpr (SRC == SRC_F32) {
+            z[4 * q + u] = __uint_as_float(w[u]);
+          } else {
+            z[8 * q + 2 * u] = __uint_as_float(w[u] << 16);
+            z[8 * q + 2 * u + 1] = __uint_as_float(w[u] & 0xFFFF0000u);
+          }
+        }
+      }
+      float amax = 0.0f;
+#pragma unroll
+      for (int i = 0; i < 32; ++i) amax = fmaxf(amax, fabsf(z[i]));
+      const int ex = e8m0_exponent(amax);
+      const int64_t idx = (seg_start + m0 + m) * C + c0 + cb;  // element index of z[0] (row-major)
+      uint32_t out[8];
+      if constexpr (RND == BSQ_SR) {
+        sr_block_e4m3(z, ex, seed, rows.stream_id, (uint64_t)(idx >> 3), out);
+      } else {
+        const float pw = pow2_neg(ex);
+#pragma unroll
+        for (int o = 0; o < 8; ++o)
+          out[o] = e4m3_exact2(z[4 * o] * pw, z[4 * o + 1] * pw) | (e4m3_exact2(z[4 * o + 2] * pw, z[4 * o + 3] * pw) << 16);
+      }
+      uint4* dst = reinterpret_cast<uint4*>(rows.codes + idx);
+      dst[0] = make_uint4(out[0], out[1], out[2], out[3]);
+      dst[1] = make_uint4(out[4], out[5], out[6], out[7]);
+      rows.scales[idx >> 5] = (uint8_t)(ex + 127);
+    }
+  }
 
   // ---- phase 2: thread -> channels c0 + CPT*lane .. +CPT-1, tokens m0 + 32*wave .. +31
   const int cl = CPT * (t & 63);
@@ -486,23 +539,24 @@ inline unsigned tq_grid(int64_t ntiles, int64_t nct) { return (unsigned)((ntiles
 
 // rows: dispatched rows (segments cover [0, rows)); in_rows: rows of the
 // input table that gathered indices point into.
-template <int SRC>
+template <int SRC, bool ROWS = false>
 int launch_tq_seg(const void* src, const uint8_t* in_scales, const float* in_outer, int in_mode, int64_t C,
                   const int32_t* gather, const int64_t* seg, int64_t nseg, int64_t rows, int64_t in_rows, int rnd,
-                  uint64_t seed, uint64_t sid, uint8_t* oc, uint8_t* os, void* ws, hipStream_t s) {
+                  uint64_t seed, uint64_t sid, uint8_t* oc, uint8_t* os, void* ws, hipStream_t s,
+                  RowOut row_out = RowOut{}) {
   const Plan p = make_plan(ws, rows, nseg);
   hipLaunchKernelGGL(k_seg_plan, dim3(1), dim3(1024), 0, s, seg, (int)nseg, rows, C, TM, p.nslots, p.slot_seg,
                      p.slot_mt, p.seg_base, p.seg_start, p.seg_len);
   constexpr int TCH = tile_channels<SRC>();
   const dim3 grid(tq_grid(p.nslots, (C + TCH - 1) / TCH));
   if (rnd == BSQ_SR)
-    hipLaunchKernelGGL((k_tq<SRC, BSQ_MXFP8, BSQ_SR, true>), grid, dim3(kThreads), 0, s, src, in_scales, in_outer,
-                       in_mode, C, in_rows, gather, p.seg_start, p.seg_len, p.slot_seg, p.slot_mt, p.seg_base, nullptr,
-                       seed, sid, oc, os, nullptr, p.nslots);
+    hipLaunchKernelGGL((k_tq<SRC, BSQ_MXFP8, BSQ_SR, true, ROWS>), grid, dim3(kThreads), 0, s, src, in_scales,
+                       in_outer, in_mode, C, in_rows, gather, p.seg_start, p.seg_len, p.slot_seg, p.slot_mt,
+                       p.seg_base, nullptr, seed, sid, oc, os, nullptr, p.nslots, row_out);
   else
-    hipLaunchKernelGGL((k_tq<SRC, BSQ_MXFP8, BSQ_RN, true>), grid, dim3(kThreads), 0, s, src, in_scales, in_outer,
-                       in_mode, C, in_rows, gather, p.seg_start, p.seg_len, p.slot_seg, p.slot_mt, p.seg_base, nullptr,
-                       seed, sid, oc, os, nullptr, p.nslots);
+    hipLaunchKernelGGL((k_tq<SRC, BSQ_MXFP8, BSQ_RN, true, ROWS>), grid, dim3(kThreads), 0, s, src, in_scales,
+                       in_outer, in_mode, C, in_rows, gather, p.seg_start, p.seg_len, p.slot_seg, p.slot_mt,
+                       p.seg_base, nullptr, seed, sid, oc, os, nullptr, p.nslots, row_out);
   return bsqh::launch_status();
 }
 
@@ -559,6 +613,39 @@ extern "C" int bsq_quantize_mxfp8(const void* x, int dtype, int64_t rows, int64_
                                 codes, scales, ws, s);
 }
 
+extern "C" int bsq_quantize_mxfp8_dual(const void* x, int dtype, int64_t rows, int64_t cols,
+                                       const int64_t* seg_offsets, int64_t num_segments, int rnd, uint64_t seed,
+                                       uint64_t stream_rows, uint64_t stream_t, uint8_t* codes, uint8_t* scales,
+                                       uint8_t* codes_t, uint8_t* scales_t, void* ws, size_t ws_bytes,
+                                       bsq_stream_t stream) {
+  BSQ_REQUIRE(dtype == BSQ_F32 || dtype == BSQ_BF16, BSQ_E_DTYPE);
+  BSQ_REQUIRE(rnd == BSQ_RN || rnd == BSQ_SR, BSQ_E_ENUM);
+  BSQ_REQUIRE(rows >= 0 && cols >= 0 && cols % TC == 0, BSQ_E_SHAPE);
+  BSQ_REQUIRE(seg_offsets == nullptr || (num_segments >= 1 && num_segments <= 1024), BSQ_E_SHAPE);
+  if (rows == 0 || cols == 0) return BSQ_OK;
+  BSQ_REQUIRE(x && codes && scales && codes_t && scales_t && ws, BSQ_E_NULL);
+  BSQ_REQUIRE(bsqh::aligned16(x) && bsqh::aligned16(codes) && bsqh::aligned16(codes_t) && bsqh::aligned16(ws),
+              BSQ_E_ALIGN);
+  const int64_t nseg = seg_offsets ? num_segments : 1;
+  BSQ_REQUIRE(ws_bytes >= bsq_quantize_mxfp8_workspace(rows, 1, nseg), BSQ_E_WORKSPACE);
+  hipStream_t s = bsqh::as_stream(stream);
+  const int64_t* seg = seg_offsets;
+  if (!seg) {
+    int64_t* own = reinterpret_cast<int64_t*>(static_cast<char*>(ws) + plan_bytes(rows, 1));
+    hipLaunchKernelGGL(k_one_segment, dim3(1), dim3(64), 0, s, rows, own);
+    seg = own;
+  }
+  RowOut ro;
+  ro.codes = codes;
+  ro.scales = scales;
+  ro.stream_id = stream_rows;
+  if (dtype == BSQ_BF16)
+    return launch_tq_seg<SRC_BF16, true>(x, nullptr, nullptr, 0, cols, nullptr, seg, nseg, rows, rows, rnd, seed,
+                                         stream_t, codes_t, scales_t, ws, s, ro);
+  return launch_tq_seg<SRC_F32, true>(x, nullptr, nullptr, 0, cols, nullptr, seg, nseg, rows, rows, rnd, seed,
+                                      stream_t, codes_t, scales_t, ws, s, ro);
+}
+
 extern "C" size_t bsq_requant_workspace(int64_t batch, int64_t rows, int64_t num_segments, int out_fmt, int gather) {
   if (gather) return plan_bytes(rows, num_segments > 0 ? num_segments : 1);
   if (out_fmt == BSQ_NVFP4 && batch > 0) return (size_t)((batch * 4 + 255) / 256 * 256);
@@ -601,11 +688,11 @@ extern "C" int bsq_requant_transpose_sr(const uint8_t* codes, const uint8_t* sca
     if (rnd == BSQ_SR)
       hipLaunchKernelGGL((k_tq<SRC_NVFP4, BSQ_MXFP8, BSQ_SR, false>), grid, dim3(kThreads), 0, s, codes, scales, outer,
                          in_mode, cols, rows, nullptr, nullptr, nullptr, nullptr, nullptr, nullptr, nullptr, seed, stream_id,
-                         out_codes, out_scales, nullptr, ntiles);
+                         out_codes, out_scales, nullptr, ntiles, RowOut{});
     else
       hipLaunchKernelGGL((k_tq<SRC_NVFP4, BSQ_MXFP8, BSQ_RN, false>), grid, dim3(kThreads), 0, s, codes, scales, outer,
                          in_mode, cols, rows, nullptr, nullptr, nullptr, nullptr, nullptr, nullptr, nullptr, seed, stream_id,
-                         out_codes, out_scales, nullptr, ntiles);
+                         out_codes, out_scales, nullptr, ntiles, RowOut{});
     return bsqh::launch_status();
   }
   BSQ_REQUIRE(out_outer && ws, BSQ_E_NULL);
@@ -619,11 +706,11 @@ extern "C" int bsq_requant_transpose_sr(const uint8_t* codes, const uint8_t* sca
   if (rnd == BSQ_SR)
     hipLaunchKernelGGL((k_tq<SRC_NVFP4, BSQ_NVFP4, BSQ_SR, false>), grid, dim3(kThreads), 0, s, codes, scales, outer,
                        in_mode, cols, rows, nullptr, nullptr, nullptr, nullptr, nullptr, nullptr, amax, seed, stream_id,
-                       out_codes, out_scales, out_outer, ntiles);
+                       out_codes, out_scales, out_outer, ntiles, RowOut{});
   else
     hipLaunchKernelGGL((k_tq<SRC_NVFP4, BSQ_NVFP4, BSQ_RN, false>), grid, dim3(kThreads), 0, s, codes, scales, outer,
                        in_mode, cols, rows, nullptr, nullptr, nullptr, nullptr, nullptr, nullptr, amax, seed, stream_id,
-                       out_codes, out_scales, out_outer, ntiles);
+                       out_codes, out_scales, out_outer, ntiles, RowOut{});
   return bsqh::launch_status();
 }
 

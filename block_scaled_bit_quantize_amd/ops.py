@@ -159,6 +159,32 @@ def quantize_mxfp8(x, rnd="sr", seed=0, stream_id=0, transpose=False, seg_offset
     return codes, scales
 
 
+def quantize_mxfp8_dual(x, rnd="sr", seed=0, stream_rows=0, stream_t=0, seg_offsets=None, out_elems=None):
+    """Both MXFP8 quantizations of x [R, C] from one read: ((codes [R, C],
+    scales [R, C/32]) as quantize_mxfp8(transpose=False, stream_id=stream_rows),
+    (codes_t, scales_t) as quantize_mxfp8(transpose=True, stream_id=stream_t))."""
+    lib = load_library()
+    _dev(x, seg_offsets)
+    R, C = x.shape
+    dt = {torch.float32: F32, torch.bfloat16: BF16}.get(x.dtype)
+    if dt is None:
+        raise BsqError("x must be float32 or bfloat16")
+    r = _enum(rnd, _RND)
+    nseg = seg_offsets.numel() - 1 if seg_offsets is not None else 1
+    n = out_elems if out_elems is not None else _segmented_capacity(R, nseg, C)
+    codes = torch.empty((R, C), dtype=torch.uint8, device=x.device)
+    scales = torch.empty((R, C // 32), dtype=torch.uint8, device=x.device)
+    codes_t = torch.empty((n,), dtype=torch.uint8, device=x.device)
+    scales_t = torch.empty((n // 32,), dtype=torch.uint8, device=x.device)
+    wsb = lib.bsq_quantize_mxfp8_workspace(R, 1, nseg)
+    ws = _ws(wsb, x.device)
+    check(lib.bsq_quantize_mxfp8_dual(x.data_ptr(), dt, R, C, _ptr(seg_offsets),
+                                      nseg if seg_offsets is not None else 0, r, seed, stream_rows, stream_t,
+                                      codes.data_ptr(), scales.data_ptr(), codes_t.data_ptr(), scales_t.data_ptr(),
+                                      ws.data_ptr(), wsb, _stream()), "bsq_quantize_mxfp8_dual")
+    return (codes, scales), (codes_t, scales_t)
+
+
 def requant_transpose_sr(codes, scales, outer, in_mode, out_fmt="mxfp8", seed=0, stream_id=0, rnd="sr",
                          row_gather=None, seg_offsets=None, out_elems=None):
     """Dequantize -> transpose -> requantize.

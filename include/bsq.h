@@ -204,6 +204,24 @@ int bsq_quantize_mxfp8(const void* x, int dtype, int64_t rows, int64_t cols, int
                        uint64_t stream_id, uint8_t* codes, uint8_t* scales, void* ws,
                        size_t ws_bytes, bsq_stream_t stream);
 
+/* Both MXFP8 quantizations of the gradient from one read of x (the quantized
+ * linear layer figure quantizes the BF16 output gradient row-wise for DGRAD
+ * and transposed for WGRAD; both consume the same gradient).
+ * Outputs are those of bsq_quantize_mxfp8 with transpose = 0 (codes, scales;
+ * random stream stream_rows) and with transpose = 1 (codes_t, scales_t;
+ * stream_t, the padded per-segment transposed layout), bit for bit, for every
+ * row inside a segment (all rows when seg_offsets[0] == 0 and the last offset
+ * == rows, or seg_offsets == NULL). Rows outside every segment (only with
+ * offsets that do not cover [0, rows)) are not written in codes/scales.
+ * cols % 64 == 0; workspace bsq_quantize_mxfp8_workspace(rows, 1, num_segments);
+ * x, codes, codes_t, ws 16-byte aligned. Errors: NULL, SHAPE, ALIGN, DTYPE,
+ * ENUM, WORKSPACE, LAUNCH. */
+int bsq_quantize_mxfp8_dual(const void* x, int dtype, int64_t rows, int64_t cols,
+                            const int64_t* seg_offsets, int64_t num_segments, int rnd, uint64_t seed,
+                            uint64_t stream_rows, uint64_t stream_t, uint8_t* codes, uint8_t* scales,
+                            uint8_t* codes_t, uint8_t* scales_t, void* ws, size_t ws_bytes,
+                            bsq_stream_t stream);
+
 /* ------------------------------------------------------------------------
  * Dequantize -> transpose -> requantize with stochastic rounding ("Re-
  * quantization with stochastic rounding"; E[w_q] = E[(w_q^T)^T]).

@@ -144,6 +144,19 @@ def test_quantize_mxfp8_validation(lib):
     assert q(FAKE, 1, 4, 64, 1, None, 0, 1, 0, 0, FAKE, FAKE, None, 0, None) == E_NULL
     assert q(FAKE, 1, 4, 64, 1, None, 0, 1, 0, 0, FAKE, FAKE, FAKE, 8, None) == E_WORKSPACE
     assert q(FAKE, 1, 4, 64, 0, None, 0, 1, 0, 0, FAKE + 4, FAKE, None, 0, None) == E_ALIGN
+    d = lib.bsq_quantize_mxfp8_dual  # x, dtype, rows, cols, seg, nseg, rnd, seed, s_rows, s_t, c, s, c_t, s_t, ws, wsb
+    ok = [FAKE, 1, 4, 64, None, 0, 1, 0, 1, 2, FAKE, FAKE, FAKE, FAKE, FAKE, 1 << 20, None]
+    def dcall(i, v):
+        a = list(ok); a[i] = v; return d(*a)
+    assert dcall(3, 96) == E_SHAPE            # cols % 64
+    assert dcall(4, FAKE) == E_SHAPE          # seg_offsets with 0 segments
+    assert dcall(6, 5) == E_ENUM
+    assert dcall(1, 3) == E_DTYPE
+    assert dcall(12, None) == E_NULL          # codes_t
+    assert dcall(10, None) == E_NULL          # row codes
+    assert dcall(10, FAKE + 4) == E_ALIGN
+    assert dcall(15, 8) == E_WORKSPACE
+    assert dcall(2, 0) == OK                  # empty
 
 
 def test_requant_validation(lib):

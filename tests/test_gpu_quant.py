@@ -212,6 +212,69 @@ def test_quantize_mxfp8_transposed_small(dtype, rnd):
     assert np.array_equal(h(gc), oc) and np.array_equal(h(gs), os_)
 
 
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+@pytest.mark.parametrize("rnd", ["rn", "sr"])
+def test_quantize_mxfp8_dual_small(dtype, rnd):
+    """Both MXFP8 quantizations from one read equal the oracle's row-wise
+    (stream 1) and per-segment transposed (stream 2) results bit for bit."""
+    log(f"quantize_mxfp8 dual {dtype} {rnd}")
+    rng = np.random.default_rng(9)
+    seg = np.array([0, 0, 45, 245, 245, 374, 375, 631], dtype=np.int64)      # empty, ragged, 1-row segments
+    x = _data(rng, (631, 192), "zeros_mix")
+    if dtype == "bf16":
+        bits = synth.bf16_bits(x)
+        x = synth.bf16_to_f32(bits).reshape(x.shape)
+        xd = bf16_t(bits.reshape(x.shape))
+    else:
+        xd = t(x)
+    r = Q.RN if rnd == "rn" else Q.SR
+    _, n = bsq.padded_segment_layout(seg, 192)
+    (gc, gs), (tc, ts) = bsq.quantize_mxfp8_dual(xd, rnd, seed=5, stream_rows=1, stream_t=2, seg_offsets=t(seg),
+                                                 out_elems=n)
+    oc, os_ = Q.quantize_mxfp8(x, r, 5, 1)
+    assert np.array_equal(h(gc), oc) and np.array_equal(h(gs), os_)
+    oc, os_ = Q.quantize_mxfp8_transposed(x, seg, r, 5, 2)
+    assert np.array_equal(h(tc), oc) and np.array_equal(h(ts), os_)
+    _, n1 = bsq.padded_segment_layout([0, 631], 192)   # no segment table: one segment of all rows
+    (gc, gs), (tc, ts) = bsq.quantize_mxfp8_dual(xd, rnd, seed=5, stream_rows=1, stream_t=2, out_elems=n1)
+    oc, os_ = Q.quantize_mxfp8(x, r, 5, 1)
+    assert np.array_equal(h(gc), oc) and np.array_equal(h(gs), os_)
+    oc, os_ = Q.quantize_mxfp8_transposed(x, [0, 631], r, 5, 2)
+    assert np.array_equal(h(tc), oc) and np.array_equal(h(ts), os_)
+
+
+def test_quantize_mxfp8_dual_uncovered_rows():
+    """Offsets [-10, 100, 50, 200] over 256 rows read as [0, 100, 100, 200]:
+    rows 0..199 get the row-wise codes and scales, rows 200..255 (in no
+    segment) keep their contents, and the transposed output is the oracle's
+    on the normalized table."""
+    log("quantize_mxfp8 dual uncovered rows")
+    rng = np.random.default_rng(12)
+    R, C = 256, 64
+    x = _data(rng, (R, C), "normal")
+    seg = np.array([-10, 100, 50, 200], np.int64)
+    norm = np.maximum.accumulate(np.clip(seg, 0, R))
+    lib = _lib.load_library()
+    codes = torch.full((R, C), 0xA5, dtype=torch.uint8, device=DEV)
+    scales = torch.full((R, C // 32), 0xA5, dtype=torch.uint8, device=DEV)
+    cap = C * (R + 31 * 3)
+    codes_t = torch.full((cap,), 0xA5, dtype=torch.uint8, device=DEV)
+    scales_t = torch.full((cap // 32,), 0xA5, dtype=torch.uint8, device=DEV)
+    wsb = lib.bsq_quantize_mxfp8_workspace(R, 1, 3)
+    ws = torch.zeros(max(wsb, 1), dtype=torch.uint8, device=DEV)
+    xd, segd = t(x), t(seg)
+    st = lib.bsq_quantize_mxfp8_dual(xd.data_ptr(), 0, R, C, segd.data_ptr(), 3, 1, 5, 1, 2, codes.data_ptr(),
+                                     scales.data_ptr(), codes_t.data_ptr(), scales_t.data_ptr(), ws.data_ptr(), wsb,
+                                     None)
+    assert st == 0
+    oc, os_ = Q.quantize_mxfp8(x, Q.SR, 5, 1)
+    gc, gs = h(codes), h(scales)
+    assert np.array_equal(gc[:200], oc[:200]) and np.array_equal(gs[:200], os_[:200])
+    assert np.all(gc[200:] == 0xA5) and np.all(gs[200:] == 0xA5)
+    tc_o, ts_o = Q.quantize_mxfp8_transposed(x, norm, Q.SR, 5, 2)
+    assert np.array_equal(h(codes_t)[:tc_o.size], tc_o) and np.array_equal(h(scales_t)[:ts_o.size], ts_o)
+
+
 @pytest.mark.parametrize("seg", [[0, 256, 0, 256], [-10, 100, 50, 400], [0, 300, 200, 100, 256]])
 def test_segmented_malformed_offsets_stay_in_bounds(seg):
     """Decreasing or out-of-range offsets are read as clamped to [0, rows]
@@ -565,24 +628,28 @@ def test_workload4_full_gradient_and_activation_requant(wl2):
     gd = bf16_t(g)
     log("quantize_mxfp8 rows workload4")
     gc, gs = bsq.quantize_mxfp8(gd, "sr", seed=42, stream_id=1)
+    mp, n = bsq.padded_segment_layout(seg, Cg)
+    (dc, ds), (dtc, dts) = bsq.quantize_mxfp8_dual(gd, "sr", seed=42, stream_rows=1, stream_t=2, seg_offsets=t(seg),
+                                                   out_elems=n)
     rows = np.unique(np.r_[0, 3, 65535, 131071, np.random.default_rng(22).choice(M, 60, replace=False)])
     gf = synth.bf16_to_f32(g[rows])
     idx = (rows[:, None].astype(np.uint64) * np.uint64(Cg) + np.arange(Cg, dtype=np.uint64)[None, :])
     oc, os_ = Q.mxfp8_quantize(gf, idx, Q.SR, 42, 1)
     assert np.array_equal(h(gc[rows]), oc) and np.array_equal(h(gs[rows]), os_)
-    del gc, gs
+    assert np.array_equal(h(dc[rows]), oc) and np.array_equal(h(ds[rows]), os_)   # the one-read variant
+    del gc, gs, dc, ds
     log("quantize_mxfp8 transposed workload4")
-    mp, n = bsq.padded_segment_layout(seg, Cg)
     tc, ts = bsq.quantize_mxfp8(gd, "sr", seed=42, stream_id=2, transpose=True, seg_offsets=t(seg), out_elems=n)
-    tc, ts = h(tc), h(ts)
+    tc, ts, dtc, dts = h(tc), h(ts), h(dtc), h(dts)
     _, base = Q.segmented_layout(seg, Cg)
     sel = [0, 11, 25, 40, 52, 63]
     gf = synth.bf16_to_f32(g).reshape(M, Cg)
     for e in sel:
         oc, os_ = Q.quantize_mxfp8_transposed(gf, seg, Q.SR, 42, 2, segments=[e])
-        assert np.array_equal(tc[base[e]:base[e] + Cg * mp[e]], oc)
-        assert np.array_equal(ts[base[e] // 32:(base[e] + Cg * mp[e]) // 32], os_)
-    del tc, ts, gd, gf
+        for c_, s_ in ((tc, ts), (dtc, dts)):
+            assert np.array_equal(c_[base[e]:base[e] + Cg * mp[e]], oc)
+            assert np.array_equal(s_[base[e] // 32:(base[e] + Cg * mp[e]) // 32], os_)
+    del tc, ts, dtc, dts, gd, gf
     log("requant x_q^T gather workload4")
     T, Kx = 16384, 4096
     rng = np.random.default_rng(4)
