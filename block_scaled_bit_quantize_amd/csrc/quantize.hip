@@ -314,12 +314,17 @@ __global__ __launch_bounds__(kThreads) void k_quant_nvfp4(
 // Per-item outer scale in one pass over HBM. Each group of the grid (one
 // workgroup per CU, at most kOnePassMaxWg; with two groups two workgroups
 // share a CU, so one group's loads overlap the other's wait and stores) walks
-// its items (every groups-th item) in order. Every
-// workgroup loads its share of item e into registers (at most BPT blocks of
-// 16 per thread), publishes its maximum in its own slot slot[e][w] (bit
-// pattern with bit 31 set as the arrival mark: magnitudes have it clear),
-// loads its share of item e + 1, then waits until every slot of item e is
-// marked and quantizes item e from registers with the maximum of the slots.
+// its items (every groups-th item) in order. Every workgroup loads its share
+// of item e into registers (at most BPT blocks of 16 per thread) and
+// publishes its maximum in its own slot slot[e][w] (bit pattern with bit 31
+// set as the arrival mark: magnitudes have it clear). It then starts the loads
+// of its share of item e + 1 and, while they are in flight, waits until every
+// slot of item e is marked (the maximum of the slots is item e's maximum),
+// publishes item e + 1's maximum once its loads have arrived, and then
+// quantizes item e from registers. One wave polls the slots; the others wait
+// at a barrier that waits for LDS operations only, so their loads stay in
+// flight (a plain __syncthreads would wait for every outstanding load and
+// store).
 // The wait is bounded: after spin_limit polls the workgroup reduces the whole
 // item itself (the same maximum, from a second read), so every wave always
 // finishes. The slots start at zero. Slot accesses are relaxed device-scope
@@ -341,7 +346,27 @@ inline uint32_t wait_polls() {
   return v ? (uint32_t)strtoul(v, nullptr, 10) : kSpinLimit;
 }
 
-template <typename T, int BPT>
+// Workgroup barrier that completes this wave's LDS operations first and
+// leaves its global loads and stores in flight.
+__device__ __forceinline__ void lds_barrier() { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory"); }
+
+// f(integral_constant<int, 0>), ..., f(integral_constant<int, N - 1>), in order.
+template <typename F, int... I>
+__device__ __forceinline__ void static_for_impl(F& f, std::integer_sequence<int, I...>) {
+  (f(std::integral_constant<int, I>{}), ...);
+}
+template <int N, typename F>
+__device__ __forceinline__ void static_for(F&& f) {
+  static_for_impl(f, std::make_integer_sequence<int, N>{});
+}
+
+// Lambdas of the kernel below are inlined whatever their size: a call would
+// put the register sets on the stack.
+#define BSQ_AI __attribute__((always_inline))
+
+// S register sets of BPT blocks per thread: up to S - 1 items in flight
+// besides the one being waited for.
+template <typename T, int BPT, int S>
 __global__ __launch_bounds__(kOnePassThreads) void k_quant_nvfp4_items(
     const T* __restrict__ x, int64_t B, int64_t bpi, int groups, uint32_t* __restrict__ slot,
     uint8_t* __restrict__ codes, uint8_t* __restrict__ scales, float* __restrict__ outer_out, uint32_t spin_limit) {
@@ -354,85 +379,143 @@ __global__ __launch_bounds__(kOnePassThreads) void k_quant_nvfp4_items(
   const int64_t hi = lo + share < bpi ? lo + share : bpi;
   const int t = threadIdx.x;
   __shared__ float red[kOnePassThreads / 64];
-  auto wg_max = [&](float m) -> float {  // every thread calls it; result in every thread
+  __shared__ float slots_max;  // item maximum found by the polling wave; -1: polls ran out
+  auto wg_max = [&](float m) BSQ_AI -> float {  // every thread calls it; result in every thread
     m = wave_max(m);
     if ((t & 63) == 0) red[t >> 6] = m;
-    __syncthreads();
+    lds_barrier();
     float r = red[0];
 #pragma unroll
     for (int w = 1; w < kOnePassThreads / 64; ++w) r = fmaxf(r, red[w]);
-    __syncthreads();
+    lds_barrier();
     return r;
   };
-  Blk16<T> blk[2][BPT];
-  float am[2][BPT];
-  auto load = [&](int b, int64_t e) -> float {  // share of item e into set b; returns the thread's maximum
+  static_assert(S >= 2, "one item in flight at least");
+  Blk16<T> blk[S][BPT];
+  // The thread's first block of a share, from a copy of the thread index the
+  // compiler cannot see through: per-block addresses are then recomputed
+  // where they are used instead of being held in registers for every set.
+  auto first = [&]() BSQ_AI -> int64_t {
+    int tr = t;
+    asm volatile("" : "+v"(tr));
+    return lo + tr;
+  };
+  // Loads and maxima are branch-free (a thread's blocks past its share load a
+  // valid block of the item and count as zero), so the compiler's wait for a
+  // set's loads is exact and never also waits for the other sets' loads.
+  auto issue = [&](int b, int64_t e) BSQ_AI {  // start the loads of item e's share into set b
+    const int64_t j0 = first();
+#pragma unroll
+    for (int k = 0; k < BPT; ++k) {
+      const int64_t j = j0 + (int64_t)k * kOnePassThreads;
+      blk[b][k].load(x + (e * bpi + (j < bpi ? j : bpi - 1)) * 16);
+    }
+  };
+  auto thread_max = [&](int b) BSQ_AI -> float {  // largest block maximum of set b (waits for its loads)
+    const int64_t j0 = first();
     float m = 0.0f;
 #pragma unroll
     for (int k = 0; k < BPT; ++k) {
-      const int64_t j = lo + t + (int64_t)k * kOnePassThreads;
-      am[b][k] = 0.0f;
-      if (j < hi) {
-        blk[b][k].load(x + (e * bpi + j) * 16);
-        am[b][k] = blk[b][k].absmax();
-        m = fmaxf(m, am[b][k]);
-      }
+      const float a = blk[b][k].absmax();
+      m = fmaxf(m, j0 + (int64_t)k * kOnePassThreads < hi ? a : 0.0f);
     }
     return m;
   };
-  auto publish = [&](int64_t e, float m) {
+  auto publish = [&](int64_t e, float m) BSQ_AI {
     const float r = wg_max(m);
     if (t == 0) __hip_atomic_store(slot + e * nwg + wid, __float_as_uint(r) | 0x80000000u, __ATOMIC_RELAXED,
                                    __HIP_MEMORY_SCOPE_AGENT);
   };
-  auto item = [&](int b, int64_t e) {
-    // wait for every workgroup's maximum of item e (thread w polls slot w)
-    float mx = 0.0f;
-    uint32_t spins = 0;
-    for (;;) {
-      uint32_t v = 0x80000000u;
-      if (t < nwg) v = __hip_atomic_load(slot + e * nwg + t, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-      if (!__syncthreads_or((v & 0x80000000u) == 0)) {
-        mx = __uint_as_float(v & 0x7FFFFFFFu);
-        break;
-      }
-      if (++spins >= spin_limit) {  // uniform: reduce the whole item here
-        for (int64_t j = t; j < bpi; j += kOnePassThreads) {
-          Blk16<T> q;
-          q.load(x + (e * bpi + j) * 16);
-          mx = fmaxf(mx, q.absmax());
+  auto outer_scale = [&](int64_t e) BSQ_AI -> float {
+    if (t < 64) {  // wave 0: lane l polls slots l, l + 64, ... (nwg <= 512) until all are marked
+      float mx = -1.0f;
+      for (uint32_t spins = 0; spins < spin_limit; ++spins) {
+        // all eight loads are issued before the first is waited for (lanes
+        // past the last slot re-read it), so a poll costs one round trip
+        uint32_t v[kOnePassMaxWg / 64];
+#pragma unroll
+        for (int q = 0; q < kOnePassMaxWg / 64; ++q) {
+          const int w = t + 64 * q;
+          v[q] = __hip_atomic_load(slot + e * nwg + (w < nwg ? w : nwg - 1), __ATOMIC_RELAXED,
+                                   __HIP_MEMORY_SCOPE_AGENT);
         }
-        break;
+        bool all = true;
+        float m = 0.0f;
+#pragma unroll
+        for (int q = 0; q < kOnePassMaxWg / 64; ++q) {
+          all = all && (v[q] & 0x80000000u) != 0;
+          m = fmaxf(m, __uint_as_float(v[q] & 0x7FFFFFFFu));
+        }
+        if (__all(all)) {  // wave-uniform
+          mx = wave_max(m);
+          break;
+        }
+        __builtin_amdgcn_s_sleep(1);
       }
-      __builtin_amdgcn_s_sleep(1);
+      if (t == 0) slots_max = mx;
     }
-    const float a = wg_max(mx);
-    const float st = a > 0.0f ? a / 2688.0f : 1.0f;
+    lds_barrier();
+    float a = slots_max;
+    if (a < 0.0f) {  // uniform: the polls ran out; reduce the whole item here
+      float m = 0.0f;
+      for (int64_t j = t; j < bpi; j += kOnePassThreads) {
+        Blk16<T> q;
+        q.load(x + (e * bpi + j) * 16);
+        m = fmaxf(m, q.absmax());
+      }
+      a = wg_max(m);
+    }
+    // slots_max is written again only in the next item's wait, after the
+    // barriers of the publish in between
+    return a > 0.0f ? a / 2688.0f : 1.0f;
+  };
+  auto quantize = [&](int b, int64_t e, float st) BSQ_AI {
     if (wid == 0 && t == 0) outer_out[e] = st;
+    const int64_t j0 = first();
 #pragma unroll
     for (int k = 0; k < BPT; ++k) {
-      const int64_t j = lo + t + (int64_t)k * kOnePassThreads;
-      if (j < hi) nvfp4_block<false>(blk[b][k], am[b][k], st, codes + (e * bpi + j) * 8, scales + e * bpi + j);
+      const int64_t j = j0 + (int64_t)k * kOnePassThreads;
+      if (j < hi) nvfp4_block<false>(blk[b][k], blk[b][k].absmax(), st, codes + (e * bpi + j) * 8, scales + e * bpi + j);
     }
   };
   const int64_t n = grp < B ? (B - grp + groups - 1) / groups : 0;  // this group's items
   if (n <= 0) return;
-  auto it = [&](int64_t i) -> int64_t { return grp + i * groups; };
-  publish(it(0), load(0, it(0)));
-  int64_t i = 0;
-  for (; i + 1 < n; i += 2) {  // register sets alternate: item i in set 0, i + 1 in set 1
-    const float m1 = load(1, it(i + 1));
-    item(0, it(i));
-    publish(it(i + 1), m1);
-    if (i + 2 < n) {
-      const float m2 = load(0, it(i + 2));
-      item(1, it(i + 1));
-      publish(it(i + 2), m2);
+  auto it = [&](int64_t i) BSQ_AI -> int64_t { return grp + i * groups; };
+  // Item i lives in register set i % S. Step i starts the loads of item
+  // i + S - 1 (into the set item i - 1 has left) and publishes item i + P,
+  // then quantizes item i once its wait is over. With three sets or more the
+  // publish (of item i + S - 2, whose loads are the second youngest in
+  // flight) comes before the wait for item i; with two it comes after it (P =
+  // 1: item i + 1's loads are the youngest). In the main loop every step
+  // issues and publishes unconditionally, so the wait the compiler places for
+  // one set's loads leaves the younger sets' loads in flight; the last
+  // 2S - 2 steps check the item count.
+  constexpr int P = S == 2 ? 1 : S - 2;
+  auto step = [&](auto set, int64_t i, auto tail) BSQ_AI {
+    constexpr int sc = decltype(set)::value;
+    constexpr bool tl = decltype(tail)::value;
+    if (!tl || i + S - 1 < n) issue((sc + S - 1) % S, it(i + S - 1));
+    if constexpr (S == 2) {
+      const float st = outer_scale(it(i));
+      if (!tl || i + P < n) publish(it(i + P), thread_max((sc + P) % S));
+      quantize(sc, it(i), st);
     } else {
-      item(1, it(i + 1));
+      if (!tl || i + P < n) publish(it(i + P), thread_max((sc + P) % S));
+      quantize(sc, it(i), outer_scale(it(i)));
     }
-  }
-  if (i < n && (n & 1)) item(0, it(i));
+  };
+  // prologue: loads of items 0 .. S - 2, maxima of items 0 .. P - 1
+  static_for<S - 1>([&](auto j) BSQ_AI {
+    if (j < n) issue(j, it(j));
+  });
+  static_for<P>([&](auto j) BSQ_AI {
+    if (j < n) publish(it(j), thread_max(j));
+  });
+  int64_t i = 0;
+  for (; i + 2 * S - 2 < n; i += S) static_for<S>([&](auto j) BSQ_AI { step(j, i + j, std::false_type{}); });
+  static_for<2 * S - 2>([&](auto j) BSQ_AI {
+    if (i + j < n) step(std::integral_constant<int, j % S>{}, i + j, std::true_type{});
+  });
 }
 
 // Row-wise MXFP8: one thread per block of 32 (element index = blk*32 + i).
@@ -496,6 +579,25 @@ int launch_quant(const T* x, int64_t row0, int64_t row_end, int64_t R, int64_t C
   return bsqh::launch_status();
 }
 
+// One launch of the one-pass kernel (BPT blocks per thread, S register
+// sets), the items split between two groups of workgroups when two of its
+// workgroups fit on a CU at once (else one group: a second group would only
+// start when the first had finished).
+template <typename T, int BPT, int S>
+void launch_items(const T* x, int64_t B, int64_t bpi, int64_t nwg, uint32_t* ws, uint8_t* codes, uint8_t* scales,
+                  float* outer_out, hipStream_t s) {
+  static const int per_cu = [] {
+    int nb = 0;
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&nb, reinterpret_cast<const void*>(&k_quant_nvfp4_items<T, BPT, S>),
+                                                     kOnePassThreads, 0) != hipSuccess)
+      nb = 1;
+    return nb;
+  }();
+  const int grp = per_cu >= 2 ? kOnePassGroups : 1;
+  hipLaunchKernelGGL((k_quant_nvfp4_items<T, BPT, S>), dim3((unsigned)(nwg * grp)), dim3(kOnePassThreads), 0, s, x, B,
+                     bpi, grp, ws, codes, scales, outer_out, wait_polls());
+}
+
 template <typename T>
 int quantize_nvfp4_t(const T* x, int64_t B, int64_t R, int64_t C, int mode, bool fs, const float* outer_in,
                      uint8_t* codes, uint8_t* scales, float* outer_out, uint32_t* ws, hipStream_t s) {
@@ -514,18 +616,19 @@ int quantize_nvfp4_t(const T* x, int64_t B, int64_t R, int64_t C, int mode, bool
   // (a float share of 8 blocks per thread would not fit in registers)
   if (!fs && one_pass_items(B, R, C) && per_thread <= (sizeof(T) == 2 ? 8 : 4)) {
     hipLaunchKernelGGL(k_fill_u32, dim3(grid1(B * nwg)), dim3(kThreads), 0, s, ws, 0u, B * nwg);
-    // two groups when two workgroups fit on a CU (at most 128 VGPRs: bf16 BPT <= 4, float BPT <= 2)
-#define BSQ_OP(BPT)                                                                                               \
-  do {                                                                                                            \
-    const int grp = BPT * sizeof(T) <= 8 ? kOnePassGroups : 1;                                                    \
-    hipLaunchKernelGGL((k_quant_nvfp4_items<T, BPT>), dim3((unsigned)(nwg * grp)), dim3(kOnePassThreads), 0, s, x, B, \
-                       bpi, grp, ws, codes, scales, outer_out, wait_polls());                                     \
-  } while (0)
-    if (per_thread <= 1) BSQ_OP(1);
-    else if (per_thread <= 2) BSQ_OP(2);
-    else if (per_thread <= 4) BSQ_OP(4);
-    else if constexpr (sizeof(T) == 2) BSQ_OP(8);
-#undef BSQ_OP
+    // three register sets where they fit in registers, two for the largest shares
+    if (per_thread <= 1) launch_items<T, 1, 3>(x, B, bpi, nwg, ws, codes, scales, outer_out, s);
+    else if (per_thread <= 2) launch_items<T, 2, 3>(x, B, bpi, nwg, ws, codes, scales, outer_out, s);
+    else if constexpr (sizeof(T) == 2) {
+      if (per_thread <= 3) launch_items<T, 3, 3>(x, B, bpi, nwg, ws, codes, scales, outer_out, s);
+      else if (per_thread <= 4) launch_items<T, 4, 3>(x, B, bpi, nwg, ws, codes, scales, outer_out, s);
+      else if (per_thread <= 5) launch_items<T, 5, 3>(x, B, bpi, nwg, ws, codes, scales, outer_out, s);
+      else if (per_thread <= 6) launch_items<T, 6, 3>(x, B, bpi, nwg, ws, codes, scales, outer_out, s);
+      else if (per_thread <= 7) launch_items<T, 7, 3>(x, B, bpi, nwg, ws, codes, scales, outer_out, s);
+      else launch_items<T, 8, 2>(x, B, bpi, nwg, ws, codes, scales, outer_out, s);
+    } else {
+      launch_items<T, 4, 2>(x, B, bpi, nwg, ws, codes, scales, outer_out, s);
+    }
     return bsqh::launch_status();
   }
   hipLaunchKernelGGL(k_fill_u32, dim3(grid1(B)), dim3(kThreads), 0, s, ws, 0u, B);
