@@ -350,6 +350,44 @@ inline uint32_t wait_polls() {
 // leaves its global loads and stores in flight.
 __device__ __forceinline__ void lds_barrier() { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory"); }
 
+// Every thread calls it. Wave 0 polls the nwg (<= kOnePassMaxWg) slots of one
+// item until all carry the arrival mark, then leaves their maximum in *out
+// (LDS; -1 when spin_limit polls found a slot unmarked); the other waves wait
+// at an LDS-only barrier with their loads in flight. Returns *out. A caller
+// writes *out again only after another barrier.
+__device__ __forceinline__ float poll_slots(const uint32_t* __restrict__ row, int nwg, uint32_t spin_limit,
+                                            float* out) {
+  const int t = threadIdx.x;
+  if (t < 64) {  // lane l polls slots l, l + 64, ...
+    float mx = -1.0f;
+    for (uint32_t spins = 0; spins < spin_limit; ++spins) {
+      // all loads are issued before the first is waited for (lanes past the
+      // last slot re-read it), so a poll costs one round trip
+      uint32_t v[kOnePassMaxWg / 64];
+#pragma unroll
+      for (int q = 0; q < kOnePassMaxWg / 64; ++q) {
+        const int w = t + 64 * q;
+        v[q] = __hip_atomic_load(row + (w < nwg ? w : nwg - 1), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      }
+      bool all = true;
+      float m = 0.0f;
+#pragma unroll
+      for (int q = 0; q < kOnePassMaxWg / 64; ++q) {
+        all = all && (v[q] & 0x80000000u) != 0;
+        m = fmaxf(m, __uint_as_float(v[q] & 0x7FFFFFFFu));
+      }
+      if (__all(all)) {  // wave-uniform
+        mx = wave_max(m);
+        break;
+      }
+      __builtin_amdgcn_s_sleep(1);
+    }
+    if (t == 0) *out = mx;
+  }
+  lds_barrier();
+  return *out;
+}
+
 // f(integral_constant<int, 0>), ..., f(integral_constant<int, N - 1>), in order.
 template <typename F, int... I>
 __device__ __forceinline__ void static_for_impl(F& f, std::integer_sequence<int, I...>) {
@@ -360,9 +398,54 @@ __device__ __forceinline__ void static_for(F&& f) {
   static_for_impl(f, std::make_integer_sequence<int, N>{});
 }
 
-// Lambdas of the kernel below are inlined whatever their size: a call would
-// put the register sets on the stack.
+// Lambdas of the one-pass kernels are inlined whatever their size: a call
+// would put the register sets on the stack.
 #define BSQ_AI __attribute__((always_inline))
+
+// The item loop of the one-pass kernels, with S register sets: issue(set, i)
+// starts the loads of the workgroup's share of (group-local) item i into a
+// set, publish(set, i) reduces and publishes the share's maximum (waiting for
+// that set's loads), wait(i) returns item i's outer scale once every
+// workgroup has published it, quant(set, i, st) writes item i's codes. Item i
+// lives in set i % S. Step i starts the loads of item i + S - 1 (into the set
+// item i - 1 has left) and publishes item i + P, then quantizes item i once
+// its wait is over. With three sets or more the publish (of item i + S - 2,
+// whose loads are the second youngest in flight) comes before the wait for
+// item i; with two it comes after it (P = 1: item i + 1's loads are the
+// youngest). In the main loop every step issues and publishes
+// unconditionally, so the wait the compiler places for one set's loads leaves
+// the younger sets' loads in flight; the last 2S - 2 steps check the count.
+template <int S, typename Issue, typename Publish, typename Wait, typename Quant>
+__device__ __forceinline__ void item_pipeline(int64_t n, Issue&& issue, Publish&& publish, Wait&& wait,
+                                              Quant&& quant) {
+  static_assert(S >= 2, "one item in flight at least");
+  constexpr int P = S == 2 ? 1 : S - 2;
+  auto step = [&](auto set, int64_t i, auto tail) BSQ_AI {
+    constexpr int sc = decltype(set)::value;
+    constexpr bool tl = decltype(tail)::value;
+    if (!tl || i + S - 1 < n) issue((sc + S - 1) % S, i + S - 1);
+    if constexpr (S == 2) {
+      const float st = wait(i);
+      if (!tl || i + P < n) publish((sc + P) % S, i + P);
+      quant(sc, i, st);
+    } else {
+      if (!tl || i + P < n) publish((sc + P) % S, i + P);
+      quant(sc, i, wait(i));
+    }
+  };
+  // prologue: loads of items 0 .. S - 2, maxima of items 0 .. P - 1
+  static_for<S - 1>([&](auto j) BSQ_AI {
+    if (j < n) issue(j, j);
+  });
+  static_for<P>([&](auto j) BSQ_AI {
+    if (j < n) publish(j, j);
+  });
+  int64_t i = 0;
+  for (; i + 2 * S - 2 < n; i += S) static_for<S>([&](auto j) BSQ_AI { step(j, i + j, std::false_type{}); });
+  static_for<2 * S - 2>([&](auto j) BSQ_AI {
+    if (i + j < n) step(std::integral_constant<int, j % S>{}, i + j, std::true_type{});
+  });
+}
 
 // S register sets of BPT blocks per thread: up to S - 1 items in flight
 // besides the one being waited for.
@@ -390,7 +473,6 @@ __global__ __launch_bounds__(kOnePassThreads) void k_quant_nvfp4_items(
     lds_barrier();
     return r;
   };
-  static_assert(S >= 2, "one item in flight at least");
   Blk16<T> blk[S][BPT];
   // The thread's first block of a share, from a copy of the thread index the
   // compiler cannot see through: per-block addresses are then recomputed
@@ -427,35 +509,7 @@ __global__ __launch_bounds__(kOnePassThreads) void k_quant_nvfp4_items(
                                    __HIP_MEMORY_SCOPE_AGENT);
   };
   auto outer_scale = [&](int64_t e) BSQ_AI -> float {
-    if (t < 64) {  // wave 0: lane l polls slots l, l + 64, ... (nwg <= 512) until all are marked
-      float mx = -1.0f;
-      for (uint32_t spins = 0; spins < spin_limit; ++spins) {
-        // all eight loads are issued before the first is waited for (lanes
-        // past the last slot re-read it), so a poll costs one round trip
-        uint32_t v[kOnePassMaxWg / 64];
-#pragma unroll
-        for (int q = 0; q < kOnePassMaxWg / 64; ++q) {
-          const int w = t + 64 * q;
-          v[q] = __hip_atomic_load(slot + e * nwg + (w < nwg ? w : nwg - 1), __ATOMIC_RELAXED,
-                                   __HIP_MEMORY_SCOPE_AGENT);
-        }
-        bool all = true;
-        float m = 0.0f;
-#pragma unroll
-        for (int q = 0; q < kOnePassMaxWg / 64; ++q) {
-          all = all && (v[q] & 0x80000000u) != 0;
-          m = fmaxf(m, __uint_as_float(v[q] & 0x7FFFFFFFu));
-        }
-        if (__all(all)) {  // wave-uniform
-          mx = wave_max(m);
-          break;
-        }
-        __builtin_amdgcn_s_sleep(1);
-      }
-      if (t == 0) slots_max = mx;
-    }
-    lds_barrier();
-    float a = slots_max;
+    float a = poll_slots(slot + e * nwg, nwg, spin_limit, &slots_max);
     if (a < 0.0f) {  // uniform: the polls ran out; reduce the whole item here
       float m = 0.0f;
       for (int64_t j = t; j < bpi; j += kOnePassThreads) {
@@ -481,41 +535,11 @@ __global__ __launch_bounds__(kOnePassThreads) void k_quant_nvfp4_items(
   const int64_t n = grp < B ? (B - grp + groups - 1) / groups : 0;  // this group's items
   if (n <= 0) return;
   auto it = [&](int64_t i) BSQ_AI -> int64_t { return grp + i * groups; };
-  // Item i lives in register set i % S. Step i starts the loads of item
-  // i + S - 1 (into the set item i - 1 has left) and publishes item i + P,
-  // then quantizes item i once its wait is over. With three sets or more the
-  // publish (of item i + S - 2, whose loads are the second youngest in
-  // flight) comes before the wait for item i; with two it comes after it (P =
-  // 1: item i + 1's loads are the youngest). In the main loop every step
-  // issues and publishes unconditionally, so the wait the compiler places for
-  // one set's loads leaves the younger sets' loads in flight; the last
-  // 2S - 2 steps check the item count.
-  constexpr int P = S == 2 ? 1 : S - 2;
-  auto step = [&](auto set, int64_t i, auto tail) BSQ_AI {
-    constexpr int sc = decltype(set)::value;
-    constexpr bool tl = decltype(tail)::value;
-    if (!tl || i + S - 1 < n) issue((sc + S - 1) % S, it(i + S - 1));
-    if constexpr (S == 2) {
-      const float st = outer_scale(it(i));
-      if (!tl || i + P < n) publish(it(i + P), thread_max((sc + P) % S));
-      quantize(sc, it(i), st);
-    } else {
-      if (!tl || i + P < n) publish(it(i + P), thread_max((sc + P) % S));
-      quantize(sc, it(i), outer_scale(it(i)));
-    }
-  };
-  // prologue: loads of items 0 .. S - 2, maxima of items 0 .. P - 1
-  static_for<S - 1>([&](auto j) BSQ_AI {
-    if (j < n) issue(j, it(j));
-  });
-  static_for<P>([&](auto j) BSQ_AI {
-    if (j < n) publish(it(j), thread_max(j));
-  });
-  int64_t i = 0;
-  for (; i + 2 * S - 2 < n; i += S) static_for<S>([&](auto j) BSQ_AI { step(j, i + j, std::false_type{}); });
-  static_for<2 * S - 2>([&](auto j) BSQ_AI {
-    if (i + j < n) step(std::integral_constant<int, j % S>{}, i + j, std::true_type{});
-  });
+  item_pipeline<S>(
+      n, [&](int set, int64_t i) BSQ_AI { issue(set, it(i)); },
+      [&](int set, int64_t i) BSQ_AI { publish(it(i), thread_max(set)); },
+      [&](int64_t i) BSQ_AI { return outer_scale(it(i)); },
+      [&](int set, int64_t i, float st) BSQ_AI { quantize(set, it(i), st); });
 }
 
 // Row-wise MXFP8: one thread per block of 32 (element index = blk*32 + i).
@@ -722,7 +746,7 @@ __device__ __forceinline__ void sq_unit(const Blk16<T>& e, float m, float st, co
   if constexpr (TR) {
     *reinterpret_cast<uint2*>(lds + sq_lds(16 * w + j, tc * 8)) = make_uint2(a0, a1);
     if (j == 0) lds_sc[w * 4 + tc] = (uint8_t)sc;
-    __syncthreads();
+    lds_barrier();  // LDS only: loads of later items stay in flight
     const int c = threadIdx.x >> 3, q = threadIdx.x & 7;  // column c, rows 16q .. 16q + 15
     const int64_t rr = r0 + 16 * q, cc = c0 + c;
     if (rr < g.R && cc < g.C) {
@@ -737,7 +761,7 @@ __device__ __forceinline__ void sq_unit(const Blk16<T>& e, float m, float st, co
       *reinterpret_cast<uint2*>(codes_t + ((b * g.C + cc) * g.R + rr) / 2) = make_uint2(o[0], o[1]);
       scales_t[(b * g.C + cc) * (g.R / 16) + rr / 16] = lds_sc[q * 4 + (c >> 4)];
     }
-    __syncthreads();  // the LDS unit is reused by the next unit of a persistent workgroup
+    lds_barrier();  // the LDS unit is reused by the next unit of a persistent workgroup
   }
 }
 

@@ -491,13 +491,14 @@ def test_quantize_nvfp4_square_small(dtype, mode, shape, kind):
 @pytest.mark.parametrize("dtype,shape", [("bf16", (3, 512, 1024)), ("bf16", (2, 1280, 2048)),
                                          ("bf16", (3, 1536, 3072)), ("bf16", (1, 4096, 2560)),
                                          ("f32", (2, 512, 1040)), ("f32", (1, 1024, 2560)),
-                                         ("f32", (1, 4096, 2560)), ("bf16", (2, 1040, 528))])
+                                         ("f32", (1, 4096, 2560)), ("bf16", (2, 1040, 528)),
+                                         ("bf16", (10, 1024, 1024)), ("bf16", (5, 1536, 4096))])
 def test_quantize_nvfp4_square_one_pass(dtype, shape):
     """Items of at least 1 MiB take the one-pass square kernel (1, 2 or 3
-    units per workgroup, one or two interleaved groups, an odd item count,
-    workgroups without a unit, ragged units); items needing more units per
-    workgroup take the two-pass path. Both layouts must equal the oracle's
-    bytes."""
+    units per workgroup, one or two interleaved groups, odd item counts and
+    enough items per group for the steady-state pipeline, workgroups without
+    a unit, ragged units); items needing more units per workgroup take the
+    two-pass path. Both layouts must equal the oracle's bytes."""
     log(f"quantize_nvfp4_square tensor one-pass {dtype} {shape}")
     rng = np.random.default_rng(17 + shape[1])
     x = rng.standard_normal(shape).astype(f32)
