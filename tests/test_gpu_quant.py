@@ -95,14 +95,16 @@ def test_quantize_nvfp4_tensor_one_pass(dtype, shape):
     assert np.array_equal(h(gc), oc)
 
 
-def test_quantize_nvfp4_tensor_one_pass_wait_fallback():
+@pytest.mark.parametrize("shape", [(2, 300, 2048), (7, 1536, 4096)])
+def test_quantize_nvfp4_tensor_one_pass_wait_fallback(shape):
     """A poll limit of 0 sends every workgroup of the one-pass kernel that
     finds a slot unmarked through its fallback (it reduces the item itself);
-    the bytes are unchanged."""
+    the bytes are unchanged (one block per thread in two groups; three blocks
+    per thread in one group with enough items for the steady-state
+    pipeline)."""
     import os
-    log("quantize_nvfp4 tensor one-pass, fallback")
+    log(f"quantize_nvfp4 tensor one-pass, fallback {shape}")
     rng = np.random.default_rng(11)
-    shape = (2, 300, 2048)
     bits = synth.bf16_bits(rng.standard_normal(shape).astype(f32))
     x = synth.bf16_to_f32(bits).reshape(shape)
     os.environ["BSQ_WAIT_POLLS"] = "0"
