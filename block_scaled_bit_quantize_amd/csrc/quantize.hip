@@ -312,19 +312,19 @@ __global__ __launch_bounds__(kThreads) void k_quant_nvfp4(
 }
 
 // Per-item outer scale in one pass over HBM. Each group of the grid (one
-// workgroup per CU, at most kOnePassMaxWg; with two groups two workgroups
-// share a CU, so one group's loads overlap the other's wait and stores) walks
-// its items (every groups-th item) in order. Every workgroup loads its share
-// of item e into registers (at most BPT blocks of 16 per thread) and
-// publishes its maximum in its own slot slot[e][w] (bit pattern with bit 31
-// set as the arrival mark: magnitudes have it clear). It then starts the loads
-// of its share of item e + 1 and, while they are in flight, waits until every
-// slot of item e is marked (the maximum of the slots is item e's maximum),
-// publishes item e + 1's maximum once its loads have arrived, and then
-// quantizes item e from registers. One wave polls the slots; the others wait
-// at a barrier that waits for LDS operations only, so their loads stay in
-// flight (a plain __syncthreads would wait for every outstanding load and
-// store).
+// workgroup per CU; two groups when two of the kernel's workgroups fit on a
+// CU, so that one group's loads overlap the other's wait and stores) walks its
+// items (every groups-th item) in order. A workgroup keeps its shares of up to
+// S items in registers (S register sets of at most BPT blocks of 16 per
+// thread): it publishes the maximum of its share of an item in its own slot
+// slot[e][w] (bit pattern with bit 31 set as the arrival mark: magnitudes
+// have it clear) as soon as that share's loads have arrived, waits until
+// every slot of an item is marked only when the item is next to be quantized
+// (the maximum of the slots is the item's maximum), and has the loads of the
+// following items in flight meanwhile (item_pipeline below). One wave polls
+// the slots; the others wait at a barrier that waits for LDS operations only,
+// so their loads stay in flight (a plain __syncthreads would wait for every
+// outstanding load and store).
 // The wait is bounded: after spin_limit polls the workgroup reduces the whole
 // item itself (the same maximum, from a second read), so every wave always
 // finishes. The slots start at zero. Slot accesses are relaxed device-scope
