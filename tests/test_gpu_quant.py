@@ -71,13 +71,14 @@ def test_quantize_nvfp4_small(dtype, mode, shape, kind):
 @pytest.mark.parametrize("dtype,shape", [("bf16", (3, 300, 4096)), ("f32", (2, 257, 1040)), ("bf16", (1, 4100, 1024)),
                                          ("bf16", (3, 3072, 4096)), ("f32", (1, 2048, 4096)),
                                          ("bf16", (5, 1536, 4096)), ("bf16", (2, 1200, 2048)), ("f32", (2, 1200, 2048)),
-                                         ("bf16", (2, 2304, 4096)), ("bf16", (2, 2048, 7168)), ("bf16", (2, 4096, 4096))])
+                                         ("bf16", (2, 2304, 4096)), ("bf16", (2, 2048, 7168)), ("bf16", (2, 4096, 4096)),
+                                         ("bf16", (32, 1024, 1536)), ("bf16", (33, 1536, 1024))])
 def test_quantize_nvfp4_tensor_one_pass(dtype, shape):
     """Items of at least 1 MiB take the one-pass grid kernel (shares of blocks
     per workgroup that do not divide evenly, several items in sequence, odd
     and even item counts per group, one and two groups, shares of 1 to 8
-    blocks per thread on 256 CUs with two and three register sets); the bytes
-    must equal the oracle's."""
+    blocks per thread on 256 CUs with two and three register sets, and 32 or
+    more items on two halves of the chip); the bytes must equal the oracle's."""
     log(f"quantize_nvfp4 tensor one-pass {dtype} {shape}")
     rng = np.random.default_rng(7 + shape[1])
     x = rng.standard_normal(shape).astype(f32)
@@ -95,13 +96,13 @@ def test_quantize_nvfp4_tensor_one_pass(dtype, shape):
     assert np.array_equal(h(gc), oc)
 
 
-@pytest.mark.parametrize("shape", [(2, 300, 2048), (7, 1536, 4096)])
+@pytest.mark.parametrize("shape", [(2, 300, 2048), (7, 1536, 4096), (32, 1024, 1536)])
 def test_quantize_nvfp4_tensor_one_pass_wait_fallback(shape):
     """A poll limit of 0 sends every workgroup of the one-pass kernel that
     finds a slot unmarked through its fallback (it reduces the item itself);
     the bytes are unchanged (one block per thread in two groups; three blocks
     per thread in one group with enough items for the steady-state
-    pipeline)."""
+    pipeline; 32 items on two halves of the chip)."""
     import os
     log(f"quantize_nvfp4 tensor one-pass, fallback {shape}")
     rng = np.random.default_rng(11)
