@@ -156,7 +156,6 @@ __device__ __forceinline__ void sr_e4m3_x8(float (&y)[8], const U32x4& w) {
 // sr_e4m3. Codes are the same either way.
 __device__ __forceinline__ void sr_block_e4m3(const float (&z)[32], int e, uint64_t seed, uint64_t stream,
                                               uint64_t grp0, uint32_t (&out)[8]) {
-  typedef short v2s __attribute__((ext_vector_type(2)));
   const float scale = __uint_as_float((uint32_t)(e + 127) << 23);  // 2^e, used for e >= -120 only
   const uint32_t thr = ((uint32_t)(e + 121) << 24) - 2u;           // (bits(2^(e-6)) << 1) - 2
   const float pw = pow2_neg(e);
