@@ -72,7 +72,8 @@ def test_quantize_nvfp4_small(dtype, mode, shape, kind):
                                          ("bf16", (3, 3072, 4096)), ("f32", (1, 2048, 4096)),
                                          ("bf16", (5, 1536, 4096)), ("bf16", (2, 1200, 2048)), ("f32", (2, 1200, 2048)),
                                          ("bf16", (2, 2304, 4096)), ("bf16", (2, 2048, 7168)), ("bf16", (2, 4096, 4096)),
-                                         ("bf16", (32, 1024, 1536)), ("bf16", (33, 1536, 1024))])
+                                         ("bf16", (32, 1024, 1536)), ("bf16", (33, 1536, 1024)),
+                                         ("bf16", (32, 1536, 2048))])
 def test_quantize_nvfp4_tensor_one_pass(dtype, shape):
     """Items of at least 1 MiB take the one-pass grid kernel (shares of blocks
     per workgroup that do not divide evenly, several items in sequence, odd
