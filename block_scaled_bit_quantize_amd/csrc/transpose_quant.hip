@@ -29,9 +29,12 @@ namespace {
 constexpr int kThreads = 256;
 constexpr int TM = 128;  // tokens per tile (input rows)
 constexpr int TC = 64;   // column granularity of the transposed layouts
+constexpr int64_t kMaxTransposeCols = 1 << 22;  // bf16/float sources: 128 rows of byte offsets below 2^31
 enum { SRC_BF16 = 0, SRC_F32 = 1, SRC_NVFP4 = 2 };
 
 typedef _Float16 h2 __attribute__((ext_vector_type(2)));
+typedef int v4i __attribute__((ext_vector_type(4)));
+typedef __amdgpu_buffer_rsrc_t brsrc_t;
 
 inline unsigned grid1(int64_t n, int t = kThreads) { return (unsigned)((n + t - 1) / t); }
 __host__ __device__ inline int64_t pad32(int64_t n) { return (n + 31) / 32 * 32; }
@@ -220,27 +223,25 @@ __global__ __launch_bounds__(kThreads) void k_tq(
   const int t = threadIdx.x;
 
   // ---- phase 1: rows m0 .. m0+127 of the segment, channels c0 .. c0+TCH-1
-  if constexpr (SRC == SRC_BF16) {
-    const uint16_t* x = static_cast<const uint16_t*>(src);
-    constexpr int TPR = TCH / 8;          // threads per row, 8 values each
-    constexpr int RPP = kThreads / TPR;   // rows per pass
+  if constexpr (SRC == SRC_BF16 || SRC == SRC_F32) {
+    // 16-byte buffer loads against a resource that starts at the tile's
+    // first row and ends with the segment's last row inside the tile: rows
+    // past the segment read as zeros, with no branch and one 32-bit offset
+    // per load (cols <= 2^22 keeps 128 rows of offsets below 2^31)
+    constexpr int VPR = TCH * (int)sizeof(TT) / 16;  // 16-byte vectors per tile row
+    constexpr int RPP = kThreads / VPR;              // rows per pass
+    const TT* x = static_cast<const TT*>(src);
+    const int64_t rows_in = Me - m0 < TM ? Me - m0 : TM;  // >= 1: the tile starts inside the segment
+    const int row_bytes = (int)(C * (int64_t)sizeof(TT));
+    const brsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(
+        (void*)(x + (seg_start + m0) * C + c0), (short)0,
+        (int)((rows_in - 1) * row_bytes + TCH * (int)sizeof(TT)), 0x00020000);
+    const int vi = t % VPR;
 #pragma unroll
     for (int p = 0; p < TM / RPP; ++p) {
-      const int m = p * RPP + t / TPR;
-      const int cc = (t % TPR) * 8;
-      uint4 v = make_uint4(0, 0, 0, 0);
-      if (m0 + m < Me && c0 + cc < C) v = *reinterpret_cast<const uint4*>(x + (seg_start + m0 + m) * C + c0 + cc);
-      *reinterpret_cast<uint4*>(&tile[m * LROW + cc * 2]) = v;
-    }
-  } else if constexpr (SRC == SRC_F32) {
-    const float* x = static_cast<const float*>(src);
-#pragma unroll
-    for (int p = 0; p < 8; ++p) {
-      const int m = p * 16 + (t >> 4);
-      const int cc = (t & 15) * 4;
-      float4 v = make_float4(0.f, 0.f, 0.f, 0.f);
-      if (m0 + m < Me && c0 + cc < C) v = *reinterpret_cast<const float4*>(x + (seg_start + m0 + m) * C + c0 + cc);
-      *reinterpret_cast<float4*>(&tile[m * LROW + cc * 4]) = v;
+      const int m = p * RPP + t / VPR;
+      const v4i v = __builtin_amdgcn_raw_buffer_load_b128(rs, m * row_bytes + vi * 16, 0, 0);
+      *reinterpret_cast<v4i*>(&tile[m * LROW + vi * 16]) = v;
     }
   } else {
     const uint8_t* codes = static_cast<const uint8_t*>(src);
@@ -592,7 +593,7 @@ extern "C" int bsq_quantize_mxfp8(const void* x, int dtype, int64_t rows, int64_
     return bsq_quantize_mxfp8_rows(x, dtype, rows, cols, rnd, seed, stream_id, codes, scales,
                                    bsqh::as_stream(stream));
   }
-  BSQ_REQUIRE(cols % TC == 0, BSQ_E_SHAPE);
+  BSQ_REQUIRE(cols % TC == 0 && cols <= kMaxTransposeCols, BSQ_E_SHAPE);
   BSQ_REQUIRE(seg_offsets == nullptr || (num_segments >= 1 && num_segments <= 1024), BSQ_E_SHAPE);
   if (rows == 0 || cols == 0) return BSQ_OK;
   BSQ_REQUIRE(x && codes && scales && ws, BSQ_E_NULL);
@@ -620,7 +621,7 @@ extern "C" int bsq_quantize_mxfp8_dual(const void* x, int dtype, int64_t rows, i
                                        bsq_stream_t stream) {
   BSQ_REQUIRE(dtype == BSQ_F32 || dtype == BSQ_BF16, BSQ_E_DTYPE);
   BSQ_REQUIRE(rnd == BSQ_RN || rnd == BSQ_SR, BSQ_E_ENUM);
-  BSQ_REQUIRE(rows >= 0 && cols >= 0 && cols % TC == 0, BSQ_E_SHAPE);
+  BSQ_REQUIRE(rows >= 0 && cols >= 0 && cols % TC == 0 && cols <= kMaxTransposeCols, BSQ_E_SHAPE);
   BSQ_REQUIRE(seg_offsets == nullptr || (num_segments >= 1 && num_segments <= 1024), BSQ_E_SHAPE);
   if (rows == 0 || cols == 0) return BSQ_OK;
   BSQ_REQUIRE(x && codes && scales && codes_t && scales_t && ws, BSQ_E_NULL);

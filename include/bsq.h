@@ -177,7 +177,8 @@ int bsq_quantize_nvfp4_square(const void* x, int dtype, int64_t batch, int64_t r
  *              zero padded, the segments one after another (the "padded
  *              per-segment transposed layout"); blocks of 32 run along tokens
  *              from the segment start; element index of (e, c, m) is
- *              cols * sum_{e'<e} Mp_e' + c * Mp_e + m. cols % 64 == 0.
+ *              cols * sum_{e'<e} Mp_e' + c * Mp_e + m. cols % 64 == 0,
+ *              cols <= 4194304.
  *              seg_offsets == NULL means one segment covering all rows.
  *              Needs bsq_quantize_mxfp8_workspace() bytes of workspace. The
  *              caller sizes codes for cols * sum_e Mp_e bytes and scales for
@@ -213,7 +214,7 @@ int bsq_quantize_mxfp8(const void* x, int dtype, int64_t rows, int64_t cols, int
  * row inside a segment (all rows when seg_offsets[0] == 0 and the last offset
  * == rows, or seg_offsets == NULL). Rows outside every segment (only with
  * offsets that do not cover [0, rows)) are not written in codes/scales.
- * cols % 64 == 0; workspace bsq_quantize_mxfp8_workspace(rows, 1, num_segments);
+ * cols % 64 == 0, cols <= 4194304; workspace bsq_quantize_mxfp8_workspace(rows, 1, num_segments);
  * x, codes, codes_t, ws 16-byte aligned. Errors: NULL, SHAPE, ALIGN, DTYPE,
  * ENUM, WORKSPACE, LAUNCH. */
 int bsq_quantize_mxfp8_dual(const void* x, int dtype, int64_t rows, int64_t cols,

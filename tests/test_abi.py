@@ -140,6 +140,7 @@ def test_quantize_mxfp8_validation(lib):
     assert q(FAKE, 3, 4, 64, 0, None, 0, 1, 0, 0, FAKE, FAKE, None, 0, None) == E_DTYPE
     assert q(FAKE, 1, 4, 64, 2, None, 0, 1, 0, 0, FAKE, FAKE, None, 0, None) == E_ENUM
     assert q(FAKE, 1, 4, 96, 1, None, 0, 1, 0, 0, FAKE, FAKE, FAKE, 1 << 20, None) == E_SHAPE   # cols % 64
+    assert q(FAKE, 1, 4, (1 << 22) + 64, 1, None, 0, 1, 0, 0, FAKE, FAKE, FAKE, 1 << 20, None) == E_SHAPE  # cols <= 2^22
     assert q(FAKE, 1, 4, 64, 1, FAKE, 0, 1, 0, 0, FAKE, FAKE, FAKE, 1 << 20, None) == E_SHAPE   # 0 segments
     assert q(FAKE, 1, 4, 64, 1, None, 0, 1, 0, 0, FAKE, FAKE, None, 0, None) == E_NULL
     assert q(FAKE, 1, 4, 64, 1, None, 0, 1, 0, 0, FAKE, FAKE, FAKE, 8, None) == E_WORKSPACE
@@ -149,6 +150,7 @@ def test_quantize_mxfp8_validation(lib):
     def dcall(i, v):
         a = list(ok); a[i] = v; return d(*a)
     assert dcall(3, 96) == E_SHAPE            # cols % 64
+    assert dcall(3, (1 << 22) + 64) == E_SHAPE  # cols <= 2^22
     assert dcall(4, FAKE) == E_SHAPE          # seg_offsets with 0 segments
     assert dcall(6, 5) == E_ENUM
     assert dcall(1, 3) == E_DTYPE
