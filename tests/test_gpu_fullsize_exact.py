@@ -1,0 +1,45 @@
+"""Every output byte of the forward's NVFP4 quantizers at full size, bit-exact
+against the oracle: the activations [16384, 4096] per token with Four Over
+Six, and the 64 expert weights [1536, 4096] with per-expert outer scales from
+the one-pass kernel (round to nearest with two-level scales, section
+"Low-precision formats on Blackwell"; Four Over Six, section "Recipe
+details"). The oracle runs in slices; each slice is compared as soon as it
+is done."""
+import numpy as np
+import pytest
+
+import block_scaled_bit_quantize_amd as bsq
+import synth
+from oracle import quant as Q
+
+from _gpu_util import bf16_t, h, log
+
+pytestmark = pytest.mark.gpu
+
+
+def test_activations_four_over_six_fullsize_exact():
+    x = synth.moe_activations(2)
+    log("fullsize exact: activations, four over six")
+    gc, gs, go = bsq.quantize_nvfp4(bf16_t(x), "row", four_over_six=True)
+    gc, gs, go = h(gc), h(gs), h(go)
+    for r0 in range(0, x.shape[0], 2048):
+        xf = synth.bf16_to_f32(x[r0:r0 + 2048])
+        oc, os_, oo = Q.quantize_nvfp4(xf[None], Q.OUTER_ROW, four_over_six=True)
+        assert np.array_equal(go[r0:r0 + 2048], oo[0]), r0
+        assert np.array_equal(gs[r0:r0 + 2048], os_[0]), r0
+        assert np.array_equal(gc[r0:r0 + 2048], oc[0]), r0
+        log(f"activations rows {r0}..{r0 + 2047} equal")
+
+
+def test_expert_weights_fullsize_exact():
+    w = synth.moe_weights(2)
+    log("fullsize exact: expert weights, per-expert outer scale (one pass)")
+    gc, gs, go = bsq.quantize_nvfp4(bf16_t(w), "tensor")
+    gc, gs, go = h(gc), h(gs), h(go)
+    for e0 in range(0, w.shape[0], 8):
+        we = synth.bf16_to_f32(w[e0:e0 + 8])
+        oc, os_, oo = Q.quantize_nvfp4(we, Q.OUTER_TENSOR)
+        assert np.array_equal(go[e0:e0 + 8], oo.reshape(-1)), e0
+        assert np.array_equal(gs[e0:e0 + 8], os_), e0
+        assert np.array_equal(gc[e0:e0 + 8], oc), e0
+        log(f"experts {e0}..{e0 + 7} equal")
