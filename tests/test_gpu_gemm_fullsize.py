@@ -1,0 +1,113 @@
+"""Every output of the step's three expert grouped GEMMs at full size under the
+accept rule of oracle.gemm: FPROP y[131072, 1536] (NVFP4, gathered token
+rows), DGRAD dx[131072, 4096] and WGRAD dw[64, 1536, 4096] (MXFP8), with the
+step's routing and random valid operand bytes. The operands are dequantized
+by the oracle (exact float64 values); the float64 reference products of each
+expert's blocks and of their magnitudes are taken with torch's float64
+matmul on the device (a library product in float64, as the oracle's own
+reference uses one; error far below the rule's bound) and compared expert by
+expert on the host. The oracle's own products are compared on sampled rows
+and experts in test_gpu_gemm.py."""
+import numpy as np
+import pytest
+import torch
+
+import block_scaled_bit_quantize_amd as bsq
+import synth
+from oracle import gemm as G
+from oracle import quant as Q
+from oracle.route import route as oroute
+
+from _gpu_util import DEV, filler_mxfp8, filler_nvfp4, h, log, t
+
+pytestmark = pytest.mark.gpu
+
+
+class _Worst:
+    def __init__(self, what):
+        self.what, self.ratio, self.n = what, 0.0, 0
+
+    def add(self, y, a, b):
+        """y: the kernel's float32 block (device); a [m, k], b [n, k] float64 (device)."""
+        yref = h(a @ b.T)
+        yabs = h(a.abs() @ b.abs().T)
+        ok, ratio = G.within_tolerance(h(y), yref, yabs)
+        assert ok, (self.what, ratio)
+        self.ratio = max(self.ratio, ratio)
+        self.n += yref.size
+
+    def report(self):
+        log(f"{self.what}: {self.n} outputs within the rule, worst bound ratio {self.ratio:.3f}")
+
+
+def _routing():
+    ids = synth.moe_routing(2)
+    row_index, seg, _ = oroute(ids, 64)
+    return row_index, seg
+
+
+def test_fprop_nvfp4_every_output():
+    E, T, K, N = 64, 16384, 4096, 1536
+    row_index, seg = _routing()
+    M = int(seg[-1])
+    rng = np.random.default_rng(71)
+    ac, as_ = filler_nvfp4(rng, (T,), K)
+    ao = rng.uniform(1e-3, 4e-3, T).astype(np.float32)
+    bc, bs = filler_nvfp4(rng, (E, N), K)
+    bo = rng.uniform(5e-6, 2e-5, E).astype(np.float32)
+    log("fullsize fprop: run")
+    y = bsq.grouped_gemm_nvfp4(t(ac), t(as_), t(ao), t(bc), t(bs), t(bo), t(seg), M, row_index=t(row_index),
+                               out_dtype=torch.float32)
+    xa = t(Q.dequantize_nvfp4_f64(ac[None], as_[None], ao.reshape(1, -1), Q.OUTER_ROW)[0])
+    ri = t(row_index.astype(np.int64))
+    w = _Worst("fprop (nvfp4)")
+    for e in range(E):
+        if seg[e + 1] == seg[e]:
+            continue
+        we = t(Q.dequantize_nvfp4_f64(bc[e:e + 1], bs[e:e + 1], bo[e:e + 1], Q.OUTER_TENSOR)[0])
+        w.add(y[seg[e]:seg[e + 1]], xa[ri[seg[e]:seg[e + 1]]], we)
+    w.report()
+
+
+def test_dgrad_wgrad_mxfp8_every_output():
+    E, Kx, Ng = 64, 4096, 1536
+    row_index, seg = _routing()
+    M = int(seg[-1])
+    rng = np.random.default_rng(72)
+    ac, as_ = filler_mxfp8(rng, M * Ng)
+    bc, bs = filler_mxfp8(rng, E * Kx * Ng)
+    log("fullsize dgrad: run")
+    y = bsq.grouped_gemm_mxfp8(False, t(ac.reshape(M, Ng)), t(as_.reshape(M, Ng // 32)),
+                               t(bc.reshape(E, Kx, Ng)), t(bs.reshape(E, Kx, Ng // 32)), t(seg), M, Kx, Ng,
+                               out_dtype=torch.float32)
+    ga = t(Q.dequantize_mxfp8_f64(ac, as_).reshape(M, Ng))
+    w = _Worst("dgrad (mxfp8)")
+    for e in range(E):
+        if seg[e + 1] == seg[e]:
+            continue
+        wt = t(Q.dequantize_mxfp8_f64(bc[e * Kx * Ng:(e + 1) * Kx * Ng], bs[e * Kx * Ng // 32:(e + 1) * Kx * Ng // 32])
+               .reshape(Kx, Ng))
+        w.add(y[seg[e]:seg[e + 1]], ga[seg[e]:seg[e + 1]], wt)
+    w.report()
+    del y, ga
+
+    log("fullsize wgrad: run")
+    _, na = bsq.padded_segment_layout(seg, Ng)
+    _, nb = bsq.padded_segment_layout(seg, Kx)
+    A, As = filler_mxfp8(rng, na)
+    B, Bs = filler_mxfp8(rng, nb)
+    mpa, basea = Q.segmented_layout(seg, Ng)
+    mpb, baseb = Q.segmented_layout(seg, Kx)
+    for e in range(E):  # the layout's padding tokens hold zeros
+        Me = int(seg[e + 1] - seg[e])
+        A[basea[e]:basea[e] + Ng * mpa[e]].reshape(Ng, mpa[e])[:, Me:] = 0
+        B[baseb[e]:baseb[e] + Kx * mpb[e]].reshape(Kx, mpb[e])[:, Me:] = 0
+    dw = bsq.grouped_gemm_mxfp8(True, t(A), t(As), t(B), t(Bs), t(seg), Ng, Kx)
+    A64 = t(Q.dequantize_mxfp8_f64(A, As))
+    B64 = t(Q.dequantize_mxfp8_f64(B, Bs))
+    w = _Worst("wgrad (mxfp8)")
+    for e in range(E):
+        a = A64[basea[e]:basea[e] + Ng * mpa[e]].reshape(Ng, mpa[e])
+        b = B64[baseb[e]:baseb[e] + Kx * mpb[e]].reshape(Kx, mpb[e])
+        w.add(dw[e], a, b)
+    w.report()
