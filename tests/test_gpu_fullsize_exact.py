@@ -1,18 +1,21 @@
-"""Every output byte of the forward's NVFP4 quantizers at full size, bit-exact
-against the oracle: the activations [16384, 4096] per token with Four Over
-Six, and the 64 expert weights [1536, 4096] with per-expert outer scales from
-the one-pass kernel (round to nearest with two-level scales, section
+"""Every output byte at full size, bit-exact against the oracle, of the
+forward's NVFP4 quantizers (the activations [16384, 4096] per token with Four
+Over Six, and the 64 expert weights [1536, 4096] with per-expert outer scales
+from the one-pass kernel: round to nearest with two-level scales, section
 "Low-precision formats on Blackwell"; Four Over Six, section "Recipe
-details"). The oracle runs in slices; each slice is compared as soon as it
-is done."""
+details") and of the combine codec. The oracle runs in slices; each slice is
+compared as soon as it is done."""
 import numpy as np
 import pytest
+import torch
 
 import block_scaled_bit_quantize_amd as bsq
 import synth
+from oracle import codec as C
 from oracle import quant as Q
+from oracle.route import route as oroute
 
-from _gpu_util import bf16_t, h, log
+from _gpu_util import bf16_t, h, log, t
 
 pytestmark = pytest.mark.gpu
 
@@ -43,3 +46,31 @@ def test_expert_weights_fullsize_exact():
         assert np.array_equal(gs[e0:e0 + 8], os_), e0
         assert np.array_equal(gc[e0:e0 + 8], oc), e0
         log(f"experts {e0}..{e0 + 7} equal")
+
+
+def test_combine_codec_fullsize_exact():
+    """The combine payload (131072 dispatched rows of 4096, the step's
+    routing): every encoded byte (RHT-32 + S2F6, section "Quantized
+    communications") and every combined token, bit-exact against the oracle."""
+    T, k, H = 16384, 8, 4096
+    mask = 0x9E3779B9
+    rows = synth.combine_rows(T * k, H)
+    _, _, pair_row = oroute(synth.moe_routing(2), 64)
+    pair_row = np.asarray(pair_row, np.int64)
+    log("fullsize exact: combine codec")
+    gc, gs = bsq.rht_s2f6_encode(bf16_t(rows), mask)
+    out = bsq.rht_s2f6_combine(gc, gs, t(pair_row.astype(np.int32)), k, mask, out_dtype=torch.float32)
+    gc, gs, out = h(gc), h(gs), h(out)
+    oc = np.empty_like(gc)
+    os_ = np.empty_like(gs)
+    for r0 in range(0, T * k, 16384):
+        oc[r0:r0 + 16384], os_[r0:r0 + 16384] = C.encode(synth.bf16_to_f32(rows[r0:r0 + 16384]), mask)
+        assert np.array_equal(gc[r0:r0 + 16384], oc[r0:r0 + 16384]), r0
+        assert np.array_equal(gs[r0:r0 + 16384], os_[r0:r0 + 16384]), r0
+    log("encoded rows equal")
+    pr = pair_row.reshape(T, k)
+    for t0 in range(0, T, 2048):
+        sub = pr[t0:t0 + 2048].reshape(-1)
+        want = C.combine(oc[sub], os_[sub], np.arange(len(sub)), k, mask)
+        assert np.array_equal(out[t0:t0 + 2048].view(np.uint32), want.view(np.uint32)), t0
+    log("combined tokens equal")
