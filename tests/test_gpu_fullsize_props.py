@@ -26,7 +26,7 @@ from oracle import formats as F
 from oracle import quant as Q
 from oracle.route import route as oroute
 
-from _gpu_util import DEV, bf16_t, filler_nvfp4, log, t
+from _gpu_util import DEV, bf16_t, filler_nvfp4, h, log, t
 
 pytestmark = pytest.mark.gpu
 
@@ -134,3 +134,53 @@ def test_gradient_and_activation_fullsize_properties():
                                       row_gather=t(row_index), seg_offsets=t(seg), out_elems=nx)
     ri = t(row_index.astype(np.int64))
     per_segment(rc, rs, lambda a, b: zx[ri[a:b]], Kx, "activations transposed")
+
+
+@pytest.mark.parametrize("dtype", [torch.float32, torch.bfloat16])
+def test_transposed_mxfp8_max_cols(dtype):
+    """The transposed quantizer and the one-read dual at their largest column
+    count (2^22: a float32 tile's row offsets reach 127 * 2^24 bytes), 160
+    rows in two ragged segments: every output by the properties above, 64
+    sampled channels bit-exact against the oracle's draws, and the dual equal
+    to the two separate calls."""
+    C = 1 << 22
+    seg = np.array([0, 37, 160], dtype=np.int64)
+    log(f"max cols transposed mxfp8 {dtype}")
+    g = torch.Generator(device=DEV)
+    g.manual_seed(2024)
+    x = (torch.randn((160, C), generator=g, device=DEV) * 3e-3).to(dtype)
+    mp, n = bsq.padded_segment_layout(seg, C)
+    _, base = Q.segmented_layout(seg, C)
+    sd = t(seg)
+    tc, ts = bsq.quantize_mxfp8(x, "sr", seed=7, stream_id=2, transpose=True, seg_offsets=sd, out_elems=n)
+    xf = x.float()
+    sums = _Sums(f"max cols {dtype}")
+    for e in range(2):
+        a, b = int(seg[e]), int(seg[e + 1])
+        for c0 in range(0, C, 1 << 20):
+            Z = torch.zeros((1 << 20, mp[e]), dtype=torch.float32, device=DEV)
+            Z[:, :b - a] = xf[a:b, c0:c0 + (1 << 20)].T
+            lo = int(base[e]) + c0 * mp[e]
+            hi = lo + (1 << 20) * mp[e]
+            _check_mx(tc[lo:hi], ts[lo // 32:hi // 32], Z, sums)
+    sums.check()
+    rng = np.random.default_rng(5)
+    chans = np.unique(np.r_[0, C - 1, rng.integers(0, C, 62)])
+    tch, tsh = h(tc), h(ts)
+    for e in range(2):
+        a, b = int(seg[e]), int(seg[e + 1])
+        zc = np.zeros((len(chans), mp[e]), dtype=np.float32)
+        zc[:, :b - a] = h(xf[a:b][:, t(chans)]).T
+        idx = (np.uint64(base[e]) + chans.astype(np.uint64)[:, None] * np.uint64(mp[e])
+               + np.arange(mp[e], dtype=np.uint64)[None, :])
+        oc, os_ = Q.mxfp8_quantize(zc, idx, Q.SR, 7, 2)
+        for i, c in enumerate(chans):
+            lo = int(base[e]) + int(c) * mp[e]
+            assert np.array_equal(tch[lo:lo + mp[e]], oc[i]), (e, c)
+            assert np.array_equal(tsh[lo // 32:(lo + mp[e]) // 32], os_[i]), (e, c)
+    del tch, tsh
+    rc, rs = bsq.quantize_mxfp8(x, "sr", seed=7, stream_id=1)
+    (dc, ds), (dtc, dts) = bsq.quantize_mxfp8_dual(x, "sr", seed=7, stream_rows=1, stream_t=2, seg_offsets=sd,
+                                                   out_elems=n)
+    assert torch.equal(dc, rc) and torch.equal(ds, rs)
+    assert torch.equal(dtc, tc) and torch.equal(dts, ts)
