@@ -3,7 +3,7 @@ forward's NVFP4 quantizers (the activations [16384, 4096] per token with Four
 Over Six, and the 64 expert weights [1536, 4096] with per-expert outer scales
 from the one-pass kernel: round to nearest with two-level scales, section
 "Low-precision formats on Blackwell"; Four Over Six, section "Recipe
-details") and of the combine codec. The oracle runs in slices; each slice is
+details"), the same for workload 5's sizes, and of the combine codec. The oracle runs in slices; each slice is
 compared as soon as it is done."""
 import numpy as np
 import pytest
@@ -74,3 +74,36 @@ def test_combine_codec_fullsize_exact():
         want = C.combine(oc[sub], os_[sub], np.arange(len(sub)), k, mask)
         assert np.array_equal(out[t0:t0 + 2048].view(np.uint32), want.view(np.uint32)), t0
     log("combined tokens equal")
+
+
+def test_workload5_quantizers_fullsize_exact():
+    """Workload 5 (65536 tokens, hidden 7168; 128 experts of 2048 x 7168):
+    every output byte of the per-token Four Over Six activation quantizer and
+    of the per-expert one-pass weight quantizer, against the oracle run over
+    slices in a pool of worker processes."""
+    import _oracle_pool
+    x = synth.moe_activations(5)
+    log("fullsize exact: workload 5 activations, four over six")
+    gc, gs, go = bsq.quantize_nvfp4(bf16_t(x), "row", four_over_six=True)
+    gc, gs, go = h(gc), h(gs), h(go)
+    R = 4096
+    with _oracle_pool.pool() as ex:
+        jobs = ((x[r0:r0 + R], "row", True) for r0 in range(0, x.shape[0], R))
+        for i, (oc, os_, oo) in enumerate(ex.map(_oracle_pool.nvfp4_slice, jobs)):
+            r0 = i * R
+            assert np.array_equal(go[r0:r0 + R], oo[0]), r0
+            assert np.array_equal(gs[r0:r0 + R], os_[0]), r0
+            assert np.array_equal(gc[r0:r0 + R], oc[0]), r0
+        log("workload 5 activations equal")
+        del x, gc, gs, go
+        w = synth.moe_weights(5)
+        log("fullsize exact: workload 5 expert weights")
+        gc, gs, go = bsq.quantize_nvfp4(bf16_t(w), "tensor")
+        gc, gs, go = h(gc), h(gs), h(go)
+        jobs = ((w[e0:e0 + 4], "tensor", False) for e0 in range(0, w.shape[0], 4))
+        for i, (oc, os_, oo) in enumerate(ex.map(_oracle_pool.nvfp4_slice, jobs)):
+            e0 = i * 4
+            assert np.array_equal(go[e0:e0 + 4], oo.reshape(-1)), e0
+            assert np.array_equal(gs[e0:e0 + 4], os_), e0
+            assert np.array_equal(gc[e0:e0 + 4], oc), e0
+        log("workload 5 expert weights equal")
