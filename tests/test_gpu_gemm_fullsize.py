@@ -111,3 +111,49 @@ def test_dgrad_wgrad_mxfp8_every_output():
         b = B64[baseb[e]:baseb[e] + Kx * mpb[e]].reshape(Kx, mpb[e])
         w.add(dw[e], a, b)
     w.report()
+
+
+def test_fprop_nvfp4_workload5_every_output():
+    """Workload 5's NVFP4 forward at full size (65536 tokens, hidden 7168, 128
+    experts of 2048 x 7168, top-8 Zipf routing: segments of 717 to 59174
+    rows), every output under the accept rule. The operands are decoded on the
+    device with the oracle's E2M1 and E4M3 tables (q * s_b * s_t, exact in
+    float64) and the rule is applied there with the oracle's constants."""
+    from oracle import formats as F
+    p = synth.WORKLOADS[5]
+    T, K, E, N = p["tokens"], p["hidden"], p["experts"], p["ffn"]
+    row_index, seg, _ = oroute(synth.moe_routing(5), E)
+    M = int(seg[-1])
+    rng = np.random.default_rng(75)
+    ac, as_ = filler_nvfp4(rng, (T,), K)
+    ao = rng.uniform(1e-3, 4e-3, T).astype(np.float32)
+    bc, bs = filler_nvfp4(rng, (E, N), K)
+    bo = rng.uniform(5e-6, 2e-5, E).astype(np.float32)
+    log("fullsize fprop workload 5: run")
+    y = bsq.grouped_gemm_nvfp4(t(ac), t(as_), t(ao), t(bc), t(bs), t(bo), t(seg), M, row_index=t(row_index),
+                               out_dtype=torch.float32)
+    q_lut = t(F.e2m1_decode(np.arange(16)).astype(np.float64))
+    s_lut = t(F.e4m3_decode(np.arange(256)).astype(np.float64))
+
+    def decode(codes, scales, outer):  # codes u8 [R, K/2] (low nibble first), scales u8 [R, K/16], outer [R, 1]
+        c = codes.long()
+        q = torch.stack((q_lut[c & 15], q_lut[c >> 4]), dim=-1).reshape(codes.shape[0], -1)
+        return q * s_lut[scales.long()].repeat_interleave(16, dim=1) * outer
+
+    xa = decode(t(ac), t(as_), t(ao.astype(np.float64)).reshape(-1, 1))
+    ri = t(row_index.astype(np.int64))
+    worst, count = 0.0, 0
+    for e in range(E):
+        a, b = int(seg[e]), int(seg[e + 1])
+        if a == b:
+            continue
+        we = decode(t(bc[e]), t(bs[e]), float(bo[e]))
+        xe = xa[ri[a:b]]
+        yref = xe @ we.T
+        yabs = xe.abs() @ we.abs().T
+        bound = G.REL_TOL * yref.abs() + G.ABS_FLOOR * yabs
+        err = (y[a:b].double() - yref).abs()
+        worst = max(worst, float((err / bound.clamp_min(1e-300)).max()))
+        count += err.numel()
+        assert bool((err <= bound).all()), (e, worst)
+    log(f"fprop workload 5: {count} outputs within the rule, worst bound ratio {worst:.3f}")
