@@ -22,3 +22,11 @@ def pool():
     import multiprocessing as mp
     from concurrent.futures import ProcessPoolExecutor
     return ProcessPoolExecutor(max_workers=max(1, min(16, os.cpu_count() or 1)), mp_context=mp.get_context("spawn"))
+
+
+def swiglu_slice(args):
+    """(bf16 bits of h13 [rows, 2F], F) -> the oracle's SwiGLU + NVFP4 (Four
+    Over Six) of the slice: (codes, scales, outer)."""
+    from oracle import chain as CH
+    bits, F = args
+    return CH.swiglu_quantize(synth.bf16_to_f32(bits), F)

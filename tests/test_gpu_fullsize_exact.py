@@ -107,3 +107,27 @@ def test_workload5_quantizers_fullsize_exact():
             assert np.array_equal(gs[e0:e0 + 4], os_), e0
             assert np.array_equal(gc[e0:e0 + 4], oc), e0
         log("workload 5 expert weights equal")
+
+
+def test_swiglu_quantize_fullsize_exact():
+    """The expert chain's quantization step at the layer's size: h13 [131072,
+    2 x 1536] bf16 -> NVFP4 of silu(gate) * up, per-row outer scale, Four Over
+    Six; every output byte against the oracle (worker pool)."""
+    import _oracle_pool
+    M, F = 131072, 1536
+    rng = np.random.default_rng(88)
+    h13 = np.empty((M, 2 * F), np.uint16)
+    for r0 in range(0, M, 16384):
+        h13[r0:r0 + 16384] = synth.bf16_bits((rng.standard_normal((16384, 2 * F), dtype=np.float32) * 2.0))
+    log("fullsize exact: swiglu + nvfp4")
+    gc, gs, go = bsq.swiglu_quantize_nvfp4(bf16_t(h13))
+    gc, gs, go = h(gc), h(gs), h(go)
+    R = 8192
+    with _oracle_pool.pool() as ex:
+        jobs = ((h13[r0:r0 + R], F) for r0 in range(0, M, R))
+        for i, (oc, os_, oo) in enumerate(ex.map(_oracle_pool.swiglu_slice, jobs)):
+            r0 = i * R
+            assert np.array_equal(go[r0:r0 + R], oo), r0
+            assert np.array_equal(gs[r0:r0 + R], os_), r0
+            assert np.array_equal(gc[r0:r0 + R], oc), r0
+    log("swiglu + nvfp4 rows equal")

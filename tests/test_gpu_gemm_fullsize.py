@@ -46,8 +46,10 @@ def _routing():
     return row_index, seg
 
 
-def test_fprop_nvfp4_every_output():
-    E, T, K, N = 64, 16384, 4096, 1536
+@pytest.mark.parametrize("N", [1536, 3072])
+def test_fprop_nvfp4_every_output(N):
+    """N = 1536: the layer's forward; N = 3072: the expert chain's w13 product."""
+    E, T, K = 64, 16384, 4096
     row_index, seg = _routing()
     M = int(seg[-1])
     rng = np.random.default_rng(71)
@@ -55,12 +57,12 @@ def test_fprop_nvfp4_every_output():
     ao = rng.uniform(1e-3, 4e-3, T).astype(np.float32)
     bc, bs = filler_nvfp4(rng, (E, N), K)
     bo = rng.uniform(5e-6, 2e-5, E).astype(np.float32)
-    log("fullsize fprop: run")
+    log(f"fullsize fprop N={N}: run")
     y = bsq.grouped_gemm_nvfp4(t(ac), t(as_), t(ao), t(bc), t(bs), t(bo), t(seg), M, row_index=t(row_index),
                                out_dtype=torch.float32)
     xa = t(Q.dequantize_nvfp4_f64(ac[None], as_[None], ao.reshape(1, -1), Q.OUTER_ROW)[0])
     ri = t(row_index.astype(np.int64))
-    w = _Worst("fprop (nvfp4)")
+    w = _Worst(f"fprop (nvfp4, N={N})")
     for e in range(E):
         if seg[e + 1] == seg[e]:
             continue
