@@ -18,7 +18,7 @@ from oracle import gemm as G
 from oracle import quant as Q
 from oracle.route import route as oroute
 
-from _gpu_util import DEV, filler_mxfp8, filler_nvfp4, h, log, t
+from _gpu_util import filler_mxfp8, filler_nvfp4, h, log, t
 
 pytestmark = pytest.mark.gpu
 
